@@ -1,0 +1,172 @@
+/*
+ * mxfp4_moe.h -- C ABI of the MI355X (gfx950) MXFP4 mixture-of-experts
+ * expert-projection library (libmxfp4_moe.so).
+ *
+ * The method (gpt-oss-20b files page):
+ *   - README section "MXFP4", checkpoint tensor table: expert weights are
+ *     stored as u8 blocks [Experts, Rows, K/32, 16] holding two E2M1 codes per
+ *     byte (low nibble = even element) and u8 E8M0 scales [Experts, Rows, K/32];
+ *     a weight is its E2M1 value times 2 ** (scale - 127).
+ *   - README section "Dense routing" and src/experts.linnet (fn ranks, route,
+ *     experts_of, weights_of): each token keeps its TopK highest router logits,
+ *     ties to the lower expert index, highest first; the router weights are the
+ *     softmax over the kept logits.
+ *   - README section "Loading" and src/experts.linnet (fn forward_topk,
+ *     forward_routed): the experts multiply only the tokens routed to them; the
+ *     gate/up projection reads the token's input, the down projection each
+ *     slot's own input; every projection adds its per-row bias; the expert sum
+ *     is taken in f32 with the router weights.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous memory on
+ *     the current HIP device.  bf16 values are passed as their uint16_t bit
+ *     patterns.  The caller owns every buffer; the library never allocates or
+ *     frees device memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous and stream-ordered; nothing synchronizes the host.
+ *   - Every argument the host can check is checked before anything is
+ *     enqueued.  On failure the call returns a nonzero mxfp4_status, enqueues
+ *     nothing, and mxfp4_last_error() describes the failure (thread-local).
+ *     Argument checks come before any HIP call, so they also run on a host
+ *     without a GPU.
+ *   - Only gfx950 devices are supported (MXFP4_ERR_UNSUPPORTED_DEVICE).
+ *   - Values written to outputs are deterministic: the same inputs give
+ *     bit-identical outputs (no floating-point atomics).
+ */
+#ifndef MXFP4_MOE_H
+#define MXFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP4_OK = 0,
+  MXFP4_ERR_INVALID_ARG = 1,        /* a null pointer, a bad size or a bad combination */
+  MXFP4_ERR_WORKSPACE = 2,          /* workspace missing or smaller than required */
+  MXFP4_ERR_UNSUPPORTED_DEVICE = 3, /* the current device is not gfx950 */
+  MXFP4_ERR_HIP = 4                 /* a HIP runtime call failed (text in mxfp4_last_error) */
+} mxfp4_status;
+
+/* Bits of the optional device error word written by mxfp4_moe_route_group. */
+#define MXFP4_ROUTE_ERR_ID_RANGE 1  /* a given expert id was outside [0, E) (or no expert could be chosen) */
+#define MXFP4_ROUTE_ERR_ID_DUP 2    /* a token's given expert ids were not distinct */
+
+/* Library limits. */
+#define MXFP4_MAX_EXPERTS 512
+#define MXFP4_MAX_TOPK 32
+
+/* Projection paths for mxfp4_expert_proj. */
+#define MXFP4_PATH_AUTO 0  /* GEMV when T * k <= 8, grouped GEMM otherwise */
+#define MXFP4_PATH_GEMV 1  /* decode GEMV: 128-bit weight streaming, fp32 products (exact) */
+#define MXFP4_PATH_GEMM 2  /* grouped GEMM on scaled-FP4 MFMA, activations as two MX-FP6 terms */
+
+/* Static text for a status code. */
+const char* mxfp4_status_string(int status);
+
+/* Detail text of the last failure on the calling thread ("" if none). */
+const char* mxfp4_last_error(void);
+
+/*
+ * Route tokens to experts and group the routed rows by expert.
+ * (README "Dense routing"; src/experts.linnet fn ranks / route / experts_of /
+ * weights_of; README "Loading": the tokens each expert was chosen for.)
+ *
+ *   logits      [T, E] bf16, or NULL.  Router logits.
+ *   ids_in      [T, k] i32, or NULL.   Given expert ids.
+ *               Exactly one of the two routes is taken:
+ *               - ids_in == NULL: topk_ids[t, s] = the expert of rank s among
+ *                 token t's logits, where an expert's rank counts the experts
+ *                 with a larger logit or an equal logit and a lower index
+ *                 (logits must be finite; logits is then required).
+ *               - ids_in != NULL: topk_ids = ids_in (slot order kept).  Ids must
+ *                 lie in [0, E) and be distinct per token; violations set bits in
+ *                 *error_word, an out-of-range id is written as -1 and its row is
+ *                 left out of the grouping.
+ *   T >= 0, 1 <= E <= MXFP4_MAX_EXPERTS, 1 <= k <= min(E, MXFP4_MAX_TOPK).
+ *   topk_ids    [T, k] i32 out.
+ *   gates       [T, k] f32 out, or NULL.  Written only when logits != NULL:
+ *               gates[t, s] = exp(l_s - max) / sum_j exp(l_j - max) over the k
+ *               logits at topk_ids[t, :] (fp32).
+ *   expert_offsets [E + 1] i32 out: exclusive prefix sum of the number of routed
+ *               rows per expert; expert_offsets[E] = number of grouped rows
+ *               (T * k when every id is valid).
+ *   sorted_rows [T * k] i32 out: the routed rows r = t * k + s, grouped by
+ *               expert (expert e's rows are sorted_rows[offsets[e] : offsets[e+1]])
+ *               and ascending within an expert.  Entries past offsets[E] are
+ *               not written.
+ *   error_word  [1] i32 out, or NULL: overwritten with the MXFP4_ROUTE_ERR_* bits
+ *               found (0 = none).
+ * One kernel launch (a single workgroup).  T = 0 writes zero offsets.
+ */
+int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k,
+                          int32_t* topk_ids, float* gates, int32_t* expert_offsets,
+                          int32_t* sorted_rows, int32_t* error_word, void* stream);
+
+/*
+ * Workspace bytes mxfp4_expert_proj needs for these sizes and this path
+ * (MXFP4_PATH_AUTO resolves exactly as mxfp4_expert_proj does).  0 means none.
+ * Returns (size_t)-1 for invalid sizes.
+ */
+size_t mxfp4_expert_proj_workspace_size(int T, int k, int K, int x_per_slot, int path);
+
+/*
+ * The routed expert projection.
+ * (README "MXFP4" for the weight format; src/experts.linnet fn forward_topk
+ * and forward_routed for the products; fn activate / down_bias_of for the
+ * per-expert bias rows.)
+ *
+ *   blocks  [E, N, K/32, 16] u8   MXFP4 codes, low nibble = even element.
+ *   scales  [E, N, K/32]     u8   E8M0 exponents (bias 127); bytes 0..254.
+ *   bias    [E, N] bf16, or NULL (no bias).
+ *   E, N, K: 1 <= E <= MXFP4_MAX_EXPERTS, N >= 1, K >= 32 and K % 32 == 0.
+ *   x       x_per_slot == 0: [T, K] bf16, one input per token shared by its k slots
+ *                            (gate/up);
+ *           x_per_slot != 0: [T, k, K] bf16, one input per routed row (down).
+ *           Values must be finite.
+ *   T >= 0, 1 <= k <= min(E, MXFP4_MAX_TOPK).
+ *   expert_offsets [E + 1], sorted_rows [T * k]: as produced by
+ *           mxfp4_moe_route_group.  Offsets outside [0, T * k] and rows outside
+ *           [0, T * k) are clamped or skipped on the device, never dereferenced.
+ *   out     [T, k, N] f32 out:
+ *           out[t, s, n] = bias[e, n] + sum_j W[e, n, j] * x_src[j],  e the expert
+ *           that row r = t * k + s is grouped under, W[e, n, j] =
+ *           e2m1(code) * 2 ** (scales[e, n, j / 32] - 127).  Rows absent from the
+ *           grouping are not written.
+ *   path    MXFP4_PATH_AUTO / _GEMV / _GEMM.  GEMV accumulates exact fp32
+ *           products.  GEMM feeds the weights to the MFMA as stored and splits
+ *           each bf16 activation block into two MX-FP6 (E2M3) terms; its error
+ *           stays within 2e-3 * sum_j |W x| + 1e-5 per output for inputs like
+ *           the model's (see the design notes).
+ *   workspace, workspace_bytes: device scratch of at least
+ *           mxfp4_expert_proj_workspace_size(T, k, K, x_per_slot, path) bytes,
+ *           16-byte aligned; may be NULL when that size is 0.  Calls that share
+ *           a workspace must be ordered on one stream.
+ * T = 0 returns MXFP4_OK and enqueues nothing.
+ */
+int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
+                      int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                      const int32_t* expert_offsets, const int32_t* sorted_rows, float* out,
+                      int path, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gate-weighted combine of the k projections of each token.
+ * (src/experts.linnet fn forward_topk: the sum over k in f32; fn down_bias_of:
+ * the down bias carries the router weights -- here the bias is already inside
+ * proj, so weighing proj weighs it too.)
+ *
+ *   proj  [T, k, N] f32, gates [T, k] f32, y [T, N] f32 out (overwritten):
+ *   y[t, n] = sum_{s = 0}^{k-1} gates[t, s] * proj[t, s, n], accumulated in f32
+ *   in slot order with fused multiply-adds.
+ *   T >= 0, k >= 1, N >= 1.  T = 0 returns MXFP4_OK and enqueues nothing.
+ */
+int moe_combine(const float* proj, const float* gates, int T, int k, int N, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_MOE_H */

@@ -10,7 +10,8 @@ machine without the library; calling any entry point without the library
 raises.
 """
 
-__all__ = ["mxfp4_moe_route_group", "mxfp4_expert_proj", "moe_combine", "library_path"]
+__all__ = ["mxfp4_moe_route_group", "mxfp4_expert_proj", "mxfp4_expert_proj_workspace_size", "moe_combine",
+           "library_path"]
 
 
 def __getattr__(name):

@@ -1,0 +1,175 @@
+// C ABI of the MXFP4 mixture-of-experts library: argument checks, the gfx950
+// device check, path selection and kernel dispatch.  Declarations and the
+// contract of each entry point are in include/mxfp4_moe.h.
+//
+// Every host-checkable precondition is tested before any HIP call, so a
+// rejected call enqueues nothing and the checks work on a host without a GPU
+// (the shape checks mirror the "checked before anything runs" convention of
+// the gpt-oss-20b files page, README "Loading").
+
+#include "mxfp4_moe.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MXFP4_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// gfx950 check of the current device, cached per device ordinal.
+constexpr int kMaxDevices = 64;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::mutex g_dev_mutex;
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MXFP4_ERR_UNSUPPORTED_DEVICE, "device ordinal %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev_state[dev] == 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+      g_dev_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+      if (g_dev_state[dev] == 2)
+        return fail(MXFP4_ERR_UNSUPPORTED_DEVICE, "device %d is %s, this library runs on gfx950 only", dev,
+                    prop.gcnArchName);
+    }
+    if (g_dev_state[dev] != 1) return fail(MXFP4_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  }
+  return MXFP4_OK;
+}
+
+int resolve_path(int path, int T, int k) {
+  if (path == MXFP4_PATH_AUTO) return ((long long)T * k <= 8) ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
+  return path;
+}
+
+bool gemv_fits(int T, int K) {
+  const long long maxm = T == 1 ? 1 : (T == 2 ? 2 : 4);
+  return maxm * K * 2 <= 65536;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp4_status_string(int status) {
+  switch (status) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_ERR_INVALID_ARG: return "invalid argument";
+    case MXFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXFP4_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case MXFP4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mxfp4_last_error(void) { return g_last_error; }
+
+int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k, int32_t* topk_ids,
+                          float* gates, int32_t* expert_offsets, int32_t* sorted_rows, int32_t* error_word,
+                          void* stream) {
+  g_last_error[0] = '\0';
+  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
+  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
+  if (k < 1 || k > E || k > MXFP4_MAX_TOPK)
+    return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, min(E = %d, %d)]", k, E, MXFP4_MAX_TOPK);
+  if ((long long)T * k > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "T * k overflows int32");
+  if (T > 0 && !logits && !ids_in) return fail(MXFP4_ERR_INVALID_ARG, "one of logits / ids_in must be given");
+  if (!expert_offsets) return fail(MXFP4_ERR_INVALID_ARG, "expert_offsets is NULL");
+  if (T > 0 && (!topk_ids || !sorted_rows)) return fail(MXFP4_ERR_INVALID_ARG, "topk_ids / sorted_rows is NULL");
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_route_group(logits, ids_in, T, E, k, topk_ids, gates, expert_offsets, sorted_rows,
+                                           error_word, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route_group launch");
+  return MXFP4_OK;
+}
+
+size_t mxfp4_expert_proj_workspace_size(int T, int k, int K, int x_per_slot, int path) {
+  if (T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
+  if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return (size_t)-1;
+  if (T == 0) return 0;
+  if (resolve_path(path, T, k) != MXFP4_PATH_GEMM) return 0;
+  return mxfp4::gemm_workspace_bytes(T, k, K, x_per_slot);
+}
+
+int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
+                      const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
+                      const int32_t* sorted_rows, float* out, int path, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_last_error[0] = '\0';
+  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
+  if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "K = %d must be a positive multiple of 32", K);
+  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
+  if (k < 1 || k > E || k > MXFP4_MAX_TOPK)
+    return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, min(E = %d, %d)]", k, E, MXFP4_MAX_TOPK);
+  if ((long long)T * k > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "T * k overflows int32");
+  if ((long long)E * N > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "E * N overflows int32");
+  if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return fail(MXFP4_ERR_INVALID_ARG, "path = %d unknown", path);
+  if (T == 0) return MXFP4_OK;
+  if (!blocks || !scales || !x || !expert_offsets || !sorted_rows || !out)
+    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
+  const int p = resolve_path(path, T, k);
+  if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
+    return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
+  if (p == MXFP4_PATH_GEMM) {
+    const size_t need = mxfp4::gemm_workspace_bytes(T, k, K, x_per_slot);
+    if (!workspace || workspace_bytes < need)
+      return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                  need);
+    if (!aligned16(workspace)) return fail(MXFP4_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e;
+  if (p == MXFP4_PATH_GEMV)
+    e = mxfp4::launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
+                                  out, static_cast<hipStream_t>(stream));
+  else
+    e = mxfp4::launch_expert_gemm(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
+                                  out, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "expert_proj launch");
+  return MXFP4_OK;
+}
+
+int moe_combine(const float* proj, const float* gates, int T, int k, int N, float* y, void* stream) {
+  g_last_error[0] = '\0';
+  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
+  if (k < 1) return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+  if (T == 0) return MXFP4_OK;
+  if (!proj || !gates || !y) return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_combine(proj, gates, T, k, N, y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MXFP4_OK;
+}
+
+}  // extern "C"

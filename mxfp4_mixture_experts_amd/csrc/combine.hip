@@ -1,0 +1,74 @@
+// Gate-weighted combine of a token's k expert outputs, for gfx950.
+//
+// gpt-oss-20b files page, src/experts.linnet fn forward_topk: the expert sum
+// is taken in f32; fn down_bias_of: the down bias is weighed by the router
+// weights (it is already part of each projection row here).
+//
+// y[t, n] = sum_s gates[t, s] * proj[t, s, n], one fused multiply-add per slot
+// in slot order, so the result does not depend on the launch shape.  The
+// kernel is a pure HBM stream: each thread owns 4 consecutive columns of one
+// token (128-bit loads and stores), the k gates of the token are read once
+// per thread from the cache.
+
+#include "kernels.h"
+#include "common.h"
+
+namespace mxfp4 {
+namespace {
+
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(
+    const float* __restrict__ proj, const float* __restrict__ gates, int T, int k, int N4,
+    float* __restrict__ y) {
+  const size_t total = (size_t)T * N4;
+  const size_t stride = (size_t)gridDim.x * kCombineThreads;
+  for (size_t i = (size_t)blockIdx.x * kCombineThreads + threadIdx.x; i < total; i += stride) {
+    const size_t t = i / N4;
+    const size_t c = i - t * N4;
+    const float4* p = reinterpret_cast<const float4*>(proj) + (t * k) * N4 + c;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < k; s++) {
+      const float g = gates[t * k + s];
+      const float4 v = load_nt(p + (size_t)s * N4);
+      acc.x = fmaf(g, v.x, acc.x);
+      acc.y = fmaf(g, v.y, acc.y);
+      acc.z = fmaf(g, v.z, acc.z);
+      acc.w = fmaf(g, v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(y)[i] = acc;
+  }
+}
+
+__global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
+    const float* __restrict__ proj, const float* __restrict__ gates, int T, int k, int N,
+    float* __restrict__ y) {
+  const size_t total = (size_t)T * N;
+  const size_t stride = (size_t)gridDim.x * kCombineThreads;
+  for (size_t i = (size_t)blockIdx.x * kCombineThreads + threadIdx.x; i < total; i += stride) {
+    const size_t t = i / N;
+    const size_t n = i - t * N;
+    float acc = 0.f;
+    for (int s = 0; s < k; s++) acc = fmaf(gates[t * k + s], proj[(t * k + s) * N + n], acc);
+    y[i] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* proj, const float* gates, int T, int k, int N, float* y,
+                          hipStream_t stream) {
+  const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(proj) | reinterpret_cast<uintptr_t>(y)) % 16 == 0);
+  const size_t items = (size_t)T * (vec ? N / 4 : N);
+  size_t blocks = (items + kCombineThreads - 1) / kCombineThreads;
+  if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
+  if (vec)
+    hipLaunchKernelGGL(combine_vec4_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
+                       gates, T, k, N / 4, y);
+  else
+    hipLaunchKernelGGL(combine_scalar_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
+                       gates, T, k, N, y);
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4

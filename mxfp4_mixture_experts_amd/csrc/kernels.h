@@ -1,0 +1,33 @@
+// Internal launchers of the gfx950 kernels.  Each enqueues on `stream` and
+// returns the hipError_t of the launch; the arguments have been checked by
+// the C ABI layer (capi.cpp) before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+// route_group.hip
+hipError_t launch_route_group(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k,
+                              int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
+                              int32_t* error_word, hipStream_t stream);
+
+// expert_gemv.hip
+hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
+                              int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                              const int32_t* offsets, const int32_t* sorted_rows, float* out,
+                              hipStream_t stream);
+
+// expert_gemm.hip
+size_t gemm_workspace_bytes(int T, int k, int K, int x_per_slot);
+hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
+                              int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                              const int32_t* offsets, const int32_t* sorted_rows, float* out,
+                              void* workspace, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const float* proj, const float* gates, int T, int k, int N, float* y,
+                          hipStream_t stream);
+
+}  // namespace mxfp4

@@ -1,0 +1,82 @@
+"""Device-side plumbing for one expert-projection workload.
+
+Uploads a synthetic problem's arrays to device memory, allocates the outputs
+and the workspace, and runs the hot path through the C ABI: route/group, the
+expert projection and (where the workload has one) the gate-weighted combine.
+No arithmetic happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _bf16_tensor(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class DeviceProblem:
+    """A synthetic MoEProblem resident in device memory, with its output buffers."""
+
+    def __init__(self, p, device="cuda:0", path=B.MXFP4_PATH_AUTO):
+        self.p = p
+        self.device = torch.device(device)
+        self.path = path
+        dev = self.device
+        self.blocks = torch.from_numpy(np.ascontiguousarray(p.blocks)).to(dev)
+        self.scales = torch.from_numpy(np.ascontiguousarray(p.scales)).to(dev)
+        self.bias = _bf16_tensor(p.bias, dev)
+        self.x = _bf16_tensor(p.x, dev)
+        self.logits = _bf16_tensor(p.logits, dev) if p.logits is not None else None
+        self.ids_in = torch.from_numpy(np.ascontiguousarray(p.ids_in, dtype=np.int32)).to(dev) if p.ids_in is not None else None
+        T, k, N, E = p.T, p.k, p.N, p.E
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=dev) if p.logits is not None else None
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        self.sorted_rows = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        self.error_word = torch.zeros((1,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, k, N), dtype=torch.float32, device=dev)
+        self.y = torch.empty((T, N), dtype=torch.float32, device=dev) if (p.combine and self.gates is not None) else None
+        self.set_path(path)
+
+    def set_path(self, path):
+        self.path = path
+        p = self.p
+        nbytes = B.mxfp4_expert_proj_workspace_size(p.T, p.k, p.K, p.x_per_slot, path)
+        self.workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device) if nbytes else None
+
+    def route_group(self, stream=None):
+        p = self.p
+        B.mxfp4_moe_route_group(self.logits, self.ids_in, p.T, p.E, p.k, self.topk_ids, self.gates, self.offsets,
+                                self.sorted_rows, self.error_word, stream)
+
+    def expert_proj(self, stream=None, blocks=None, scales=None):
+        p = self.p
+        B.mxfp4_expert_proj(self.blocks if blocks is None else blocks, self.scales if scales is None else scales,
+                            self.bias, p.E, p.N, p.K, self.x, p.x_per_slot, p.T, p.k, self.offsets,
+                            self.sorted_rows, self.out, self.path, self.workspace, stream)
+
+    def combine(self, stream=None):
+        if self.y is not None:
+            p = self.p
+            B.moe_combine(self.out, self.gates, p.T, p.k, p.N, self.y, stream)
+
+    def run(self, stream=None):
+        self.route_group(stream)
+        self.expert_proj(stream)
+        self.combine(stream)
+
+    def results(self):
+        torch.cuda.synchronize(self.device)
+        r = {
+            "ids": self.topk_ids.cpu().numpy(),
+            "offsets": self.offsets.cpu().numpy(),
+            "sorted_rows": self.sorted_rows.cpu().numpy(),
+            "error_word": int(self.error_word.cpu().item()),
+            "out": self.out.cpu().numpy(),
+        }
+        r["gates"] = self.gates.cpu().numpy() if self.gates is not None else None
+        r["y"] = self.y.cpu().numpy() if self.y is not None else None
+        return r

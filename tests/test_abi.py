@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every symbol include/*.h declares, and rejects bad
+arguments with the documented status before any HIP call.  No GPU needed."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from mxfp4_mixture_experts_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.library_path()), reason="library not built")
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const\s+char\s*\*|void)\s*\**\s*(\w+)\s*\(", src, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert {"mxfp4_moe_route_group", "mxfp4_expert_proj", "moe_combine"} <= names
+    assert set(B.ENTRY_POINTS) <= names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(B.library_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = B.load_library()
+    assert lib.mxfp4_status_string(0) == b"ok"
+    assert b"gfx950" in lib.mxfp4_status_string(3)
+
+
+def _route(lib, logits, ids, T, E, k, topk=1, off=1, rows=1):
+    p = ctypes.c_void_p
+    return lib.mxfp4_moe_route_group(logits and p(16), ids and p(16), T, E, k, topk and p(16), None,
+                                     off and p(16), rows and p(16), None, None)
+
+
+@pytest.mark.parametrize("args,why", [
+    ((0, 0, 4, 32, 4), "no logits and no ids"),
+    ((1, 0, -1, 32, 4), "negative T"),
+    ((1, 0, 4, 0, 1), "E = 0"),
+    ((1, 0, 4, 513, 4), "E above the limit"),
+    ((1, 0, 4, 32, 0), "k = 0"),
+    ((1, 0, 4, 4, 5), "k > E"),
+    ((1, 0, 4, 64, 33), "k above the limit"),
+])
+def test_route_group_rejects_bad_arguments(args, why):
+    lib = B.load_library()
+    assert _route(lib, *args) == 1, why
+    assert lib.mxfp4_last_error() != b""
+
+
+def test_route_group_rejects_missing_outputs():
+    lib = B.load_library()
+    assert _route(lib, 1, 0, 4, 32, 4, off=0) == 1
+    assert _route(lib, 1, 0, 4, 32, 4, rows=0) == 1
+
+
+def _proj(lib, E=32, N=64, K=128, T=4, k=4, path=0, ws=None, ws_bytes=0, ptr=16, x_per_slot=0):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.mxfp4_expert_proj(p, p, None, E, N, K, p, x_per_slot, T, k, p, p, p, path,
+                                 ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), 1), (dict(K=0), 1), (dict(N=0), 1), (dict(E=0), 1), (dict(k=33, E=64), 1),
+    (dict(k=5, E=4), 1), (dict(T=-1), 1), (dict(path=7), 1), (dict(ptr=0), 1), (dict(ptr=8), 1),
+    (dict(path=2, ws=None), 2), (dict(path=2, ws=ctypes.c_void_p(16), ws_bytes=10), 2),
+    (dict(path=1, K=32768, T=64, k=4), 1),
+])
+def test_expert_proj_rejects_bad_arguments(kw, status):
+    lib = B.load_library()
+    assert _proj(lib, **kw) == status
+
+
+def test_expert_proj_t0_is_a_noop():
+    lib = B.load_library()
+    assert _proj(lib, T=0, ptr=0) == 0
+
+
+def test_workspace_size():
+    lib = B.load_library()
+    ws = lib.mxfp4_expert_proj_workspace_size
+    assert ws(1, 4, 2880, 0, 1) == 0                 # GEMV needs none
+    assert ws(1, 4, 2880, 0, 0) == 0                 # auto picks GEMV for 4 rows
+    # GEMM: per quantized row 92 padded blocks of 48 code bytes + 2 scale bytes
+    n = ws(4096, 4, 2880, 0, 2)
+    assert n >= 4096 * 92 * 50 and n < 4096 * 92 * 50 + 256
+    assert ws(2048, 4, 2880, 1, 0) >= 8192 * 92 * 50
+    assert ws(4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
+
+
+def test_combine_rejects_bad_arguments():
+    lib = B.load_library()
+    p = ctypes.c_void_p(16)
+    assert lib.moe_combine(p, p, -1, 4, 8, p, None) == 1
+    assert lib.moe_combine(p, p, 4, 0, 8, p, None) == 1
+    assert lib.moe_combine(p, p, 4, 4, 0, p, None) == 1
+    assert lib.moe_combine(None, p, 4, 4, 8, p, None) == 1
+    assert lib.moe_combine(None, None, 0, 4, 8, None, None) == 0

@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing ids, expert offsets and grouped rows must match bit for bit; gates
+within 1e-6; every fp32 output within 2e-3 * sum|w x| + 1e-5 (bias excluded
+from the magnitude).  Small workloads are compared element by element; the
+model-size workloads on sampled outputs the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mxfp4_mixture_experts_amd import binding as B
+from mxfp4_mixture_experts_amd import synthetic as S
+from mxfp4_mixture_experts_amd.runner import DeviceProblem
+
+pytestmark = pytest.mark.gpu
+
+GATE_TOL = 1e-6
+PATHS = {0: "auto", 1: "gemv", 2: "gemm"}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def check_close(gpu, ref, mag, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    bound = O.parity_bound(mag)
+    worst = float((err / bound).max()) if err.size else 0.0
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{what}: {len(bad)} outputs outside the bound, worst err/bound {worst:.3g}, first at {bad[:3].tolist()}"
+    return worst
+
+
+def check_routing(g, ref):
+    np.testing.assert_array_equal(g["ids"], ref["ids"])
+    np.testing.assert_array_equal(g["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(g["sorted_rows"], ref["sorted_rows"])
+    if ref["gates"] is not None:
+        assert np.abs(g["gates"].astype(np.float64) - ref["gates"]).max() <= GATE_TOL
+
+
+def full_parity(p, path):
+    _announce(f"{p.name} path={PATHS[path]}")
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p, path=path)
+    dp.run()
+    g = dp.results()
+    assert g["error_word"] == 0
+    check_routing(g, ref)
+    worst = check_close(g["out"], ref["out"], ref["mag"], f"{p.name} out")
+    if "y" in ref:
+        assert g["y"] is not None
+        check_close(g["y"], ref["y"], ref["mag_y"], f"{p.name} y")
+    return worst
+
+
+# ----------------------------------------------------------------- small, element by element
+@pytest.mark.parametrize("path", [0, 1, 2])
+def test_tiny_config(path):
+    full_parity(S.make_config(0), path)
+
+
+SMALL_CASES = {
+    # name: make_custom kwargs
+    "ragged_shared_logits": dict(E=8, N=200, K=320, T=37, k=3, route="logits"),
+    "per_slot_ids_gates": dict(E=8, N=136, K=2880, T=50, k=4, x_per_slot=True, route="ids+logits"),
+    "zipf_per_slot": dict(E=32, N=300, K=256, T=300, k=4, x_per_slot=True, route="zipf+logits"),
+    "big_tiles_ragged": dict(E=4, N=260, K=416, T=300, k=2, route="logits"),
+    "one_expert": dict(E=1, N=1, K=32, T=5, k=1, route="logits"),
+    "one_token_top1": dict(E=16, N=70, K=64, T=1, k=1, route="logits"),
+    "wide_k": dict(E=6, N=64, K=4096, T=9, k=2, x_per_slot=True, route="ids"),
+}
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("case", sorted(SMALL_CASES))
+def test_small_cases(case, path):
+    p = S.make_custom(**SMALL_CASES[case])
+    p.name = case
+    full_parity(p, path)
+
+
+def test_paths_agree_closely():
+    """GEMV (exact products) and GEMM (two-term MX-FP6 activations) on the same input."""
+    p = S.make_custom(E=8, N=256, K=2880, T=24, k=4, route="logits")
+    _announce("paths agree")
+    outs = []
+    for path in (1, 2):
+        dp = DeviceProblem(p, path=path)
+        dp.run()
+        outs.append(dp.results()["out"].astype(np.float64))
+    ref = O.run_problem(p)
+    check_close(outs[1], outs[0], ref["mag"], "gemm vs gemv")
+
+
+# ----------------------------------------------------------------- edge cases
+def test_empty_batch():
+    _announce("T=0")
+    p = S.make_custom(E=8, N=64, K=64, T=0, k=2, route="logits")
+    dp = DeviceProblem(p)
+    dp.offsets.fill_(-7)
+    dp.run()
+    g = dp.results()
+    assert g["offsets"].tolist() == [0] * 9
+
+
+def test_given_ids_errors_are_flagged():
+    _announce("bad given ids")
+    p = S.make_custom(E=8, N=64, K=64, T=4, k=2, route="ids+logits")
+    p.ids_in = np.array([[0, 1], [2, 2], [9, 3], [4, -1]], np.int32)
+    dp = DeviceProblem(p, path=1)
+    dp.out.fill_(12345.0)
+    dp.run()
+    g = dp.results()
+    assert g["error_word"] == (B.MXFP4_ROUTE_ERR_ID_RANGE | B.MXFP4_ROUTE_ERR_ID_DUP)
+    assert g["ids"].tolist() == [[0, 1], [2, 2], [-1, 3], [4, -1]]
+    valid_rows = [0, 1, 2, 3, 5, 6]
+    assert g["offsets"][-1] == len(valid_rows)
+    assert sorted(g["sorted_rows"][:6].tolist()) == valid_rows
+    # rows left out of the grouping are not written
+    assert np.all(g["out"].reshape(8, 64)[[4, 7]] == 12345.0)
+    vals, mags = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, False, np.where(g["ids"] < 0, 0, g["ids"]),
+                                       np.repeat(valid_rows, 64), np.tile(np.arange(64), len(valid_rows)))
+    check_close(g["out"].reshape(8, 64)[valid_rows].reshape(-1), vals, mags, "valid rows")
+
+
+def test_deterministic_and_stream():
+    _announce("determinism + side stream")
+    p = S.make_custom(E=16, N=512, K=2880, T=64, k=4, x_per_slot=True, route="logits")
+    dp = DeviceProblem(p)
+    dp.run()
+    first = dp.results()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dp.out.zero_()
+        dp.y.zero_()
+        dp.run(stream=s)
+    s.synchronize()
+    second = dp.results()
+    for key in ("ids", "offsets", "sorted_rows", "gates", "out", "y"):
+        assert np.array_equal(first[key], second[key]), key
+
+
+# ----------------------------------------------------------------- model-size workloads (sampled)
+def _sample_pairs(rng, R, N, n):
+    rows = rng.integers(0, R, n)
+    cols = rng.integers(0, N, n)
+    rows[:4] = [0, R - 1, 0, R - 1]
+    cols[:4] = [0, N - 1, N - 1, 0]
+    return rows, cols
+
+
+@pytest.mark.parametrize("cfg,path", [(1, 0), (1, 2), (2, 0), (2, 1), (3, 0), (4, 0)])
+def test_model_size_config(cfg, path):
+    p = S.make_config(cfg)
+    _announce(f"{p.name} path={PATHS[path]} (sampled)")
+    if p.ids_in is not None:
+        ids = p.ids_in
+        gates = O.gates_for_ids(p.logits, ids)
+    else:
+        ids, gates = O.route_topk(p.logits, p.k)
+    offsets, rows_sorted = O.group_by_expert(ids, p.E)
+    dp = DeviceProblem(p, path=path)
+    dp.run()
+    g = dp.results()
+    assert g["error_word"] == 0
+    check_routing(g, dict(ids=ids, gates=gates, offsets=offsets, sorted_rows=rows_sorted))
+    R = p.T * p.k
+    rng = np.random.default_rng(1000 + cfg)
+    rows, cols = _sample_pairs(rng, R, p.N, 1500)
+    vals, mags = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, rows, cols)
+    check_close(g["out"].reshape(R, p.N)[rows, cols], vals, mags, f"{p.name} out")
+    if p.combine:
+        toks = rng.integers(0, p.T, 200)
+        cols = rng.integers(0, p.N, 200)
+        y_ref = np.zeros(200)
+        m_ref = np.zeros(200)
+        for s in range(p.k):
+            v, m = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, toks * p.k + s, cols)
+            y_ref += gates[toks, s] * v
+            m_ref += gates[toks, s] * m
+        check_close(g["y"][toks, cols], y_ref, m_ref, f"{p.name} y")
