@@ -1,0 +1,305 @@
+"""Throughput of the MXFP4 mixture-of-experts expert projection on one MI355X.
+
+A step is one pass of the hot path over one batch of seeded synthetic input:
+route + group (mxfp4_moe_route_group), the expert projection
+(mxfp4_expert_proj) and, for workloads that have one, the gate-weighted
+combine (moe_combine).  The headline workload is the gpt-oss-20b gate_up
+decode of one token (E=32 experts of [5760, 2880] MXFP4, top-4 from bf16
+router logits).  Inputs are resident in HBM before the timed region; every
+step reads a different copy of the expert weights (enough copies that one
+rotation touches >= 1 GiB) so that the 256 MB last-level cache cannot serve
+the weights.  The timed steps are replayed from a HIP graph.
+
+Prints one JSON line.  See --help for the options.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4 MFMA, published
+METRIC = "MXFP4 expert-proj HBM GB/s (decode) & TFLOP/s (prefill), % of MI355X roofline"
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_gemv_gate_up_decode_t1.traffic.txt")
+KERNEL_SOURCES = {
+    "expert_gemv": ["mxfp4_mixture_experts_amd/csrc/expert_gemv.hip", "mxfp4_mixture_experts_amd/csrc/common.h"],
+    "expert_gemm": ["mxfp4_mixture_experts_amd/csrc/expert_gemm.hip", "mxfp4_mixture_experts_amd/csrc/common.h"],
+}
+
+
+def kernel_source_hash(name: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, v = line.split(":", 1)
+                vals[key.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ accounting
+def algorithmic(p, used):
+    """Minimum bytes each stage must move and the flops of the projection; `used` is the
+    number of experts that received at least one routed row."""
+    KB = p.K // 32
+    R = p.T * p.k
+    weights = used * p.N * (KB * 16 + KB + 2)           # code blocks + scale bytes + bias
+    x = (R if p.x_per_slot else p.T) * p.K * 2
+    out = R * p.N * 4
+    grouping_in = (p.E + 1) * 4 + R * 4
+    proj = weights + x + out + grouping_in
+    route = (p.T * p.E * 2 if p.logits is not None else 0) + (R * 4 if p.ids_in is not None else 0)
+    route += R * 4 + (R * 4 if p.logits is not None else 0) + (p.E + 1) * 4 + R * 4
+    comb = (R * p.N * 4 + R * 4 + p.T * p.N * 4) if (p.combine and p.logits is not None) else 0
+    flops = 2.0 * R * p.N * p.K
+    return {"proj": proj, "route": route, "combine": comb, "step": proj + route + comb, "flops": flops,
+            "experts_touched": int(used), "weight_bytes": weights}
+
+
+# ------------------------------------------------------------------ GPU measurement
+class Workload:
+    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0):
+        import torch
+        from mxfp4_mixture_experts_amd import synthetic as S
+        from mxfp4_mixture_experts_amd.runner import DeviceProblem
+        self.torch = torch
+        self.p = S.make_config(cfg_index)
+        self.dp = DeviceProblem(self.p, device="cuda:0", path=path)
+        self.dp.route_group()            # the device's own routing decides which experts are touched
+        counts = torch.diff(self.dp.offsets.to(torch.int64)).cpu().numpy()
+        self.acc = algorithmic(self.p, int((counts > 0).sum()))
+        touched = max(self.acc["weight_bytes"], 1)
+        self.copies = max(1, math.ceil(rotate_bytes / touched))
+        self.weights = [(self.dp.blocks, self.dp.scales)]
+        for _ in range(self.copies - 1):
+            self.weights.append((self.dp.blocks.clone(), self.dp.scales.clone()))
+        torch.cuda.synchronize()
+
+    def step(self, i, stream=None):
+        b, s = self.weights[i % self.copies]
+        self.dp.route_group(stream)
+        self.dp.expert_proj(stream, blocks=b, scales=s)
+        self.dp.combine(stream)
+
+    def proj_only(self, i, stream=None):
+        b, s = self.weights[i % self.copies]
+        self.dp.expert_proj(stream, blocks=b, scales=s)
+
+    def capture(self, fn, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)                      # one eager call on the capture stream before capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g):
+        """(event ms, wall s) of one replay, bracketed by synchronisation."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return e0.elapsed_time(e1), t1 - t0
+
+
+def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None):
+    """Time `steps` whole-path steps and, separately, back-to-back launches of the
+    projection alone (for the kernel's roofline)."""
+    w = Workload(cfg_index, rotate_bytes, path)
+    for i in range(warmup):
+        w.step(i)
+    w.torch.cuda.synchronize()
+    g_steps = w.capture(w.step, steps)
+    g_steps.replay()                      # untimed: first replay of the instantiated graph
+    ms_total, wall = w.time_graph(g_steps)
+    kreps = kernel_reps or steps
+    g_proj = w.capture(w.proj_only, kreps)
+    g_proj.replay()
+    ms_proj, _ = w.time_graph(g_proj)
+    res = {
+        "p": w.p, "acc": w.acc, "copies": w.copies, "steps": steps,
+        "ms_per_step": ms_total / steps, "wall_s": wall,
+        "proj_us": 1e3 * ms_proj / kreps,
+    }
+    del g_steps, g_proj, w
+    return res
+
+
+def describe(p):
+    name = {
+        "tiny": "tiny",
+        "gate_up_decode_t1": "gpt-oss-20b gate_up decode",
+        "down_decode_t64": "gpt-oss-20b down decode",
+        "gate_up_prefill_t4096": "gpt-oss-20b gate_up prefill",
+        "down_prefill_zipf_t2048": "gpt-oss-20b down prefill, Zipf(1.2) routing",
+    }[p.name]
+    return (f"{name}: E={p.E} N={p.N} K={p.K} T={p.T} top-{p.k}, MXFP4 blocks [{p.E},{p.N},{p.K // 32},16] "
+            f"+ E8M0 scales, bf16 x {'[T,k,K]' if p.x_per_slot else '[T,K]'}, fp32 out [T,k,N]"
+            + (" + combine [T,N]" if p.combine else ""))
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(cfg_index, reps=2):
+    """The oracle as it stands, on this host, one BLAS thread, on the whole headline workload."""
+    from threadpoolctl import threadpool_limits
+    import oracle.moe_oracle as O
+    from mxfp4_mixture_experts_amd import synthetic as S
+    p = S.make_config(cfg_index)
+    ids = p.ids_in if p.ids_in is not None else O.route_topk(p.logits, p.k)[0]
+    acc = algorithmic(p, np.unique(ids).size)
+    best = float("inf")
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            O.run_problem(p)
+            best = min(best, time.perf_counter() - t0)
+    return {"value": round(acc["step"] / best / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole {p.name} step (route, group, projection{', combine' if p.combine else ''}) "
+                      f"in float64 numpy, best of {reps}, {best:.2f} s per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default 1: gate_up decode T=1)")
+    ap.add_argument("--rotate-bytes", type=int, default=ROTATE_BYTES)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other model-size workloads")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="run N plain 256 MiB device copies first (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from mxfp4_mixture_experts_amd import binding as B
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    B.load_library()
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.calibrate_copy):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    head = measure(args.config, args.steps, args.warmup, args.rotate_bytes)
+    p, acc = head["p"], head["acc"]
+    kernel = "expert_gemv" if p.T * p.k <= 8 else "expert_gemm"
+    gbs = acc["step"] / (head["ms_per_step"] * 1e-3) / 1e9
+    proj_gbs = acc["proj"] / (head["proj_us"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": describe(p),
+            "seed": 0,
+            "path": "route_group + expert_proj(auto: " + ("GEMV" if kernel == "expert_gemv" else "GEMM") + ")"
+                    + (" + combine" if p.combine else ""),
+            "algorithmic_bytes_per_step": acc["step"],
+            "experts_touched": acc["experts_touched"],
+            "weight_copies_rotated": head["copies"],
+            "timing": "HIP graph replay of the timed steps; events on the replay stream",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(proj_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(proj_gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(kernel),
+            "kernel_us": round(head["proj_us"], 3),
+            "algorithmic_bytes_per_launch": acc["proj"],
+        },
+    }
+    if not args.no_secondary:
+        sec = []
+        for cfg, steps in ((2, 100), (3, 20), (4, 40)):
+            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps)
+            a = r["acc"]
+            t_step = r["ms_per_step"] * 1e-3
+            t_proj = r["proj_us"] * 1e-6
+            roof_t = max(a["flops"] / (MXFP4_PEAK_TFLOPS * 1e12), a["step"] / (HBM_PEAK_GBS * 1e9))
+            sec.append({
+                "workload": describe(r["p"]),
+                "ms_per_step": round(r["ms_per_step"], 4),
+                "step_GBps": round(a["step"] / t_step / 1e9, 1),
+                "step_TFLOPs": round(a["flops"] / t_step / 1e12, 2),
+                "proj_us": round(r["proj_us"], 2),
+                "proj_GBps": round(a["proj"] / t_proj / 1e9, 1),
+                "proj_TFLOPs": round(a["flops"] / t_proj / 1e12, 2),
+                "proj_frac_hbm": round(a["proj"] / t_proj / 1e9 / HBM_PEAK_GBS, 4),
+                "proj_frac_mxfp4_peak": round(a["flops"] / t_proj / 1e12 / MXFP4_PEAK_TFLOPS, 4),
+                "step_frac_combined_roofline": round(roof_t / t_step, 4),
+                "weight_copies_rotated": r["copies"],
+            })
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,8 +60,8 @@ typedef enum {
 #define MXFP4_MAX_TOPK 32
 
 /* Projection paths for mxfp4_expert_proj. */
-#define MXFP4_PATH_AUTO 0  /* GEMV when T * k <= 8, grouped GEMM otherwise */
-#define MXFP4_PATH_GEMV 1  /* decode GEMV: 128-bit weight streaming, fp32 products (exact) */
+#define MXFP4_PATH_AUTO 0  /* GEMV while T * k <= 16 * min(E, T * k), grouped GEMM otherwise */
+#define MXFP4_PATH_GEMV 1  /* decode GEMV: 128-bit weight streaming, exact bf16 products, fp32 sums */
 #define MXFP4_PATH_GEMM 2  /* grouped GEMM on scaled-FP4 MFMA, activations as two MX-FP6 terms */
 
 /* Static text for a status code. */
@@ -111,7 +111,7 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
  * (MXFP4_PATH_AUTO resolves exactly as mxfp4_expert_proj does).  0 means none.
  * Returns (size_t)-1 for invalid sizes.
  */
-size_t mxfp4_expert_proj_workspace_size(int T, int k, int K, int x_per_slot, int path);
+size_t mxfp4_expert_proj_workspace_size(int E, int T, int k, int K, int x_per_slot, int path);
 
 /*
  * The routed expert projection.
@@ -136,13 +136,15 @@ size_t mxfp4_expert_proj_workspace_size(int T, int k, int K, int x_per_slot, int
  *           that row r = t * k + s is grouped under, W[e, n, j] =
  *           e2m1(code) * 2 ** (scales[e, n, j / 32] - 127).  Rows absent from the
  *           grouping are not written.
- *   path    MXFP4_PATH_AUTO / _GEMV / _GEMM.  GEMV accumulates exact fp32
- *           products.  GEMM feeds the weights to the MFMA as stored and splits
+ *   path    MXFP4_PATH_AUTO / _GEMV / _GEMM.  GEMV multiplies exact bf16
+ *           weights (the E2M1 value times the E8M0 factor) by the bf16 inputs on
+ *           the bf16 MFMA and sums in fp32; it needs K <= 5088 when T > 4
+ *           (its LDS staging).  GEMM feeds the weights to the MFMA as stored and splits
  *           each bf16 activation block into two MX-FP6 (E2M3) terms; its error
  *           stays within 2e-3 * sum_j |W x| + 1e-5 per output for inputs like
  *           the model's (see the design notes).
  *   workspace, workspace_bytes: device scratch of at least
- *           mxfp4_expert_proj_workspace_size(T, k, K, x_per_slot, path) bytes,
+ *           mxfp4_expert_proj_workspace_size(E, T, k, K, x_per_slot, path) bytes,
  *           16-byte aligned; may be NULL when that size is 0.  Calls that share
  *           a workspace must be ordered on one stream.
  * T = 0 returns MXFP4_OK and enqueues nothing.

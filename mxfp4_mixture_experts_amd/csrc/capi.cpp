@@ -62,15 +62,17 @@ int check_device() {
   return MXFP4_OK;
 }
 
-int resolve_path(int path, int T, int k) {
-  if (path == MXFP4_PATH_AUTO) return ((long long)T * k <= 8) ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
-  return path;
+// The GEMV streams each used expert's weights once per 16 routed rows; the
+// grouped GEMM pays a quantization pass but runs at the MX-FP4 MFMA rate.  The
+// GEMV wins while the routed rows per expert stay around 16 or fewer.
+int resolve_path(int path, int T, int k, int E) {
+  if (path != MXFP4_PATH_AUTO) return path;
+  const long long R = (long long)T * k;
+  const long long used = R < E ? R : E;
+  return R <= 16 * used ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
 }
 
-bool gemv_fits(int T, int K) {
-  const long long maxm = T == 1 ? 1 : (T == 2 ? 2 : 4);
-  return maxm * K * 2 <= 65536;
-}
+bool gemv_fits(int T, int K) { return mxfp4::gemv_lds_bytes(T, K) <= 160 * 1024 - 1024; }
 
 }  // namespace
 
@@ -109,11 +111,11 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
   return MXFP4_OK;
 }
 
-size_t mxfp4_expert_proj_workspace_size(int T, int k, int K, int x_per_slot, int path) {
-  if (T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
+size_t mxfp4_expert_proj_workspace_size(int E, int T, int k, int K, int x_per_slot, int path) {
+  if (E < 1 || E > MXFP4_MAX_EXPERTS || T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
   if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return (size_t)-1;
   if (T == 0) return 0;
-  if (resolve_path(path, T, k) != MXFP4_PATH_GEMM) return 0;
+  if (resolve_path(path, T, k, E) != MXFP4_PATH_GEMM) return 0;
   return mxfp4::gemm_workspace_bytes(T, k, K, x_per_slot);
 }
 
@@ -135,7 +137,7 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
   if (!blocks || !scales || !x || !expert_offsets || !sorted_rows || !out)
     return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
-  const int p = resolve_path(path, T, k);
+  const int p = resolve_path(path, T, k, E);
   if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
     return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
   if (p == MXFP4_PATH_GEMM) {

@@ -14,6 +14,7 @@ hipError_t launch_route_group(const uint16_t* logits, const int32_t* ids_in, int
                               int32_t* error_word, hipStream_t stream);
 
 // expert_gemv.hip
+size_t gemv_lds_bytes(int T, int K);
 hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
                               int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
                               const int32_t* offsets, const int32_t* sorted_rows, float* out,

@@ -1,5 +1,5 @@
 // Router top-k, softmax gates and stable grouping of the routed rows by
-// expert, in one single-workgroup kernel for gfx950.
+// expert, for gfx950.
 //
 // Routing follows the gpt-oss-20b files page, README "Dense routing" and
 // src/experts.linnet fn ranks / route / experts_of / weights_of: an expert's
@@ -9,142 +9,196 @@
 // expert was chosen for, sorted by expert) is a stable counting sort of the
 // rows r = t * k + s.
 //
-// Layout of the work inside the one workgroup of 1024 threads (16 waves):
-//   phase 1  one thread per token: k selection passes over its E logits,
-//            each pass taking the best expert that comes after the previous
-//            pick in (logit desc, index asc) order -- O(k * E), no sort state;
-//   phase 2  each wave owns a contiguous range of rows and counts, per
-//            64-row tile, the lanes sharing an expert (a ballot per id bit
-//            gives each lane the mask of its peers); the tile's leader lane
-//            adds the count into the wave's LDS counter of that expert;
-//   phase 3  per expert, the wave counters become running bases: expert start
-//            (exclusive scan over experts) plus the counts of earlier waves;
-//   phase 4  each wave walks its tiles again in order and scatters row r to
-//            base + (peers below it); the leader then advances the base.
-// Because waves own contiguous row ranges in order and lanes are ranked by
-// lane index, the rows of each expert come out in ascending order.
+// Routing: one wave per token.  Lane e holds expert e's logit (lane e + 64 i
+// for more than 64 experts); every lane counts the experts that beat its own
+// by broadcasting each logit in turn with v_readlane, so the rank definition
+// above is evaluated directly and in parallel.  The lane whose rank is s
+// writes slot s; the gates come from a wave max and a wave sum.
+//
+// Grouping, in one workgroup of 16 waves: each wave owns a contiguous range of
+// rows and loads its ids up front; per 64-row tile a ballot per id bit gives
+// each lane the mask of lanes sharing its expert; the tile's lowest such lane
+// adds the count into the wave's LDS counter of that expert.  An exclusive scan
+// over experts, plus the counts of earlier waves, turns the counters into
+// bases; a second walk scatters row r to base + (peers below it).  Waves own
+// row ranges in order and lanes are ranked by index, so each expert's rows
+// come out in ascending order.
+//
+// Small batches (T <= 256) run both parts in one single-workgroup kernel.
+// Larger batches route with many workgroups and then group in a second,
+// single-workgroup launch.  A row whose given id is out of range is written
+// as -1 and left out of the grouping; a repeated given id is flagged to the
+// grouping pass in bit 30 of the id (cleared again there).
 
 #include "kernels.h"
 #include "common.h"
+#include "mxfp4_moe.h"
 #include <math.h>
 
 namespace mxfp4 {
 namespace {
 
-constexpr int kRgThreads = 1024;
-constexpr int kRgWaves = kRgThreads / 64;
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / 64;
+constexpr int kTilesPerLoad = 16;       // 64-row tiles whose ids a wave loads at once
+constexpr int kExpertChunks = 8;        // 64 experts per lane chunk: E <= 512
+constexpr int kSmallT = 256;            // single-kernel path up to this many tokens
+constexpr int kRouteThreads = 256;      // multi-workgroup routing: 4 waves, 4 tokens per wave
+constexpr int kTokensPerRouteWave = 4;
+constexpr int32_t kDupFlag = 1 << 30;
 
-__device__ __forceinline__ float logit_at(const uint16_t* row, int e) {
-  return bf16_bits_to_f32(row[e]);
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
 }
 
-// gates over the k logits at ids[0..k) of one token (all ids valid)
-__device__ void write_gates(const uint16_t* lrow, const int32_t* ids, int k, float* g) {
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Route token t with the calling wave; returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
+template <int EC>
+__device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int t, int E,
+                           int k, int lane, int32_t* __restrict__ topk_ids, float* __restrict__ gates) {
+  int32_t* ids = topk_ids + (size_t)t * k;
+  const uint16_t* lrow = logits ? logits + (size_t)t * E : nullptr;
+  if (ids_in) {
+    // lane s < k holds the given id of slot s
+    const int32_t* given = ids_in + (size_t)t * k;
+    const int e = lane < k ? given[lane] : -1;
+    const bool in_range = lane < k && (unsigned)e < (unsigned)E;
+    bool dup = false;
+    for (int j = 0; j < k; j++) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      dup |= (lane < k && j != lane && ej == e && in_range);
+    }
+    const uint64_t bad = __ballot(lane < k && !in_range);
+    const uint64_t dups = __ballot(dup);
+    if (lane < k) ids[lane] = in_range ? (e | (dup ? kDupFlag : 0)) : -1;
+    if (gates && lrow && bad == 0) {
+      const float l = lane < k ? bf16_bits_to_f32(lrow[in_range ? e : 0]) : -INFINITY;
+      const float mx = wave_max(l);
+      const float num = lane < k ? expf(l - mx) : 0.f;
+      const float sum = wave_sum(num);
+      if (lane < k) gates[(size_t)t * k + lane] = num / sum;
+    }
+    return (bad ? MXFP4_ROUTE_ERR_ID_RANGE : 0) | (dups ? MXFP4_ROUTE_ERR_ID_DUP : 0);
+  }
+  float l[EC];
+  int rank[EC];
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const int e = lane + 64 * i;
+    l[i] = bf16_bits_to_f32(lrow[min(e, E - 1)]);  // unconditional load: no branch per load
+    if (e >= E) l[i] = -INFINITY;
+    rank[i] = 0;
+  }
+  // rank[e] = #{j : l_j > l_e or (l_j == l_e and j < e)}
+#pragma unroll
+  for (int jc = 0; jc < EC; jc++) {
+    const int jn = min(64, E - 64 * jc);
+    for (int jj = 0; jj < jn; jj++) {
+      const float lj = readlane_f(l[jc], jj);
+      const int j = 64 * jc + jj;
+#pragma unroll
+      for (int i = 0; i < EC; i++) {
+        const int e = lane + 64 * i;
+        rank[i] += (lj > l[i] || (lj == l[i] && j < e)) ? 1 : 0;
+      }
+    }
+  }
+  // slot s <- the expert of rank s; the largest kept logit has rank 0
   float mx = -INFINITY;
-  for (int s = 0; s < k; s++) mx = fmaxf(mx, logit_at(lrow, ids[s]));
-  float sum = 0.f;
-  for (int s = 0; s < k; s++) sum += expf(logit_at(lrow, ids[s]) - mx);
-  for (int s = 0; s < k; s++) g[s] = expf(logit_at(lrow, ids[s]) - mx) / sum;
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const int e = lane + 64 * i;
+    const bool top = e < E && rank[i] == 0;
+    const uint64_t m = __ballot(top);
+    if (m) mx = readlane_f(l[i], __ffsll((long long)m) - 1);
+  }
+  float num[EC];
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const int e = lane + 64 * i;
+    const bool kept = e < E && rank[i] < k;
+    num[i] = kept ? expf(l[i] - mx) : 0.f;
+    part += num[i];
+    if (kept) ids[rank[i]] = e;
+  }
+  if (gates) {
+    const float sum = wave_sum(part);
+#pragma unroll
+    for (int i = 0; i < EC; i++) {
+      const int e = lane + 64 * i;
+      if (e < E && rank[i] < k) gates[(size_t)t * k + rank[i]] = num[i] / sum;
+    }
+  }
+  // finite logits always give k experts; a NaN breaks the order
+  int seen = 0;
+#pragma unroll
+  for (int i = 0; i < EC; i++) seen += __popcll(__ballot(lane + 64 * i < E && rank[i] < k));
+  return seen == k ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
 }
 
-__global__ __launch_bounds__(kRgThreads) void route_group_kernel(
-    const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int T, int E, int k,
-    int32_t* __restrict__ topk_ids, float* __restrict__ gates, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ error_word) {
-  extern __shared__ int lds[];
-  int* cnt = lds;                       // [kRgWaves][E] counters, later running bases
-  int* start = lds + kRgWaves * E;      // [E] expert start offsets
-  __shared__ int err_sh;
-  __shared__ int total_sh;
-
+// Grouping of the R = T * k rows by the single workgroup that calls it.
+// cnt: LDS [kGroupWaves][E] zeroed; start: LDS [E].  Returns the error bits
+// found in the ids (range: negative ids; dup: flagged ids, whose flag is
+// cleared in place).
+__device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t* __restrict__ offsets,
+                          int32_t* __restrict__ sorted_rows, int* cnt, int* start, int* total_sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-
-  for (int i = tid; i < kRgWaves * E; i += kRgThreads) cnt[i] = 0;
-  if (tid == 0) err_sh = 0;
-  __syncthreads();
-
-  // ---------------- phase 1: routing, one thread per token
-  int errbits = 0;
-  for (int t = tid; t < T; t += kRgThreads) {
-    int32_t* ids = topk_ids + (size_t)t * k;
-    const uint16_t* lrow = logits ? logits + (size_t)t * E : nullptr;
-    bool all_valid = true;
-    if (ids_in) {
-      const int32_t* given = ids_in + (size_t)t * k;
-      for (int s = 0; s < k; s++) {
-        int e = given[s];
-        if ((unsigned)e >= (unsigned)E) {
-          errbits |= 1;
-          all_valid = false;
-          e = -1;
-        } else {
-          for (int s2 = 0; s2 < s; s2++)
-            if (given[s2] == e) errbits |= 2;
-        }
-        ids[s] = e;
-      }
-    } else {
-      float prev_l = INFINITY;
-      int prev_e = -1;
-      for (int s = 0; s < k; s++) {
-        float best_l = -INFINITY;
-        int best_e = -1;
-        for (int e = 0; e < E; e++) {
-          const float l = logit_at(lrow, e);
-          const bool after_prev = (l < prev_l) || (l == prev_l && e > prev_e);
-          const bool better = (best_e < 0) || (l > best_l);  // equal: keep the lower index
-          if (after_prev && better) {
-            best_l = l;
-            best_e = e;
-          }
-        }
-        if (best_e < 0) {
-          errbits |= 1;
-          all_valid = false;
-        }
-        ids[s] = best_e;
-        prev_l = best_l;
-        prev_e = best_e;
-      }
-    }
-    if (gates && lrow && all_valid) write_gates(lrow, ids, k, gates + (size_t)t * k);
-  }
-  if (errbits) atomicOr(&err_sh, errbits);
-  __syncthreads();  // topk_ids of every token visible to the whole workgroup
-
-  // ---------------- phase 2: per-wave, per-expert counts
-  const int R = T * k;
   int ebits = 1;
   while ((1 << ebits) < E) ebits++;
-  const int per_wave = ((R + kRgWaves * 64 - 1) / (kRgWaves * 64)) * 64;
+  const int per_wave = (R + kGroupWaves * 64 - 1) / (kGroupWaves * 64) * 64;
   const int w_begin = min(R, wave * per_wave);
   const int w_end = min(R, w_begin + per_wave);
+  int errbits = 0;
 
-  for (int base = w_begin; base < w_end; base += 64) {
-    const int r = base + lane;
-    const int e = (r < w_end) ? topk_ids[r] : -1;
-    const bool valid = e >= 0;
-    uint64_t peers = wave_ballot(valid);
-    for (int b = 0; b < ebits; b++) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = wave_ballot(bit);
-      peers &= bit ? m : ~m;
+  // ---- count (and clean the repeat flags)
+  for (int base = w_begin; base < w_end; base += 64 * kTilesPerLoad) {
+    int ev[kTilesPerLoad];
+#pragma unroll
+    for (int i = 0; i < kTilesPerLoad; i++) {
+      const int r = base + 64 * i + lane;
+      ev[i] = topk_ids[min(r, w_end - 1)];  // unconditional load, masked below
+      if (r >= w_end) ev[i] = -1;
     }
-    if (valid && lanes_below(peers) == 0) cnt[wave * E + e] += __popcll(peers);
+#pragma unroll
+    for (int i = 0; i < kTilesPerLoad; i++) {
+      if (base + 64 * i >= w_end) continue;  // wave-uniform
+      const int r = base + 64 * i + lane;
+      if (r < w_end) {
+        if (ev[i] < 0) errbits |= MXFP4_ROUTE_ERR_ID_RANGE;
+        if (ev[i] >= 0 && (ev[i] & kDupFlag)) {
+          errbits |= MXFP4_ROUTE_ERR_ID_DUP;
+          ev[i] &= ~kDupFlag;
+          topk_ids[r] = ev[i];
+        }
+      }
+      const int e = ev[i];
+      const bool valid = e >= 0;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < ebits; b++) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      if (valid && lanes_below(peers) == 0) cnt[wave * E + e] += __popcll(peers);
+    }
   }
   __syncthreads();
 
-  // ---------------- phase 3: expert starts and per-wave running bases
+  // ---- expert starts and per-wave running bases
   if (wave == 0) {
     int carry = 0;
     for (int c0 = 0; c0 < E; c0 += 64) {
       const int e = c0 + lane;
       int tot = 0;
       if (e < E)
-        for (int w = 0; w < kRgWaves; w++) tot += cnt[w * E + e];
-      // inclusive scan over the 64 lanes
+        for (int w = 0; w < kGroupWaves; w++) tot += cnt[w * E + e];
       int inc = tot;
       for (int d = 1; d < 64; d <<= 1) {
         const int o = __shfl_up(inc, d, 64);
@@ -153,46 +207,133 @@ __global__ __launch_bounds__(kRgThreads) void route_group_kernel(
       if (e < E) start[e] = carry + inc - tot;
       carry += __shfl(inc, 63, 64);
     }
-    if (lane == 0) total_sh = carry;
+    if (lane == 0) *total_sh = carry;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kRgThreads) {
+  for (int e = tid; e < E; e += kGroupThreads) {
     int b = start[e];
     offsets[e] = b;
-    for (int w = 0; w < kRgWaves; w++) {
+    for (int w = 0; w < kGroupWaves; w++) {
       const int c = cnt[w * E + e];
       cnt[w * E + e] = b;
       b += c;
     }
   }
-  if (tid == 0) {
-    offsets[E] = total_sh;
-    if (error_word) *error_word = err_sh;
-  }
+  if (tid == 0) offsets[E] = *total_sh;
   __syncthreads();
 
-  // ---------------- phase 4: stable scatter
-  for (int base = w_begin; base < w_end; base += 64) {
-    const int r = base + lane;
-    const int e = (r < w_end) ? topk_ids[r] : -1;
-    const bool valid = e >= 0;
-    uint64_t peers = wave_ballot(valid);
-    for (int b = 0; b < ebits; b++) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = wave_ballot(bit);
-      peers &= bit ? m : ~m;
+  // ---- stable scatter
+  for (int base = w_begin; base < w_end; base += 64 * kTilesPerLoad) {
+    int ev[kTilesPerLoad];
+#pragma unroll
+    for (int i = 0; i < kTilesPerLoad; i++) {
+      const int r = base + 64 * i + lane;
+      ev[i] = topk_ids[min(r, w_end - 1)];
+      if (r >= w_end) ev[i] = -1;
     }
-    const int below = lanes_below(peers);
-    int pos = 0;
-    if (valid) pos = cnt[wave * E + e] + below;
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      sorted_rows[pos] = r;
-      if (below == 0) cnt[wave * E + e] = pos + __popcll(peers);
+#pragma unroll
+    for (int i = 0; i < kTilesPerLoad; i++) {
+      if (base + 64 * i >= w_end) continue;  // wave-uniform
+      const int r = base + 64 * i + lane;
+      const int e = ev[i];
+      const bool valid = e >= 0;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < ebits; b++) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      const int below = lanes_below(peers);
+      int pos = 0;
+      if (valid) pos = cnt[wave * E + e] + below;
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        sorted_rows[pos] = r;
+        if (below == 0) cnt[wave * E + e] = pos + __popcll(peers);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
+  return errbits;
+}
+
+// T <= kSmallT: routing and grouping in one workgroup.
+template <int EC>
+__global__ __launch_bounds__(kGroupThreads) void route_group_small_kernel(
+    const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int T, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ gates, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ error_word) {
+  extern __shared__ int lds[];
+  int* cnt = lds;
+  int* start = lds + kGroupWaves * E;
+  __shared__ int err_sh;
+  __shared__ int total_sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) cnt[i] = 0;
+  if (tid == 0) err_sh = 0;
+  int errbits = 0;
+  for (int t = wave; t < T; t += kGroupWaves)
+    errbits |= route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates);
+  __syncthreads();  // the routed ids of every token visible to the whole workgroup
+  errbits |= group_rows(topk_ids, T * k, E, offsets, sorted_rows, cnt, start, &total_sh);
+  if (errbits) atomicOr(&err_sh, errbits);
+  __syncthreads();
+  if (tid == 0 && error_word) *error_word = err_sh;
+}
+
+// T > kSmallT, first launch: routing, one wave per token, many workgroups.
+template <int EC>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const uint16_t* __restrict__ logits,
+                                                             const int32_t* __restrict__ ids_in, int T, int E,
+                                                             int k, int32_t* __restrict__ topk_ids,
+                                                             float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int w = (blockIdx.x * kRouteThreads + threadIdx.x) >> 6;
+  for (int i = 0; i < kTokensPerRouteWave; i++) {
+    const int t = w * kTokensPerRouteWave + i;
+    if (t < T) route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates);
+  }
+}
+
+// T > kSmallT, second launch: grouping (range errors show as -1 ids, repeats as flagged ids).
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restrict__ topk_ids, int R, int E,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_rows,
+                                                              int32_t* __restrict__ error_word) {
+  extern __shared__ int lds[];
+  int* cnt = lds;
+  int* start = lds + kGroupWaves * E;
+  __shared__ int err_sh;
+  __shared__ int total_sh;
+  for (int i = threadIdx.x; i < kGroupWaves * E; i += kGroupThreads) cnt[i] = 0;
+  if (threadIdx.x == 0) err_sh = 0;
+  __syncthreads();
+  const int errbits = group_rows(topk_ids, R, E, offsets, sorted_rows, cnt, start, &total_sh);
+  if (errbits) atomicOr(&err_sh, errbits);
+  __syncthreads();
+  if (threadIdx.x == 0 && error_word) *error_word = err_sh;
+}
+
+template <int EC>
+hipError_t launch_ec(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k, int32_t* topk_ids,
+                     float* gates, int32_t* offsets, int32_t* sorted_rows, int32_t* error_word, hipStream_t stream) {
+  const size_t lds_bytes = (size_t)(kGroupWaves + 1) * E * sizeof(int);
+  if (T <= kSmallT) {
+    hipLaunchKernelGGL(route_group_small_kernel<EC>, dim3(1), dim3(kGroupThreads), lds_bytes, stream, logits, ids_in,
+                       T, E, k, topk_ids, gates, offsets, sorted_rows, error_word);
+    return hipGetLastError();
+  }
+  const int tokens_per_block = (kRouteThreads / 64) * kTokensPerRouteWave;
+  hipLaunchKernelGGL(route_kernel<EC>, dim3((T + tokens_per_block - 1) / tokens_per_block), dim3(kRouteThreads), 0,
+                     stream, logits, ids_in, T, E, k, topk_ids, gates);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds_bytes, stream, topk_ids, T * k, E, offsets,
+                     sorted_rows, error_word);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -200,10 +341,12 @@ __global__ __launch_bounds__(kRgThreads) void route_group_kernel(
 hipError_t launch_route_group(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k,
                               int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
                               int32_t* error_word, hipStream_t stream) {
-  const size_t lds_bytes = (size_t)(kRgWaves + 1) * E * sizeof(int);
-  hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(kRgThreads), lds_bytes, stream, logits, ids_in,
-                     T, E, k, topk_ids, gates, offsets, sorted_rows, error_word);
-  return hipGetLastError();
+  if (E <= 64)
+    return launch_ec<1>(logits, ids_in, T, E, k, topk_ids, gates, offsets, sorted_rows, error_word, stream);
+  if (E <= 128)
+    return launch_ec<2>(logits, ids_in, T, E, k, topk_ids, gates, offsets, sorted_rows, error_word, stream);
+  return launch_ec<kExpertChunks>(logits, ids_in, T, E, k, topk_ids, gates, offsets, sorted_rows, error_word,
+                                  stream);
 }
 
 }  // namespace mxfp4

@@ -78,7 +78,7 @@ def _proj(lib, E=32, N=64, K=128, T=4, k=4, path=0, ws=None, ws_bytes=0, ptr=16,
     (dict(K=100), 1), (dict(K=0), 1), (dict(N=0), 1), (dict(E=0), 1), (dict(k=33, E=64), 1),
     (dict(k=5, E=4), 1), (dict(T=-1), 1), (dict(path=7), 1), (dict(ptr=0), 1), (dict(ptr=8), 1),
     (dict(path=2, ws=None), 2), (dict(path=2, ws=ctypes.c_void_p(16), ws_bytes=10), 2),
-    (dict(path=1, K=32768, T=64, k=4), 1),
+    (dict(path=1, K=8192, T=64, k=4), 1),
 ])
 def test_expert_proj_rejects_bad_arguments(kw, status):
     lib = B.load_library()
@@ -93,13 +93,15 @@ def test_expert_proj_t0_is_a_noop():
 def test_workspace_size():
     lib = B.load_library()
     ws = lib.mxfp4_expert_proj_workspace_size
-    assert ws(1, 4, 2880, 0, 1) == 0                 # GEMV needs none
-    assert ws(1, 4, 2880, 0, 0) == 0                 # auto picks GEMV for 4 rows
-    # GEMM: per quantized row 92 padded blocks of 48 code bytes + 2 scale bytes
-    n = ws(4096, 4, 2880, 0, 2)
-    assert n >= 4096 * 92 * 50 and n < 4096 * 92 * 50 + 256
-    assert ws(2048, 4, 2880, 1, 0) >= 8192 * 92 * 50
-    assert ws(4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
+    assert ws(32, 1, 4, 2880, 0, 1) == 0             # GEMV needs none
+    assert ws(32, 1, 4, 2880, 0, 0) == 0             # auto: 4 rows over 4 experts -> GEMV
+    assert ws(32, 64, 4, 2880, 1, 0) == 0            # auto: 256 rows over 32 experts -> GEMV
+    # GEMM: per quantized row KB padded to a multiple of 8 blocks, 48 code bytes + 2 scale bytes each
+    n = ws(32, 4096, 4, 2880, 0, 2)
+    assert n >= 4096 * 96 * 50 and n < 4096 * 96 * 50 + 256
+    assert ws(32, 2048, 4, 2880, 1, 0) >= 8192 * 96 * 50
+    assert ws(32, 4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
+    assert ws(0, 4, 4, 128, 0, 0) == ctypes.c_size_t(-1).value
 
 
 def test_combine_rejects_bad_arguments():
