@@ -111,7 +111,7 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
  * (MXFP4_PATH_AUTO resolves exactly as mxfp4_expert_proj does).  0 means none.
  * Returns (size_t)-1 for invalid sizes.
  */
-size_t mxfp4_expert_proj_workspace_size(int E, int T, int k, int K, int x_per_slot, int path);
+size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x_per_slot, int path);
 
 /*
  * The routed expert projection.
@@ -144,7 +144,7 @@ size_t mxfp4_expert_proj_workspace_size(int E, int T, int k, int K, int x_per_sl
  *           stays within 2e-3 * sum_j |W x| + 1e-5 per output for inputs like
  *           the model's (see the design notes).
  *   workspace, workspace_bytes: device scratch of at least
- *           mxfp4_expert_proj_workspace_size(E, T, k, K, x_per_slot, path) bytes,
+ *           mxfp4_expert_proj_workspace_size(E, N, T, k, K, x_per_slot, path) bytes,
  *           16-byte aligned; may be NULL when that size is 0.  Calls that share
  *           a workspace must be ordered on one stream.
  * T = 0 returns MXFP4_OK and enqueues nothing.

@@ -58,7 +58,7 @@ def load_library():
     lib.mxfp4_last_error.restype = ctypes.c_char_p
     lib.mxfp4_moe_route_group.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.mxfp4_moe_route_group.restype = i32
-    lib.mxfp4_expert_proj_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.mxfp4_expert_proj_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.mxfp4_expert_proj_workspace_size.restype = sz
     lib.mxfp4_expert_proj.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.mxfp4_expert_proj.restype = i32
@@ -123,10 +123,10 @@ def mxfp4_moe_route_group(logits, ids_in, T: int, E: int, k: int, topk_ids, gate
     _check(st)
 
 
-def mxfp4_expert_proj_workspace_size(E: int, T: int, k: int, K: int, x_per_slot: bool,
+def mxfp4_expert_proj_workspace_size(E: int, N: int, T: int, k: int, K: int, x_per_slot: bool,
                                      path: int = MXFP4_PATH_AUTO) -> int:
-    n = load_library().mxfp4_expert_proj_workspace_size(int(E), int(T), int(k), int(K), int(bool(x_per_slot)),
-                                                        int(path))
+    n = load_library().mxfp4_expert_proj_workspace_size(int(E), int(N), int(T), int(k), int(K),
+                                                        int(bool(x_per_slot)), int(path))
     if n == ctypes.c_size_t(-1).value:
         raise MXFP4Error(1, "invalid sizes for the workspace query")
     return int(n)

@@ -111,12 +111,12 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
   return MXFP4_OK;
 }
 
-size_t mxfp4_expert_proj_workspace_size(int E, int T, int k, int K, int x_per_slot, int path) {
-  if (E < 1 || E > MXFP4_MAX_EXPERTS || T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
+size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x_per_slot, int path) {
+  if (E < 1 || E > MXFP4_MAX_EXPERTS || N < 1 || T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
   if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return (size_t)-1;
   if (T == 0) return 0;
   if (resolve_path(path, T, k, E) != MXFP4_PATH_GEMM) return 0;
-  return mxfp4::gemm_workspace_bytes(T, k, K, x_per_slot);
+  return mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
 }
 
 int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
@@ -141,7 +141,7 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
   if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
     return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
   if (p == MXFP4_PATH_GEMM) {
-    const size_t need = mxfp4::gemm_workspace_bytes(T, k, K, x_per_slot);
+    const size_t need = mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
     if (!workspace || workspace_bytes < need)
       return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                   need);

@@ -21,7 +21,7 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
                               hipStream_t stream);
 
 // expert_gemm.hip
-size_t gemm_workspace_bytes(int T, int k, int K, int x_per_slot);
+size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
                               int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
                               const int32_t* offsets, const int32_t* sorted_rows, float* out,

@@ -44,7 +44,7 @@ class DeviceProblem:
     def set_path(self, path):
         self.path = path
         p = self.p
-        nbytes = B.mxfp4_expert_proj_workspace_size(p.E, p.T, p.k, p.K, p.x_per_slot, path)
+        nbytes = B.mxfp4_expert_proj_workspace_size(p.E, p.N, p.T, p.k, p.K, p.x_per_slot, path)
         self.workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device) if nbytes else None
 
     def route_group(self, stream=None):

@@ -93,15 +93,20 @@ def test_expert_proj_t0_is_a_noop():
 def test_workspace_size():
     lib = B.load_library()
     ws = lib.mxfp4_expert_proj_workspace_size
-    assert ws(32, 1, 4, 2880, 0, 1) == 0             # GEMV needs none
-    assert ws(32, 1, 4, 2880, 0, 0) == 0             # auto: 4 rows over 4 experts -> GEMV
-    assert ws(32, 64, 4, 2880, 1, 0) == 0            # auto: 256 rows over 32 experts -> GEMV
-    # GEMM: per quantized row KB padded to a multiple of 8 blocks, 48 code bytes + 2 scale bytes each
-    n = ws(32, 4096, 4, 2880, 0, 2)
-    assert n >= 4096 * 96 * 50 and n < 4096 * 96 * 50 + 256
-    assert ws(32, 2048, 4, 2880, 1, 0) >= 8192 * 96 * 50
-    assert ws(32, 4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
-    assert ws(0, 4, 4, 128, 0, 0) == ctypes.c_size_t(-1).value
+    assert ws(32, 5760, 1, 4, 2880, 0, 1) == 0             # GEMV needs none
+    assert ws(32, 5760, 1, 4, 2880, 0, 0) == 0             # auto: 4 rows over 4 experts -> GEMV
+    assert ws(32, 2880, 64, 4, 2880, 1, 0) == 0            # auto: 256 rows over 32 experts -> GEMV
+    # GEMM, K = 2880: 45 stages of two blocks.  Per quantized row and stage a
+    # 96-byte code record and two 4-byte scale words; per expert, 256-row
+    # panel and stage 512 repacked weight-scale bytes (5760 rows = 23 panels).
+    n = ws(32, 5760, 4096, 4, 2880, 0, 2)
+    assert n == 4096 * 45 * 96 + 4096 * 90 * 4 + 32 * 23 * 45 * 512
+    assert ws(32, 2880, 2048, 4, 2880, 1, 0) >= 8192 * 45 * 104 + 32 * 12 * 45 * 512
+    # stage counts are padded to a multiple of 3: K = 64 has 1 stage -> 3
+    assert ws(8, 256, 512, 2, 64, 1, 2) == 1024 * 3 * 96 + 1024 * 6 * 4 + 8 * 1 * 3 * 512
+    assert ws(32, 5760, 4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
+    assert ws(0, 5760, 4, 4, 128, 0, 0) == ctypes.c_size_t(-1).value
+    assert ws(32, 0, 4, 4, 128, 0, 2) == ctypes.c_size_t(-1).value
 
 
 def test_combine_rejects_bad_arguments():
