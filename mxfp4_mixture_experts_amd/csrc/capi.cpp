@@ -72,7 +72,7 @@ int resolve_path(int path, int T, int k, int E) {
   return R <= 16 * used ? MXFP4_PATH_GEMV : MXFP4_PATH_GEMM;
 }
 
-bool gemv_fits(int T, int K) { return mxfp4::gemv_lds_bytes(T, K) <= 160 * 1024 - 1024; }
+bool gemv_fits(int T, int K) { return mxfp4::gemv_lds_bytes(T, K) <= 160 * 1024 - 1024; }  // = kGemvMaxDynLds
 
 }  // namespace
 

@@ -172,11 +172,13 @@ __global__ __launch_bounds__(kThreads) void repack_wscales_kernel(const uint8_t*
   const uintptr_t first = base + ((size_t)e * N + n) * KB + kb0;
   const uintptr_t blk0 = first & ~(uintptr_t)15;
   const uintptr_t blk1 = (base + ((size_t)e * N + n) * KB + kb1) & ~(uintptr_t)15;
+  // the blocks through the (global) scales pointer, so the loads stay global
+  const uint4* blocks16 = reinterpret_cast<const uint4*>(scales - (base - blk0));
+  const int last16 = (int)((blk1 - blk0) >> 4);
   uint32_t wv[12];
 #pragma unroll
   for (int i = 0; i < 3; i++) {
-    const uintptr_t a = min(blk0 + 16 * i, blk1);
-    const uint4 v = *reinterpret_cast<const uint4*>(a);
+    const uint4 v = blocks16[min(i, last16)];
     wv[4 * i] = v.x; wv[4 * i + 1] = v.y; wv[4 * i + 2] = v.z; wv[4 * i + 3] = v.w;
   }
   const int sh = (int)(first - blk0);  // < 16

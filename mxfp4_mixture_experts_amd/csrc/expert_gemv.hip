@@ -67,30 +67,69 @@ __device__ __forceinline__ bool find_group(const int32_t* offsets, int E, int R,
   return false;
 }
 
+#define MXFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, MXFP4_LDS(dst), 16, 0, 0);
+}
+
+// Wait until at most VM vector-memory instructions of this wave are
+// outstanding and its LDS instructions are done, then meet the other waves.
+// Only compiler-level fences: a workgroup fence would also wait for the LDS
+// DMAs and weight loads still in flight.
+template <int VM>
+__device__ __forceinline__ void bare_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));  // vmcnt(VM) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that orders LDS only: __syncthreads() would also wait for
+// every weight load in flight (its fence covers global memory).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   // 2^(s - 127) as an fp32 bit pattern; s = 0 is the subnormal 2^-127
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-template <int MT, int WAVES, int NCH>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void expert_gemv_kernel(
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void expert_gemv_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int T, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out) {
-  // [MT + 1][XS] bf16 token rows, 16 bytes per entry: rows >= the pass's count and
-  // the extra last row are zero, as is every entry past K, so every read below
-  // is unconditional.  XS = 16 entries per K group (groups rounded up to whole
-  // chunks of NCH) + 1 (the +1 puts 16 rows on distinct banks).
+  // [MT][XS] bf16 token rows, 16 bytes per entry (16 per K group), staged by
+  // LDS DMA; entries past K and rows past the pass's count are zeroed in
+  // registers when read.
   extern __shared__ uint4 xs[];
   __shared__ int rows_lds[MT];
+  // KS > 1: the KS waves of a row group split K and add their partial sums here
+  constexpr int RW = WAVES / KS;  // row groups (16 weight rows each) per workgroup
+  static_assert(WAVES % KS == 0, "whole row groups");
+  __shared__ f32x4_v red[KS > 1 ? RW * (KS - 1) * 64 : 1];
   const int KB = K >> 5;
   const int K8 = K >> 3;
   const int NIT = (KB + 3) >> 2;
-  const int NITC = (NIT + NCH - 1) / NCH * NCH;
-  const int XS = NITC * 16 + 1;
+  // K groups padded to whole rounds of NST chunks per K part (padding groups
+  // re-read the row's last block and meet zero activations)
+  const int NITC = (NIT + KS * NST * NCH - 1) / (KS * NST * NCH) * (KS * NST * NCH);
+  const int XS = (NITC * 16 + 63) / 64 * 64 + 1;  // whole 64-entry DMAs, +1 spreads rows over banks
+  static_assert(NST == 2 || NST == 3, "two or three chunks in flight");
+  static_assert(NST == 3 || NCH >= 1, "");
   const int R = T * k;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  // after the token rows: the workgroup's weight-scale rows (16 * WAVES rows x
+  // KB bytes, contiguous in memory), staged once as the aligned 16-byte blocks
+  // covering them
+  uint4* sc_lds = xs + MT * XS;
 
   int e, m0, m1;
   if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
@@ -98,84 +137,129 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   m0 = __builtin_amdgcn_readfirstlane(m0);
   m1 = __builtin_amdgcn_readfirstlane(m1);
 
-  const int n_base = (blockIdx.x * WAVES + wave) * 16;
+  const int wg_row0 = blockIdx.x * RW * 16;
+  const int rw = wave / KS, kpart = wave % KS;
+  const int n_base = wg_row0 + rw * 16;
   const int row = n_base + (lane & 15);
   const int kq = lane >> 4;
   const bool row_ok = row < N;
   // rows past N and blocks past K read real (clamped) weights and meet zero activations
   const uint4* wrow = reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(row, N - 1)) * KB;
-  const uint8_t* srow = scales + ((size_t)e * N + min(row, N - 1)) * KB;
   const float bias_v = (bias && row_ok) ? bf16_bits_to_f32(bias[(size_t)e * N + row]) : 0.f;
 
-  auto load_chunk = [&](int c0, uint4 (&w)[NCH], uint32_t (&s)[NCH]) {
+  auto load_chunk = [&](int c0, uint4 (&w)[NCH]) {
     // groups past K re-read the row's last block; they meet zero activations
 #pragma unroll
-    for (int i = 0; i < NCH; i++) {
-      const int kb = min((c0 + i) * 4 + kq, KB - 1);
-      w[i] = load_nt(wrow + kb);
-      s[i] = srow[kb];
-    }
+    for (int i = 0; i < NCH; i++) w[i] = load_nt(wrow + min((c0 + i) * 4 + kq, KB - 1));
+  };
+
+  // ---- weight scales of rows wg_row0 .. wg_row0 + 16 * WAVES - 1 (clamped to
+  // N - 1) into LDS: the aligned 16-byte blocks from the one holding the first
+  // byte to the one holding the last (an aligned block that holds a valid byte
+  // never leaves that byte's page).  Lane byte (row, kb) then sits at
+  // sc_base + (row - wg_row0) * KB + kb.
+  const int rows_wg = min(RW * 16, N - wg_row0);
+  const uintptr_t sbase = reinterpret_cast<uintptr_t>(scales);
+  const uintptr_t s_first = sbase + ((size_t)e * N + wg_row0) * KB;
+  const uintptr_t s_blk0 = s_first & ~(uintptr_t)15;
+  const uintptr_t s_blk1 = (s_first + (size_t)rows_wg * KB - 1) & ~(uintptr_t)15;
+  const int n_sblk = (int)((s_blk1 - s_blk0) >> 4) + 1;
+  const int sc_base = (int)(s_first - s_blk0);
+  // the same blocks through the (global) scales pointer, so loads stay global
+  const uint4* s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
+  auto sorted_rows_checked = [&](int i) {
+    const int r = sorted_rows[i];
+    return (r < 0 || r >= R) ? -1 : r;
   };
 
   for (int mb = m0; mb < m1; mb += MT) {
     const int mc = min(MT, m1 - mb);
-    // ---- the first two chunks of weights are in flight while the token rows are staged
-    uint4 wa[NCH], wb[NCH];
-    uint32_t sa[NCH], sb[NCH];
-    load_chunk(0, wa, sa);
-    if (NCH < NIT) load_chunk(NCH, wb, sb);
-    __syncthreads();  // the previous pass is done with the staged rows
+    // ---- prologue.  The token rows and the weight-scale blocks go to LDS by
+    // LDS DMA (no registers), issued before all of this wave's first NST
+    // chunks of weights; the wave then waits for its DMAs only (the weight
+    // loads are younger, and the counter is in order) and meets the others.
+    // Every wave issues the same number of DMAs (a wave with fewer real ones
+    // repeats one: the same bytes to the same place).  Lanes past the data
+    // read a clamped source into padding that is never read.
+    bare_barrier<63>();  // the previous pass is done with the staged rows (its reads have returned)
     // token row m's source: uniform per m, so these are scalar loads
-    int src[MT + 1];
+    int src[MT];
 #pragma unroll
-    for (int m = 0; m <= MT; m++) {
+    for (int m = 0; m < MT; m++) {
       int r = -1;
       if (m < mc) {
         r = sorted_rows[mb + m];
         if (r < 0 || r >= R) r = -1;
       }
-      if (threadIdx.x == 0 && m < MT) rows_lds[m] = r;
-      src[m] = r < 0 ? -1 : (x_per_slot ? r : r / k);
+      src[m] = r < 0 ? 0 : (x_per_slot ? r : r / k);  // row 0 stands in: masked when read
     }
-    // all of a thread's activation loads first, then the LDS stores
-    constexpr int kPerRow = MT == 1 ? 4 : (MT <= 4 ? 2 : 1);  // entries per thread per row and round
-    for (int c0 = 0; c0 < XS; c0 += kPerRow * WAVES * 64) {
-      uint4 v[MT + 1][kPerRow];
-#pragma unroll
-      for (int m = 0; m <= MT; m++)
-#pragma unroll
-        for (int j = 0; j < kPerRow; j++) {
-          const int c = c0 + j * WAVES * 64 + threadIdx.x;
-          v[m][j] = (src[m] >= 0 && c < K8) ? reinterpret_cast<const uint4*>(x + (size_t)src[m] * K)[c]
-                                            : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-      for (int m = 0; m <= MT; m++)
-#pragma unroll
-        for (int j = 0; j < kPerRow; j++) {
-          const int c = c0 + j * WAVES * 64 + threadIdx.x;
-          if (c < XS) xs[m * XS + c] = v[m][j];
-        }
+    if (threadIdx.x < MT) rows_lds[threadIdx.x] = threadIdx.x < mc ? sorted_rows_checked(mb + threadIdx.x) : -1;
+    {
+      // scale blocks: 64 per DMA, instructions spread over the waves
+      const int n_si = (n_sblk + 63) >> 6;
+      const int per_wave = (n_si + WAVES - 1) / WAVES;
+      for (int q = 0; q < per_wave; q++) {
+        const int ins = (q * WAVES + wave) % n_si;
+        const int b = min(ins * 64 + lane, n_sblk - 1);
+        dma16(s_blocks + b, reinterpret_cast<uint8_t*>(sc_lds + ins * 64));
+      }
+      // token rows: 64 entries per DMA
+      const int x_per_row = (NITC * 16 + 63) >> 6;
+      const int n_xi = mc * x_per_row;
+      const int xper_wave = (n_xi + WAVES - 1) / WAVES;
+      for (int q = 0; q < xper_wave; q++) {
+        const int ins = (q * WAVES + wave) % n_xi;
+        const int m = ins / x_per_row, j = ins - m * x_per_row;
+        const int c = min(j * 64 + lane, K8 - 1);
+        dma16(reinterpret_cast<const uint4*>(x + (size_t)src[m] * K) + c,
+              reinterpret_cast<uint8_t*>(xs + m * XS + j * 64));
+      }
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");  // the weight loads stay behind the DMAs
+    uint4 wa[NCH], wb[NCH], wc[NCH];
+    const int g_first = kpart * (NITC / KS);  // this wave's first K group
+    load_chunk(g_first, wa);
+    load_chunk(g_first + NCH, wb);
+    if (NST == 3) load_chunk(g_first + 2 * NCH, wc);
+    bare_barrier<NST * NCH>();  // every wave's DMAs have landed
+    const uint8_t* srow = reinterpret_cast<const uint8_t*>(sc_lds) + sc_base +
+                          (size_t)min(row - wg_row0, rows_wg - 1) * KB;
 
     f32x4_v acc[4];
 #pragma unroll
     for (int d = 0; d < 4; d++) acc[d] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    const uint4* xrow = xs + ((lane & 15) < mc ? (lane & 15) : MT) * XS + kq * 4;
+    const bool xrow_ok = (lane & 15) < mc;
+    const uint4* xrow = xs + min(lane & 15, mc - 1) * XS + kq * 4;
+    // rows past the pass's count and entries past K (LDS padding) read as zero
+    auto xread = [&](int idx) {
+      const uint4 v = xrow[idx];
+      const uint32_t keep = (xrow_ok && idx + kq * 4 < K8) ? 0xffffffffu : 0u;
+      return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    };
 
-    // ---- two-stage pipeline over chunks of NCH K groups: chunk c + 1 loads
-    // while chunk c converts and multiplies (4 MFMAs per 128-bit load into four
+    // ---- NST chunks of NCH K groups in flight: a chunk is converted and
+    // multiplied while the later ones load (4 MFMAs per 128-bit load into four
     // independent accumulators; A = token rows, lane l: row l % 16; B = weights)
-    auto compute_chunk = [&](int c0, const uint4 (&w)[NCH], const uint32_t (&s)[NCH]) {
+    // At 3 waves per SIMD the next group's token rows are not prefetched from
+    // LDS (the registers are needed for the weights in flight; the other waves
+    // cover the LDS latency).
+    constexpr bool kXPrefetch = OCC < 3;
+    auto compute_chunk = [&](int c0, const uint4 (&w)[NCH]) {
+      uint32_t s[NCH];
+#pragma unroll
+      for (int i = 0; i < NCH; i++) s[i] = srow[min((c0 + i) * 4 + kq, KB - 1)];
       uint4 xv[4], xn[4];
 #pragma unroll
-      for (int d = 0; d < 4; d++) xv[d] = xrow[c0 * 16 + d];
+      for (int d = 0; d < 4; d++) xv[d] = xread(c0 * 16 + d);
 #pragma unroll
       for (int i = 0; i < NCH; i++) {
-        if (i + 1 < NCH) {
+        if (kXPrefetch && i + 1 < NCH) {
 #pragma unroll
-          for (int d = 0; d < 4; d++) xn[d] = xrow[(c0 + i + 1) * 16 + d];
+          for (int d = 0; d < 4; d++) xn[d] = xread((c0 + i + 1) * 16 + d);
+        }
+        if (!kXPrefetch && i > 0) {
+#pragma unroll
+          for (int d = 0; d < 4; d++) xv[d] = xread((c0 + i) * 16 + d);
         }
         const float sf = e8m0_to_float(s[i]);
         const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
@@ -188,28 +272,49 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
           const bf16x8_t bw = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
           acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[d]), bw, acc[d], 0, 0, 0);
         }
-        if (i + 1 < NCH) {
+        if (kXPrefetch && i + 1 < NCH) {
 #pragma unroll
           for (int d = 0; d < 4; d++) xv[d] = xn[d];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    for (int c0 = 0; c0 < NIT; c0 += 2 * NCH) {
-      compute_chunk(c0, wa, sa);
-      if (c0 + 2 * NCH < NIT) load_chunk(c0 + 2 * NCH, wa, sa);
-      if (c0 + NCH >= NIT) break;
-      compute_chunk(c0 + NCH, wb, sb);
-      if (c0 + 3 * NCH < NIT) load_chunk(c0 + 3 * NCH, wb, sb);
+    // rounds of NST chunks: every round but the last requests the next round
+    // (unconditionally, so the compiler's wait counts stay exact)
+    const int rounds = NITC / (KS * NST * NCH);
+    for (int rd = 0; rd + 1 < rounds; rd++) {
+      const int c0 = g_first + rd * NST * NCH;
+      compute_chunk(c0, wa);
+      load_chunk(c0 + NST * NCH, wa);
+      compute_chunk(c0 + NCH, wb);
+      load_chunk(c0 + (NST + 1) * NCH, wb);
+      if (NST == 3) {
+        compute_chunk(c0 + 2 * NCH, wc);
+        load_chunk(c0 + 5 * NCH, wc);
+      }
     }
-    const f32x4_v tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    {
+      const int c0 = g_first + (rounds - 1) * NST * NCH;
+      compute_chunk(c0, wa);
+      compute_chunk(c0 + NCH, wb);
+      if (NST == 3) compute_chunk(c0 + 2 * NCH, wc);
+    }
+    f32x4_v tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (KS > 1) {  // K parts 1.. hand their sums to part 0 (fixed order: deterministic)
+      if (kpart > 0) red[(rw * (KS - 1) + kpart - 1) * 64 + lane] = tot;
+      lds_barrier();
+      if (kpart == 0) {
+#pragma unroll
+        for (int j = 0; j < KS - 1; j++) tot += red[(rw * (KS - 1) + j) * 64 + lane];
+      }
+    }
 
     // ---- lane l holds tokens 4 * (l / 16) + i of weight row l % 16
-    if (row_ok) {
+    if (row_ok && kpart == 0) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int m = 4 * kq + i;
-        if (m < mc && m < MT) {
+        if (m < mc) {
           const int r = rows_lds[m];
           if (r >= 0) out[(size_t)r * N + row] = tot[i] + bias_v;
         }
@@ -218,59 +323,90 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-template <int MT, int WAVES, int NCH>
+// largest dynamic LDS a launch may use (the rest of the 160 KB holds rows_lds)
+constexpr int kGemvMaxDynLds = 160 * 1024 - 1024;
+
+// Dynamic LDS of one workgroup: the MT staged token rows, then the
+// weight-scale rows of its 16 * WAVES weight rows (+2 blocks of alignment slack).
+size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K) {
+  const int nit = (K / 32 + 3) / 4;
+  const int r = KS * NST * NCH;
+  const size_t xs = (size_t)MT * (((nit + r - 1) / r * r * 16 + 63) / 64 * 64 + 1) * 16;
+  const size_t blocks = ((size_t)(WAVES / KS) * 16 * (K / 32) + 15) / 16 + 2;
+  const size_t sc = (blocks + 63) / 64 * 64 * 16;
+  return xs + sc;
+}
+
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC>
 hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                              const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                              const int32_t* sorted_rows, float* out, hipStream_t stream) {
-  const int nit = (K / 32 + 3) / 4;
-  const size_t lds = (size_t)(MT + 1) * ((nit + NCH - 1) / NCH * NCH * 16 + 1) * 16;
-  static bool attr_set = false;  // raise the dynamic LDS limit once per instantiation
+  const size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K);
+  static bool attr_set = false;  // raise the dynamic LDS limit (to what any K may need) once
   if (!attr_set && lds > 65536) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxDynLds);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
   const int R = T * k;
   const int groups = R < E ? R : E;
-  const int rows_per_block = WAVES * 16;
+  const int rows_per_block = WAVES / KS * 16;
   const dim3 grid((N + rows_per_block - 1) / rows_per_block, groups);
-  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH>), grid, dim3(WAVES * 64), lds, stream, blocks, scales, bias, E,
+  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC>), grid, dim3(WAVES * 64), lds, stream, blocks, scales, bias, E,
                      N, K, x, x_per_slot, T, k, offsets, sorted_rows, out);
   return hipGetLastError();
 }
 
-}  // namespace
+// Chunk length NCH (K groups of 128 elements) for a ring of NST chunks per K
+// part: the candidate that pads K's groups to whole rounds least (ties: the
+// longer chunk).
+int gemv_pick_chunk(int ks, int nst, int K, const int* cand, int ncand) {
+  const int nit = (K / 32 + 3) / 4;
+  int best = cand[0], best_pad = 1 << 30;
+  for (int i = 0; i < ncand; i++) {
+    const int r = ks * nst * cand[i];
+    const int pad = (nit + r - 1) / r * r - nit;
+    if (pad < best_pad || (pad == best_pad && cand[i] > best)) best = cand[i], best_pad = pad;
+  }
+  return best;
+}
 
-namespace {
-// K groups (128 elements) per fully unrolled chunk
-int gemv_chunk(int K) { return (K / 32 + 3) / 4 <= 4 ? 4 : 8; }
+// Launch shape by batch size.  One token: workgroups of 2 waves that share 16
+// weight rows and split K (so that all of a row group's weights are requested
+// at once without exceeding the registers of 3 waves per SIMD); the many small
+// workgroups spread evenly over the CUs.  Larger batches: wider workgroups
+// share the staged token rows.  Chunk lengths are those that fit the registers
+// without spilling.
+struct GemvShape {
+  int mt, waves, nch, nst, ks;
+};
+GemvShape gemv_shape(int T, int K) {
+  static const int c1[] = {4}, c4[] = {4}, c16[] = {4, 6, 8};
+  if (T <= 1) return {1, 2, gemv_pick_chunk(2, 3, K, c1, 1), 3, 2};
+  if (T <= 4) return {4, 4, gemv_pick_chunk(1, 3, K, c4, 1), 3, 1};
+  return {16, 8, gemv_pick_chunk(1, 2, K, c16, 3), 2, 1};
+}
+
 }  // namespace
 
 size_t gemv_lds_bytes(int T, int K) {
-  const int mt = T <= 1 ? 1 : (T <= 4 ? 4 : 16);
-  const int nch = gemv_chunk(K);
-  const int nit = (K / 32 + 3) / 4;
-  return (size_t)(mt + 1) * ((nit + nch - 1) / nch * nch * 16 + 1) * 16;
+  const GemvShape g = gemv_shape(T, K);
+  return gemv_lds_for(g.mt, g.waves, g.nch, g.nst, g.ks, K);
 }
 
 hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                               const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                               const int32_t* sorted_rows, float* out, hipStream_t stream) {
-#define MXFP4_GEMV_LAUNCH(MT, W, NCH)                                                                      \
-  return launch_gemv_shape<MT, W, NCH>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, \
-                                       out, stream)
-  const bool small_k = gemv_chunk(K) == 4;
-  if (T <= 1) {
-    if (small_k) MXFP4_GEMV_LAUNCH(1, 4, 4);
-    MXFP4_GEMV_LAUNCH(1, 4, 8);
-  }
-  if (T <= 4) {
-    if (small_k) MXFP4_GEMV_LAUNCH(4, 4, 4);
-    MXFP4_GEMV_LAUNCH(4, 4, 8);
-  }
-  if (small_k) MXFP4_GEMV_LAUNCH(16, 8, 4);
-  MXFP4_GEMV_LAUNCH(16, 8, 8);
+#define MXFP4_GEMV_LAUNCH(MT, W, NCH, NST, KS, OCC)                                                        \
+  return launch_gemv_shape<MT, W, NCH, NST, KS, OCC>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k,  \
+                                                     offsets, sorted_rows, out, stream)
+  const GemvShape g = gemv_shape(T, K);
+  if (g.mt == 1) MXFP4_GEMV_LAUNCH(1, 2, 4, 3, 2, 3);
+  if (g.mt == 4) MXFP4_GEMV_LAUNCH(4, 4, 4, 3, 1, 2);
+  if (g.nch == 4) MXFP4_GEMV_LAUNCH(16, 8, 4, 2, 1, 2);
+  if (g.nch == 6) MXFP4_GEMV_LAUNCH(16, 8, 6, 2, 1, 2);
+  MXFP4_GEMV_LAUNCH(16, 8, 8, 2, 1, 2);
 #undef MXFP4_GEMV_LAUNCH
 }
 

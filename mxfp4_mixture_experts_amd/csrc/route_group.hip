@@ -24,7 +24,9 @@
 // row ranges in order and lanes are ranked by index, so each expert's rows
 // come out in ascending order.
 //
-// Small batches (T <= 256) run both parts in one single-workgroup kernel.
+// Tiny batches (T * k <= 64) group in a single wave without LDS counters.
+// Small batches (T <= 256) run both parts in one single-workgroup kernel,
+// which keeps a copy of the routed ids in LDS for the grouping.
 // Larger batches route with many workgroups and then group in a second,
 // single-workgroup launch.  A row whose given id is out of range is written
 // as -1 and left out of the grouping; a repeated given id is flagged to the
@@ -46,6 +48,8 @@ constexpr int kSmallT = 256;            // single-kernel path up to this many to
 constexpr int kRouteThreads = 256;      // multi-workgroup routing: 4 waves, 4 tokens per wave
 constexpr int kTokensPerRouteWave = 4;
 constexpr int32_t kDupFlag = 1 << 30;
+constexpr int kMaxRouteE = MXFP4_MAX_EXPERTS;
+constexpr int kMaxRouteK = MXFP4_MAX_TOPK;
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -59,8 +63,10 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // Route token t with the calling wave; returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
 template <int EC>
 __device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int t, int E,
-                           int k, int lane, int32_t* __restrict__ topk_ids, float* __restrict__ gates) {
+                           int k, int lane, int32_t* __restrict__ topk_ids, float* __restrict__ gates,
+                           int32_t* ids_copy) {
   int32_t* ids = topk_ids + (size_t)t * k;
+  int32_t* idc = ids_copy ? ids_copy + t * k : nullptr;  // the grouping's copy (LDS), if any
   const uint16_t* lrow = logits ? logits + (size_t)t * E : nullptr;
   if (ids_in) {
     // lane s < k holds the given id of slot s
@@ -74,7 +80,11 @@ __device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* _
     }
     const uint64_t bad = __ballot(lane < k && !in_range);
     const uint64_t dups = __ballot(dup);
-    if (lane < k) ids[lane] = in_range ? (e | (dup ? kDupFlag : 0)) : -1;
+    const int idv = in_range ? (e | (dup ? kDupFlag : 0)) : -1;
+    if (lane < k) {
+      ids[lane] = idv;
+      if (idc) idc[lane] = idv;
+    }
     if (gates && lrow && bad == 0) {
       const float l = lane < k ? bf16_bits_to_f32(lrow[in_range ? e : 0]) : -INFINITY;
       const float mx = wave_max(l);
@@ -124,7 +134,10 @@ __device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* _
     const bool kept = e < E && rank[i] < k;
     num[i] = kept ? expf(l[i] - mx) : 0.f;
     part += num[i];
-    if (kept) ids[rank[i]] = e;
+    if (kept) {
+      ids[rank[i]] = e;
+      if (idc) idc[rank[i]] = e;
+    }
   }
   if (gates) {
     const float sum = wave_sum(part);
@@ -142,11 +155,13 @@ __device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* _
 }
 
 // Grouping of the R = T * k rows by the single workgroup that calls it.
-// cnt: LDS [kGroupWaves][E] zeroed; start: LDS [E].  Returns the error bits
-// found in the ids (range: negative ids; dup: flagged ids, whose flag is
-// cleared in place).
-__device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t* __restrict__ offsets,
-                          int32_t* __restrict__ sorted_rows, int* cnt, int* start, int* total_sh) {
+// ids_src: where the ids are read (an LDS copy of topk_ids, or topk_ids
+// itself); cnt: LDS [kGroupWaves][E] zeroed; start: LDS [E].  Returns the
+// error bits found in the ids (range: negative ids; dup: flagged ids, whose
+// flag is cleared in topk_ids and in ids_src).
+__device__ int group_rows(int32_t* __restrict__ topk_ids, int32_t* ids_src, int R, int E,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows, int* cnt, int* start,
+                          int* total_sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -163,7 +178,7 @@ __device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t*
 #pragma unroll
     for (int i = 0; i < kTilesPerLoad; i++) {
       const int r = base + 64 * i + lane;
-      ev[i] = topk_ids[min(r, w_end - 1)];  // unconditional load, masked below
+      ev[i] = ids_src[min(r, w_end - 1)];  // unconditional load, masked below
       if (r >= w_end) ev[i] = -1;
     }
 #pragma unroll
@@ -176,6 +191,7 @@ __device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t*
           errbits |= MXFP4_ROUTE_ERR_ID_DUP;
           ev[i] &= ~kDupFlag;
           topk_ids[r] = ev[i];
+          ids_src[r] = ev[i];
         }
       }
       const int e = ev[i];
@@ -228,7 +244,7 @@ __device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t*
 #pragma unroll
     for (int i = 0; i < kTilesPerLoad; i++) {
       const int r = base + 64 * i + lane;
-      ev[i] = topk_ids[min(r, w_end - 1)];
+      ev[i] = ids_src[min(r, w_end - 1)];
       if (r >= w_end) ev[i] = -1;
     }
 #pragma unroll
@@ -246,7 +262,9 @@ __device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t*
       const int below = lanes_below(peers);
       int pos = 0;
       if (valid) pos = cnt[wave * E + e] + below;
-      __builtin_amdgcn_s_waitcnt(0);
+      // every lane's read of its counter precedes the lowest peer's update (LDS
+      // instructions of a wave run in order; wait for the reads themselves only)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
       if (valid) {
         sorted_rows[pos] = r;
@@ -258,6 +276,57 @@ __device__ int group_rows(int32_t* __restrict__ topk_ids, int R, int E, int32_t*
   return errbits;
 }
 
+// T * k <= 64: up to 16 waves route a token each, then one wave groups the
+// rows without LDS counters or further barriers: lane r holds row r's id;
+// offsets[e] counts the valid rows with an id below e, and row r goes to the
+// rows with a smaller id plus the rows before it with the same id (the
+// grouping's definition, evaluated directly with v_readlane broadcasts).
+template <int EC>
+__global__ __launch_bounds__(kGroupThreads) void route_group_tiny_kernel(
+    const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int T, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ gates, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ error_word) {
+  __shared__ int ids_lds[64];
+  __shared__ int err_lds[kGroupWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  int errbits = 0;
+  for (int t = wave; t < T; t += nwaves)
+    errbits |= route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates, ids_lds);
+  if (lane == 0) err_lds[wave] = errbits;
+  __syncthreads();
+  if (wave != 0) return;
+  const int R = T * k;
+  int err = 0;
+  for (int w = 0; w < nwaves; w++) err |= err_lds[w];
+  int id = lane < R ? ids_lds[lane] : -1;
+  if (lane < R && id >= 0 && (id & kDupFlag)) {
+    id &= ~kDupFlag;
+    topk_ids[lane] = id;
+    err |= MXFP4_ROUTE_ERR_ID_DUP;
+  }
+  if (lane < R && id < 0) err |= MXFP4_ROUTE_ERR_ID_RANGE;
+  err = (__ballot(err & MXFP4_ROUTE_ERR_ID_RANGE) ? MXFP4_ROUTE_ERR_ID_RANGE : 0) |
+        (__ballot(err & MXFP4_ROUTE_ERR_ID_DUP) ? MXFP4_ROUTE_ERR_ID_DUP : 0);
+  for (int c0 = 0; c0 <= E; c0 += 64) {
+    const int e = c0 + lane;
+    int cnt = 0;
+    for (int r = 0; r < R; r++) {
+      const int ir = __builtin_amdgcn_readlane(id, r);
+      cnt += (ir >= 0 && ir < e) ? 1 : 0;
+    }
+    if (e <= E) offsets[e] = cnt;
+  }
+  int before = 0;
+  for (int r = 0; r < R; r++) {
+    const int ir = __builtin_amdgcn_readlane(id, r);
+    before += (ir >= 0 && (ir < id || (ir == id && r < lane))) ? 1 : 0;
+  }
+  if (lane < R && id >= 0) sorted_rows[before] = lane;
+  if (lane == 0 && error_word) *error_word = err;
+}
+
 // T <= kSmallT: routing and grouping in one workgroup.
 template <int EC>
 __global__ __launch_bounds__(kGroupThreads) void route_group_small_kernel(
@@ -267,6 +336,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_small_kernel(
   extern __shared__ int lds[];
   int* cnt = lds;
   int* start = lds + kGroupWaves * E;
+  int* ids_lds = start + E;  // [T * k]: the routed ids, read back by the grouping
   __shared__ int err_sh;
   __shared__ int total_sh;
   const int tid = threadIdx.x;
@@ -276,9 +346,9 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_small_kernel(
   if (tid == 0) err_sh = 0;
   int errbits = 0;
   for (int t = wave; t < T; t += kGroupWaves)
-    errbits |= route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates);
+    errbits |= route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates, ids_lds);
   __syncthreads();  // the routed ids of every token visible to the whole workgroup
-  errbits |= group_rows(topk_ids, T * k, E, offsets, sorted_rows, cnt, start, &total_sh);
+  errbits |= group_rows(topk_ids, ids_lds, T * k, E, offsets, sorted_rows, cnt, start, &total_sh);
   if (errbits) atomicOr(&err_sh, errbits);
   __syncthreads();
   if (tid == 0 && error_word) *error_word = err_sh;
@@ -294,7 +364,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const uint16_t* __
   const int w = (blockIdx.x * kRouteThreads + threadIdx.x) >> 6;
   for (int i = 0; i < kTokensPerRouteWave; i++) {
     const int t = w * kTokensPerRouteWave + i;
-    if (t < T) route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates);
+    if (t < T) route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates, nullptr);
   }
 }
 
@@ -311,7 +381,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
   for (int i = threadIdx.x; i < kGroupWaves * E; i += kGroupThreads) cnt[i] = 0;
   if (threadIdx.x == 0) err_sh = 0;
   __syncthreads();
-  const int errbits = group_rows(topk_ids, R, E, offsets, sorted_rows, cnt, start, &total_sh);
+  const int errbits = group_rows(topk_ids, topk_ids, R, E, offsets, sorted_rows, cnt, start, &total_sh);
   if (errbits) atomicOr(&err_sh, errbits);
   __syncthreads();
   if (threadIdx.x == 0 && error_word) *error_word = err_sh;
@@ -321,8 +391,23 @@ template <int EC>
 hipError_t launch_ec(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k, int32_t* topk_ids,
                      float* gates, int32_t* offsets, int32_t* sorted_rows, int32_t* error_word, hipStream_t stream) {
   const size_t lds_bytes = (size_t)(kGroupWaves + 1) * E * sizeof(int);
+  if ((long long)T * k <= 64) {
+    const int waves = T < 1 ? 1 : (T < kGroupWaves ? T : kGroupWaves);  // T = 0 still writes the zero offsets
+    hipLaunchKernelGGL(route_group_tiny_kernel<EC>, dim3(1), dim3(64 * waves), 0, stream, logits, ids_in, T, E, k,
+                       topk_ids, gates, offsets, sorted_rows, error_word);
+    return hipGetLastError();
+  }
   if (T <= kSmallT) {
-    hipLaunchKernelGGL(route_group_small_kernel<EC>, dim3(1), dim3(kGroupThreads), lds_bytes, stream, logits, ids_in,
+    const size_t small_lds = lds_bytes + (size_t)T * k * sizeof(int);
+    static bool attr_set = false;  // up to (16 + 1) * 512 + 256 * 32 ints: raise the dynamic LDS limit once
+    if (!attr_set && small_lds > 65536) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_group_small_kernel<EC>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)((kGroupWaves + 1) * kMaxRouteE + kSmallT * kMaxRouteK) * 4);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(route_group_small_kernel<EC>, dim3(1), dim3(kGroupThreads), small_lds, stream, logits, ids_in,
                        T, E, k, topk_ids, gates, offsets, sorted_rows, error_word);
     return hipGetLastError();
   }

@@ -97,6 +97,27 @@ def test_paths_agree_closely():
     check_close(outs[1], outs[0], ref["mag"], "gemm vs gemv")
 
 
+# ----------------------------------------------------------------- routing paths
+# one-wave grouping (T * k <= 64), single-workgroup routing + grouping
+# (T <= 256), multi-workgroup routing then grouping (T > 256); 1, 2 and 8
+# lane chunks of experts
+ROUTE_CASES = [(16, 4, 32), (13, 5, 32), (64, 1, 100), (65, 1, 100), (256, 4, 32), (257, 4, 32),
+               (40, 7, 300), (300, 3, 300), (1, 32, 512)]
+
+
+@pytest.mark.parametrize("route", ["logits", "ids+logits"])
+@pytest.mark.parametrize("T,k,E", ROUTE_CASES)
+def test_route_group_paths(T, k, E, route):
+    _announce(f"route T={T} k={k} E={E} {route}")
+    p = S.make_custom(E=E, N=1, K=32, T=T, k=k, route=route)
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p)
+    dp.route_group()
+    g = dp.results()
+    assert g["error_word"] == 0
+    check_routing(g, ref)
+
+
 # ----------------------------------------------------------------- edge cases
 def test_empty_batch():
     _announce("T=0")
