@@ -323,6 +323,140 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   }
 }
 
+// ---------------------------------------------------------------------------
+// single token: row-contiguous streaming with lane dot products
+// ---------------------------------------------------------------------------
+//
+// With one token the MFMA above does one row of useful work, and its operand
+// layout (16 rows x 64 bytes per load) streams HBM markedly slower than loads
+// that cover longer runs of a row.  Here 16 lanes share a weight row: lane
+// (row q, j) of a wave holds block 16 i + j of the row, so a load covers 4 rows
+// x 256 contiguous bytes.  Each lane turns its block into 32 exact bf16
+// weights (v_cvt_scalef32_pk_bf16_fp4 with the block's E8M0 factor) and takes
+// v_dot2_f32_bf16 products with the token row (bf16 x bf16 is exact in fp32;
+// fp32 sums); the 16 lanes of a row then add their sums with shuffles in a
+// fixed order.  All of K's loads (K <= 3072) are in flight at once.
+
+constexpr int kT1Waves = 4;                     // waves per workgroup
+constexpr int kT1Rows = kT1Waves * 8;           // 8 weight rows per wave (two quads of 4)
+constexpr int kT1MaxKB = 96;                    // K <= 3072
+constexpr int kT1Ins = kT1MaxKB / 16;           // loads per quad and lane
+constexpr int kT1ScBlocks = 256;                // LDS for 32 rows x 96 scale bytes, whole 64-block DMAs
+
+__global__ __launch_bounds__(kT1Waves * 64) void expert_gemv_t1_kernel(
+    const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
+    int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int k,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out) {
+  __shared__ uint4 xs1[kT1MaxKB * 4];       // the token row: 4 entries of 8 bf16 per block
+  __shared__ uint4 sc1[kT1ScBlocks];       // the workgroup's scale rows, from their aligned blocks
+  const int KB = K >> 5;
+  const int K8 = K >> 3;
+  const int R = k;  // one token
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e, m0, m1;
+  if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  m1 = __builtin_amdgcn_readfirstlane(m1);
+  // Never taken (K >= 32): arrays written only by LDS DMA look unwritten to the
+  // optimizer, which would then fold their loads away.
+  if (K < 0) { xs1[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u); sc1[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u); }
+
+  const int wg_row0 = blockIdx.x * kT1Rows;
+  const int rows_wg = min(kT1Rows, N - wg_row0);
+  const int j = lane & 15;            // block lane within a row
+  const int q4 = lane >> 4;           // row within a quad
+  int rowq[2];
+  const uint4* wrow[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    rowq[q] = wg_row0 + wave * 8 + q * 4 + q4;
+    wrow[q] = reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(rowq[q], N - 1)) * KB;
+  }
+  // scale rows wg_row0 .. wg_row0 + rows_wg - 1, contiguous: the aligned 16-byte
+  // blocks from the one holding the first byte to the one holding the last (an
+  // aligned block that holds a valid byte never leaves that byte's page)
+  const uintptr_t sbase = reinterpret_cast<uintptr_t>(scales);
+  const uintptr_t s_first = sbase + ((size_t)e * N + wg_row0) * KB;
+  const uintptr_t s_blk0 = s_first & ~(uintptr_t)15;
+  const uintptr_t s_blk1 = (s_first + (size_t)rows_wg * KB - 1) & ~(uintptr_t)15;
+  const int n_sblk = (int)((s_blk1 - s_blk0) >> 4) + 1;
+  const int sc_base = (int)(s_first - s_blk0);
+  const uint4* s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
+
+  for (int mb = m0; mb < m1; mb++) {  // one routed row per expert unless given ids repeat
+    const int r_raw = sorted_rows[mb];
+    const int r = (r_raw < 0 || r_raw >= R) ? -1 : r_raw;
+    const int src = r < 0 ? 0 : (x_per_slot ? r : 0);
+    bare_barrier<63>();  // the previous row is done with the staged token row
+    // ---- LDS DMAs (scale blocks, then the token row), the same count on every wave
+    {
+      const int n_si = (n_sblk + 63) >> 6;
+      const int per_wave = (n_si + kT1Waves - 1) / kT1Waves;
+      for (int qd = 0; qd < per_wave; qd++) {
+        const int ins = (qd * kT1Waves + wave) % n_si;
+        dma16(s_blocks + min(ins * 64 + lane, n_sblk - 1), reinterpret_cast<uint8_t*>(sc1 + ins * 64));
+      }
+      const int n_xi = (K8 + 63) >> 6;
+      const int xper_wave = (n_xi + kT1Waves - 1) / kT1Waves;
+      for (int qd = 0; qd < xper_wave; qd++) {
+        const int ins = (qd * kT1Waves + wave) % n_xi;
+        dma16(reinterpret_cast<const uint4*>(x + (size_t)src * K) + min(ins * 64 + lane, K8 - 1),
+              reinterpret_cast<uint8_t*>(xs1 + ins * 64));
+      }
+    }
+    asm volatile("" ::: "memory");  // the weight loads stay behind the DMAs
+    // ---- all of the wave's weights: two quads x kT1Ins loads, blocks past K
+    // re-read the row's last block (zeroed below)
+    uint4 w0[kT1Ins], w1[kT1Ins];
+#pragma unroll
+    for (int i = 0; i < kT1Ins; i++) w0[i] = load_nt(wrow[0] + min(16 * i + j, KB - 1));
+#pragma unroll
+    for (int i = 0; i < kT1Ins; i++) w1[i] = load_nt(wrow[1] + min(16 * i + j, KB - 1));
+    bare_barrier<2 * kT1Ins>();  // every wave's DMAs have landed
+    const uint8_t* scb = reinterpret_cast<const uint8_t*>(sc1) + sc_base;
+    float acc0 = 0.f, acc1 = 0.f;
+    auto block_dot = [&](const uint4 w, int rl, int i, float acc) {
+      const int b = 16 * i + j;
+      const int bc = min(b, KB - 1);
+      const uint32_t keep = b < KB ? 0xffffffffu : 0u;
+      const float sf = e8m0_to_float(scb[min(rl, rows_wg - 1) * KB + bc]);
+      const uint32_t wd[4] = {w.x & keep, w.y & keep, w.z & keep, w.w & keep};
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const uint4 xv = xs1[bc * 4 + d];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 0),
+                                              __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 1),
+                                              __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 2),
+                                              __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 3),
+                                              __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
+      }
+      return acc;
+    };
+    const int rl0 = wave * 8 + q4, rl1 = wave * 8 + 4 + q4;
+#pragma unroll
+    for (int i = 0; i < kT1Ins; i++) acc0 = block_dot(w0[i], rl0, i, acc0);
+#pragma unroll
+    for (int i = 0; i < kT1Ins; i++) acc1 = block_dot(w1[i], rl1, i, acc1);
+    // ---- the 16 lanes of a row add their sums (fixed order: deterministic)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      acc0 += __shfl_xor(acc0, o, 64);
+      acc1 += __shfl_xor(acc1, o, 64);
+    }
+    if (j == 0 && r >= 0) {
+      if (rowq[0] < N)
+        out[(size_t)r * N + rowq[0]] = acc0 + (bias ? bf16_bits_to_f32(bias[(size_t)e * N + rowq[0]]) : 0.f);
+      if (rowq[1] < N)
+        out[(size_t)r * N + rowq[1]] = acc1 + (bias ? bf16_bits_to_f32(bias[(size_t)e * N + rowq[1]]) : 0.f);
+    }
+  }
+}
+
 // largest dynamic LDS a launch may use (the rest of the 160 KB holds rows_lds)
 constexpr int kGemvMaxDynLds = 160 * 1024 - 1024;
 
@@ -391,6 +525,7 @@ GemvShape gemv_shape(int T, int K) {
 }  // namespace
 
 size_t gemv_lds_bytes(int T, int K) {
+  if (T == 1 && K / 32 <= kT1MaxKB) return 0;  // static LDS only
   const GemvShape g = gemv_shape(T, K);
   return gemv_lds_for(g.mt, g.waves, g.nch, g.nst, g.ks, K);
 }
@@ -398,6 +533,12 @@ size_t gemv_lds_bytes(int T, int K) {
 hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                               const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                               const int32_t* sorted_rows, float* out, hipStream_t stream) {
+  if (T == 1 && K / 32 <= kT1MaxKB) {
+    const dim3 grid((N + kT1Rows - 1) / kT1Rows, k < E ? k : E);
+    hipLaunchKernelGGL(expert_gemv_t1_kernel, grid, dim3(kT1Waves * 64), 0, stream, blocks, scales, bias, E, N, K,
+                       x, x_per_slot, k, offsets, sorted_rows, out);
+    return hipGetLastError();
+  }
 #define MXFP4_GEMV_LAUNCH(MT, W, NCH, NST, KS, OCC)                                                        \
   return launch_gemv_shape<MT, W, NCH, NST, KS, OCC>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k,  \
                                                      offsets, sorted_rows, out, stream)
