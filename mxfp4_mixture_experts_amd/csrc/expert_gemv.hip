@@ -337,18 +337,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 // fp32 sums); the 16 lanes of a row then add their sums with shuffles in a
 // fixed order.  All of K's loads (K <= 3072) are in flight at once.
 
-constexpr int kT1Waves = 4;                     // waves per workgroup
-constexpr int kT1Rows = kT1Waves * 8;           // 8 weight rows per wave (two quads of 4)
 constexpr int kT1MaxKB = 96;                    // K <= 3072
 constexpr int kT1Ins = kT1MaxKB / 16;           // loads per quad and lane
-constexpr int kT1ScBlocks = 256;                // LDS for 32 rows x 96 scale bytes, whole 64-block DMAs
 
-__global__ __launch_bounds__(kT1Waves * 64) void expert_gemv_t1_kernel(
+// QUADS groups of 4 weight rows per wave, WAVES waves per workgroup
+template <int QUADS, int WAVES>
+struct T1Shape {
+  static constexpr int kRows = WAVES * 4 * QUADS;
+  // the workgroup's scale bytes (kRows x K/32) plus alignment slack, in whole 64-block DMAs
+  static constexpr int kScBlocks = ((kRows * kT1MaxKB + 31) / 16 + 63) / 64 * 64;
+};
+
+template <int QUADS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out) {
-  __shared__ uint4 xs1[kT1MaxKB * 4];       // the token row: 4 entries of 8 bf16 per block
-  __shared__ uint4 sc1[kT1ScBlocks];       // the workgroup's scale rows, from their aligned blocks
+  using Sh = T1Shape<QUADS, WAVES>;
+  __shared__ uint4 xs1[kT1MaxKB * 4];        // the token row: 4 entries of 8 bf16 per block
+  __shared__ uint4 sc1[Sh::kScBlocks];       // the workgroup's scale rows, from their aligned blocks
   const int KB = K >> 5;
   const int K8 = K >> 3;
   const int R = k;  // one token
@@ -363,15 +370,15 @@ __global__ __launch_bounds__(kT1Waves * 64) void expert_gemv_t1_kernel(
   // optimizer, which would then fold their loads away.
   if (K < 0) { xs1[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u); sc1[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u); }
 
-  const int wg_row0 = blockIdx.x * kT1Rows;
-  const int rows_wg = min(kT1Rows, N - wg_row0);
+  const int wg_row0 = blockIdx.x * Sh::kRows;
+  const int rows_wg = min(Sh::kRows, N - wg_row0);
   const int j = lane & 15;            // block lane within a row
   const int q4 = lane >> 4;           // row within a quad
-  int rowq[2];
-  const uint4* wrow[2];
+  int rowq[QUADS];
+  const uint4* wrow[QUADS];
 #pragma unroll
-  for (int q = 0; q < 2; q++) {
-    rowq[q] = wg_row0 + wave * 8 + q * 4 + q4;
+  for (int q = 0; q < QUADS; q++) {
+    rowq[q] = wg_row0 + (wave * QUADS + q) * 4 + q4;
     wrow[q] = reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(rowq[q], N - 1)) * KB;
   }
   // scale rows wg_row0 .. wg_row0 + rows_wg - 1, contiguous: the aligned 16-byte
@@ -386,76 +393,92 @@ __global__ __launch_bounds__(kT1Waves * 64) void expert_gemv_t1_kernel(
   const uint4* s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
 
   for (int mb = m0; mb < m1; mb++) {  // one routed row per expert unless given ids repeat
-    const int r_raw = sorted_rows[mb];
-    const int r = (r_raw < 0 || r_raw >= R) ? -1 : r_raw;
-    const int src = r < 0 ? 0 : (x_per_slot ? r : 0);
-    bare_barrier<63>();  // the previous row is done with the staged token row
-    // ---- LDS DMAs (scale blocks, then the token row), the same count on every wave
+    // With one shared token row the output row is not needed until the store:
+    // its load then waits behind the weight loads instead of in front of them.
+    int src = 0;
+    if (x_per_slot) {
+      const int r_raw = sorted_rows[mb];
+      src = (r_raw < 0 || r_raw >= R) ? 0 : r_raw;
+    }
+    if (mb > m0) bare_barrier<63>();  // the previous row is done with the staged token row
+    // ---- LDS DMAs (scale blocks, then the token row), spread over the waves;
+    // they are older than every weight load, which is all the wait below needs
     {
       const int n_si = (n_sblk + 63) >> 6;
-      const int per_wave = (n_si + kT1Waves - 1) / kT1Waves;
-      for (int qd = 0; qd < per_wave; qd++) {
-        const int ins = (qd * kT1Waves + wave) % n_si;
+      for (int ins = wave; ins < n_si; ins += WAVES)
         dma16(s_blocks + min(ins * 64 + lane, n_sblk - 1), reinterpret_cast<uint8_t*>(sc1 + ins * 64));
-      }
       const int n_xi = (K8 + 63) >> 6;
-      const int xper_wave = (n_xi + kT1Waves - 1) / kT1Waves;
-      for (int qd = 0; qd < xper_wave; qd++) {
-        const int ins = (qd * kT1Waves + wave) % n_xi;
-        dma16(reinterpret_cast<const uint4*>(x + (size_t)src * K) + min(ins * 64 + lane, K8 - 1),
-              reinterpret_cast<uint8_t*>(xs1 + ins * 64));
-      }
+      const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)src * K);
+      for (int ins = wave; ins < n_xi; ins += WAVES)
+        dma16(xrow + min(ins * 64 + lane, K8 - 1), reinterpret_cast<uint8_t*>(xs1 + ins * 64));
     }
     asm volatile("" ::: "memory");  // the weight loads stay behind the DMAs
-    // ---- all of the wave's weights: two quads x kT1Ins loads, blocks past K
+    // ---- all of the wave's weights: QUADS x kT1Ins loads, blocks past K
     // re-read the row's last block (zeroed below)
-    uint4 w0[kT1Ins], w1[kT1Ins];
+    uint4 w[QUADS][kT1Ins];
 #pragma unroll
-    for (int i = 0; i < kT1Ins; i++) w0[i] = load_nt(wrow[0] + min(16 * i + j, KB - 1));
+    for (int q = 0; q < QUADS; q++)
 #pragma unroll
-    for (int i = 0; i < kT1Ins; i++) w1[i] = load_nt(wrow[1] + min(16 * i + j, KB - 1));
-    bare_barrier<2 * kT1Ins>();  // every wave's DMAs have landed
+      for (int i = 0; i < kT1Ins; i++) w[q][i] = load_nt(wrow[q] + min(16 * i + j, KB - 1));
+    asm volatile("" ::: "memory");
+    const int r_raw = sorted_rows[mb];
+    const int r = (r_raw < 0 || r_raw >= R) ? -1 : r_raw;
+    bare_barrier<QUADS * kT1Ins>();  // every wave's DMAs have landed
     const uint8_t* scb = reinterpret_cast<const uint8_t*>(sc1) + sc_base;
-    float acc0 = 0.f, acc1 = 0.f;
-    auto block_dot = [&](const uint4 w, int rl, int i, float acc) {
+    float acc[QUADS];
+#pragma unroll
+    for (int q = 0; q < QUADS; q++) acc[q] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kT1Ins; i++) {
       const int b = 16 * i + j;
       const int bc = min(b, KB - 1);
       const uint32_t keep = b < KB ? 0xffffffffu : 0u;
-      const float sf = e8m0_to_float(scb[min(rl, rows_wg - 1) * KB + bc]);
-      const uint32_t wd[4] = {w.x & keep, w.y & keep, w.z & keep, w.w & keep};
+      const uint4 x0 = xs1[bc * 4 + 0], x1 = xs1[bc * 4 + 1], x2 = xs1[bc * 4 + 2], x3 = xs1[bc * 4 + 3];
 #pragma unroll
-      for (int d = 0; d < 4; d++) {
-        const uint4 xv = xs1[bc * 4 + d];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 0),
-                                              __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 1),
-                                              __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 2),
-                                              __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 3),
-                                              __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
+      for (int q = 0; q < QUADS; q++) {
+        const int rl = (wave * QUADS + q) * 4 + q4;
+        const float sf = e8m0_to_float(scb[min(rl, rows_wg - 1) * KB + bc]);
+        float a = acc[q];
+#define MXFP4_T1_WORD(WD, XV)                                                                              \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 0),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).x), a, false);                     \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 1),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).y), a, false);                     \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 2),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).z), a, false);                     \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 3),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).w), a, false);
+        MXFP4_T1_WORD(w[q][i].x, x0)
+        MXFP4_T1_WORD(w[q][i].y, x1)
+        MXFP4_T1_WORD(w[q][i].z, x2)
+        MXFP4_T1_WORD(w[q][i].w, x3)
+#undef MXFP4_T1_WORD
+        acc[q] = a;
       }
-      return acc;
-    };
-    const int rl0 = wave * 8 + q4, rl1 = wave * 8 + 4 + q4;
-#pragma unroll
-    for (int i = 0; i < kT1Ins; i++) acc0 = block_dot(w0[i], rl0, i, acc0);
-#pragma unroll
-    for (int i = 0; i < kT1Ins; i++) acc1 = block_dot(w1[i], rl1, i, acc1);
+    }
     // ---- the 16 lanes of a row add their sums (fixed order: deterministic)
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      acc0 += __shfl_xor(acc0, o, 64);
-      acc1 += __shfl_xor(acc1, o, 64);
-    }
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int q = 0; q < QUADS; q++) acc[q] += __shfl_xor(acc[q], o, 64);
     if (j == 0 && r >= 0) {
-      if (rowq[0] < N)
-        out[(size_t)r * N + rowq[0]] = acc0 + (bias ? bf16_bits_to_f32(bias[(size_t)e * N + rowq[0]]) : 0.f);
-      if (rowq[1] < N)
-        out[(size_t)r * N + rowq[1]] = acc1 + (bias ? bf16_bits_to_f32(bias[(size_t)e * N + rowq[1]]) : 0.f);
+#pragma unroll
+      for (int q = 0; q < QUADS; q++)
+        if (rowq[q] < N)
+          out[(size_t)r * N + rowq[q]] = acc[q] + (bias ? bf16_bits_to_f32(bias[(size_t)e * N + rowq[q]]) : 0.f);
     }
   }
 }
+
+#ifndef MXFP4_T1_QUADS
+#define MXFP4_T1_QUADS 1
+#endif
+#ifndef MXFP4_T1_WAVES
+#define MXFP4_T1_WAVES 4
+#endif
+constexpr int kT1Quads = MXFP4_T1_QUADS;
+constexpr int kT1Waves = MXFP4_T1_WAVES;
+constexpr int kT1Rows = T1Shape<kT1Quads, kT1Waves>::kRows;
 
 // largest dynamic LDS a launch may use (the rest of the 160 KB holds rows_lds)
 constexpr int kGemvMaxDynLds = 160 * 1024 - 1024;
@@ -535,7 +558,7 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
                               const int32_t* sorted_rows, float* out, hipStream_t stream) {
   if (T == 1 && K / 32 <= kT1MaxKB) {
     const dim3 grid((N + kT1Rows - 1) / kT1Rows, k < E ? k : E);
-    hipLaunchKernelGGL(expert_gemv_t1_kernel, grid, dim3(kT1Waves * 64), 0, stream, blocks, scales, bias, E, N, K,
+    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves>), grid, dim3(kT1Waves * 64), 0, stream, blocks, scales, bias, E, N, K,
                        x, x_per_slot, k, offsets, sorted_rows, out);
     return hipGetLastError();
   }
