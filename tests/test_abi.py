@@ -97,14 +97,20 @@ def test_workspace_size():
     assert ws(32, 5760, 1, 4, 2880, 0, 1) == 0             # GEMV needs none
     assert ws(32, 5760, 1, 4, 2880, 0, 0) == 0             # auto: 4 rows over 4 experts -> GEMV
     assert ws(32, 2880, 64, 4, 2880, 1, 0) == 0            # auto: 256 rows over 32 experts -> GEMV
-    # GEMM, K = 2880: 45 stages of two blocks.  Per quantized row and stage a
-    # 96-byte code record and two 4-byte scale words; per expert, 256-row
-    # panel and stage 512 repacked weight-scale bytes (5760 rows = 23 panels).
+    # GEMM, K = 2880: 90 blocks = 45 MFMA k-steps, staged 8 blocks at a time:
+    # 12 stages (padded to an even count), 48 k-steps.  The activations are
+    # quantized into row tiles of 128 routed rows (at most ceil(R / 128) plus
+    # one partial tile per expert), per tile, 32-row sub-tile and k-step 3 KB
+    # of codes and 256 bytes of scales; the weight scales are repacked to 2 KB
+    # per expert, 256-row panel (5760 rows = 23 panels) and stage.
+    tiles = 16384 // 128 + 32
     n = ws(32, 5760, 4096, 4, 2880, 0, 2)
-    assert n == 4096 * 45 * 96 + 4096 * 90 * 4 + 32 * 23 * 45 * 512
-    assert ws(32, 2880, 2048, 4, 2880, 1, 0) >= 8192 * 45 * 104 + 32 * 12 * 45 * 512
-    # stage counts are padded to a multiple of 3: K = 64 has 1 stage -> 3
-    assert ws(8, 256, 512, 2, 64, 1, 2) == 1024 * 3 * 96 + 1024 * 6 * 4 + 8 * 1 * 3 * 512
+    assert n == tiles * 4 * 48 * (3072 + 256) + 32 * 23 * 12 * 2048
+    assert ws(32, 2880, 2048, 4, 2880, 1, 0) == (64 + 32) * 4 * 48 * 3328 + 32 * 12 * 12 * 2048
+    # K = 64: one stage, padded to 2 (8 k-steps); 1024 rows over 8 experts: 8 + 8 tiles
+    assert ws(8, 256, 512, 2, 64, 1, 2) == 16 * 4 * 8 * 3328 + 8 * 1 * 2 * 2048
+    # fewer rows than experts: at most one partial tile per row
+    assert ws(32, 256, 3, 2, 64, 0, 2) == (1 + 6) * 4 * 8 * 3328 + 32 * 1 * 2 * 2048
     assert ws(32, 5760, 4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(0, 5760, 4, 4, 128, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(32, 0, 4, 4, 128, 0, 2) == ctypes.c_size_t(-1).value
