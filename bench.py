@@ -3,7 +3,9 @@
 A step is one pass of the hot path over one batch of seeded synthetic input:
 route + group (mxfp4_moe_route_group), the expert projection
 (mxfp4_expert_proj) and, for workloads that have one, the gate-weighted
-combine (moe_combine).  The headline workload is the gpt-oss-20b gate_up
+combine (moe_combine).  A one-token workload routed from logits runs route,
+group and projection as one launch (mxfp4_moe_decode, same outputs); the
+three-call step is reported beside it.  The headline workload is the gpt-oss-20b gate_up
 decode of one token (E=32 experts of [5760, 2880] MXFP4, top-4 from bf16
 router logits).  Inputs are resident in HBM before the timed region; every
 step reads a different copy of the expert weights (enough copies that one
@@ -85,13 +87,19 @@ def algorithmic(p, used):
 
 
 # ------------------------------------------------------------------ GPU measurement
+def fusable(p):
+    """One token routed from logits, within the single-launch decode's limits."""
+    return p.T == 1 and p.logits is not None and p.E <= 64 and p.K <= 3072
+
+
 class Workload:
-    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0):
+    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0, fused: bool = False):
         import torch
         from mxfp4_mixture_experts_amd import synthetic as S
         from mxfp4_mixture_experts_amd.runner import DeviceProblem
         self.torch = torch
         self.p = S.make_config(cfg_index)
+        self.fused = fused and fusable(self.p)
         self.dp = DeviceProblem(self.p, device="cuda:0", path=path)
         self.dp.route_group()            # the device's own routing decides which experts are touched
         counts = torch.diff(self.dp.offsets.to(torch.int64)).cpu().numpy()
@@ -105,13 +113,20 @@ class Workload:
 
     def step(self, i, stream=None):
         b, s = self.weights[i % self.copies]
-        self.dp.route_group(stream)
-        self.dp.expert_proj(stream, blocks=b, scales=s)
+        if self.fused:
+            self.dp.decode(stream, blocks=b, scales=s)
+        else:
+            self.dp.route_group(stream)
+            self.dp.expert_proj(stream, blocks=b, scales=s)
         self.dp.combine(stream)
 
     def proj_only(self, i, stream=None):
+        """The dominant kernel alone: the projection (the single-launch decode when fused)."""
         b, s = self.weights[i % self.copies]
-        self.dp.expert_proj(stream, blocks=b, scales=s)
+        if self.fused:
+            self.dp.decode(stream, blocks=b, scales=s)
+        else:
+            self.dp.expert_proj(stream, blocks=b, scales=s)
 
     def capture(self, fn, n):
         torch = self.torch
@@ -143,10 +158,10 @@ class Workload:
         return e0.elapsed_time(e1), t1 - t0
 
 
-def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None):
+def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fused=False):
     """Time `steps` whole-path steps and, separately, back-to-back launches of the
     projection alone (for the kernel's roofline)."""
-    w = Workload(cfg_index, rotate_bytes, path)
+    w = Workload(cfg_index, rotate_bytes, path, fused)
     for i in range(warmup):
         w.step(i)
     w.torch.cuda.synchronize()
@@ -158,7 +173,7 @@ def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None):
     g_proj.replay()
     ms_proj, _ = w.time_graph(g_proj)
     res = {
-        "p": w.p, "acc": w.acc, "copies": w.copies, "steps": steps,
+        "p": w.p, "acc": w.acc, "copies": w.copies, "steps": steps, "fused": w.fused,
         "ms_per_step": ms_total / steps, "wall_s": wall,
         "proj_us": 1e3 * ms_proj / kreps,
     }
@@ -234,11 +249,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = measure(args.config, args.steps, args.warmup, args.rotate_bytes)
+    head = measure(args.config, args.steps, args.warmup, args.rotate_bytes, fused=True)
     p, acc = head["p"], head["acc"]
     kernel = "expert_gemv" if p.T * p.k <= 8 else "expert_gemm"
     gbs = acc["step"] / (head["ms_per_step"] * 1e-3) / 1e9
-    proj_gbs = acc["proj"] / (head["proj_us"] * 1e-6) / 1e9
+    # the fused launch moves the routing bytes too
+    kernel_bytes = acc["proj"] + (acc["route"] if head["fused"] else 0)
+    proj_gbs = kernel_bytes / (head["proj_us"] * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -255,7 +272,8 @@ def main():
         "config": {
             "workload": describe(p),
             "seed": 0,
-            "path": "route_group + expert_proj(auto: " + ("GEMV" if kernel == "expert_gemv" else "GEMM") + ")"
+            "path": ("moe_decode (route + group + GEMV in one launch)" if head["fused"] else
+                     "route_group + expert_proj(auto: " + ("GEMV" if kernel == "expert_gemv" else "GEMM") + ")")
                     + (" + combine" if p.combine else ""),
             "algorithmic_bytes_per_step": acc["step"],
             "experts_touched": acc["experts_touched"],
@@ -271,9 +289,17 @@ def main():
             "frac": round(proj_gbs / HBM_PEAK_GBS, 4),
             "traffic": read_traffic(kernel),
             "kernel_us": round(head["proj_us"], 3),
-            "algorithmic_bytes_per_launch": acc["proj"],
+            "algorithmic_bytes_per_launch": kernel_bytes,
         },
     }
+    if head["fused"]:
+        # the same step as three launches (route_group, expert_proj, combine)
+        three = measure(args.config, args.steps, args.warmup, args.rotate_bytes, fused=False)
+        line["config"]["three_call_step"] = {
+            "ms_per_step": round(three["ms_per_step"], 6),
+            "GBps": round(acc["step"] / (three["ms_per_step"] * 1e-3) / 1e9, 2),
+            "expert_proj_us": round(three["proj_us"], 3),
+        }
     if not args.no_secondary:
         sec = []
         for cfg, steps in ((2, 100), (3, 20), (4, 40)):

@@ -58,6 +58,8 @@ typedef enum {
 /* Library limits. */
 #define MXFP4_MAX_EXPERTS 512
 #define MXFP4_MAX_TOPK 32
+#define MXFP4_DECODE_MAX_EXPERTS 64  /* mxfp4_moe_decode: experts routed in one wave */
+#define MXFP4_DECODE_MAX_K 3072      /* mxfp4_moe_decode: all of a row's loads in flight at once */
 
 /* Projection paths for mxfp4_expert_proj. */
 #define MXFP4_PATH_AUTO 0  /* GEMV while T * k <= 16 * min(E, T * k), grouped GEMM otherwise */
@@ -153,6 +155,33 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
                       int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
                       const int32_t* expert_offsets, const int32_t* sorted_rows, float* out,
                       int path, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode token: routing, grouping and the expert projection in a single
+ * launch -- mxfp4_moe_route_group (logits route) followed by mxfp4_expert_proj
+ * for T = 1, with the same results bit for bit.  Every workgroup ranks the
+ * token's E logits itself, so no launch waits on another's outputs.
+ * (README "Dense routing" for the routing; README "MXFP4" and
+ * src/experts.linnet fn forward_topk for the one-token product, which streams
+ * each chosen expert's four-bit bytes once.)
+ *
+ *   logits  [1, E] bf16, finite.  1 <= E <= MXFP4_DECODE_MAX_EXPERTS,
+ *           1 <= k <= min(E, MXFP4_MAX_TOPK).
+ *   blocks, scales, bias, N: as for mxfp4_expert_proj;
+ *           32 <= K <= MXFP4_DECODE_MAX_K, K % 32 == 0.
+ *   x       x_per_slot == 0: [1, K] bf16; x_per_slot != 0: [1, k, K] bf16.
+ *   topk_ids [1, k] i32, gates [1, k] f32 (or NULL), expert_offsets [E + 1] i32,
+ *   sorted_rows [k] i32, error_word [1] i32 (or NULL): out, exactly as
+ *           mxfp4_moe_route_group writes them for T = 1.
+ *   out     [1, k, N] f32 out, as mxfp4_expert_proj writes it (GEMV path).
+ * One kernel launch, no workspace.  A NaN logit can leave fewer than k
+ * experts chosen: error_word then holds MXFP4_ROUTE_ERR_ID_RANGE and the
+ * slots without an expert are not written.
+ */
+int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
+                     const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot, int32_t* topk_ids,
+                     float* gates, int32_t* expert_offsets, int32_t* sorted_rows, int32_t* error_word, float* out,
+                     void* stream);
 
 /*
  * Gate-weighted combine of the k projections of each token.

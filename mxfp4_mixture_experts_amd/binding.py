@@ -18,6 +18,7 @@ MXFP4_OK = 0
 MXFP4_PATH_AUTO, MXFP4_PATH_GEMV, MXFP4_PATH_GEMM = 0, 1, 2
 MXFP4_ROUTE_ERR_ID_RANGE, MXFP4_ROUTE_ERR_ID_DUP = 1, 2
 MXFP4_MAX_EXPERTS, MXFP4_MAX_TOPK = 512, 32
+MXFP4_DECODE_MAX_EXPERTS, MXFP4_DECODE_MAX_K = 64, 3072
 
 #: the C entry points this binding uses (all declared in include/mxfp4_moe.h)
 ENTRY_POINTS = (
@@ -27,6 +28,7 @@ ENTRY_POINTS = (
     "mxfp4_expert_proj_workspace_size",
     "mxfp4_expert_proj",
     "moe_combine",
+    "mxfp4_moe_decode",
 )
 
 _lib_handle = None
@@ -64,6 +66,8 @@ def load_library():
     lib.mxfp4_expert_proj.restype = i32
     lib.moe_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.moe_combine.restype = i32
+    lib.mxfp4_moe_decode.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.mxfp4_moe_decode.restype = i32
     _lib_handle = lib
     return lib
 
@@ -157,4 +161,20 @@ def moe_combine(proj, gates, T: int, k: int, N: int, y, stream=None):
     dev = y.device
     st = lib.moe_combine(_ptr(proj, "proj", _F32, dev), _ptr(gates, "gates", _F32, dev), int(T), int(k), int(N),
                          _ptr(y, "y", _F32, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_moe_decode(logits, E: int, k: int, blocks, scales, bias, N: int, K: int, x, x_per_slot: bool,
+                     topk_ids, gates, expert_offsets, sorted_rows, out, error_word=None, stream=None):
+    """One decode token in one launch (mxfp4_moe_decode): routing and grouping from logits [1,E]
+    bf16 and the projection into out [1,k,N] f32, with the same outputs as
+    mxfp4_moe_route_group followed by mxfp4_expert_proj."""
+    lib = load_library()
+    dev = out.device
+    st = lib.mxfp4_moe_decode(
+        _ptr(logits, "logits", _BF16, dev), int(E), int(k), _ptr(blocks, "blocks", _U8, dev),
+        _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(N), int(K), _ptr(x, "x", _BF16, dev),
+        int(bool(x_per_slot)), _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(error_word, "error_word", _I32, dev), _ptr(out, "out", _F32, dev), _stream(stream, dev))
     _check(st)

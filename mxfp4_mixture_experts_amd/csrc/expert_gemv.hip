@@ -29,6 +29,7 @@
 
 #include "kernels.h"
 #include "common.h"
+#include "mxfp4_moe.h"
 
 namespace mxfp4 {
 namespace {
@@ -348,11 +349,33 @@ struct T1Shape {
   static constexpr int kScBlocks = ((kRows * kT1MaxKB + 31) / 16 + 63) / 64 * 64;
 };
 
-template <int QUADS, int WAVES>
+// Routing parameters of the fused single-token decode: the token's router
+// logits in, the routing outputs (written by workgroup (0, 0)) out.
+struct FusedRoute {
+  const uint16_t* logits;
+  int32_t* topk_ids;
+  float* gates;
+  int32_t* offsets;
+  int32_t* sorted_rows;
+  int32_t* error_word;
+};
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// FUSED: the workgroup routes the token itself (E <= 64) instead of reading
+// expert offsets: every lane e counts the experts whose logit beats its own
+// (a larger logit, or an equal one at a lower index), the k with count < k
+// are chosen, and workgroup row blockIdx.y takes the blockIdx.y-th chosen
+// expert in index order; its slot is its count, its routed row the slot.
+// The same arithmetic as the routing kernel, so the outputs are identical.
+template <int QUADS, int WAVES, bool FUSED>
 __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int k,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
+    FusedRoute fr) {
   using Sh = T1Shape<QUADS, WAVES>;
   __shared__ uint4 xs1[kT1MaxKB * 4];        // the token row: 4 entries of 8 bf16 per block
   __shared__ uint4 sc1[Sh::kScBlocks];       // the workgroup's scale rows, from their aligned blocks
@@ -362,10 +385,46 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int e, m0, m1;
-  if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
-  e = __builtin_amdgcn_readfirstlane(e);
-  m0 = __builtin_amdgcn_readfirstlane(m0);
-  m1 = __builtin_amdgcn_readfirstlane(m1);
+  int fused_row = -1;
+  if constexpr (FUSED) {
+    const float l = lane < E ? bf16_bits_to_f32(fr.logits[lane]) : -INFINITY;
+    int rank = 0;
+    for (int jj = 0; jj < E; jj++) {
+      const float lj = readlane_f(l, jj);
+      rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
+    }
+    const bool chosen = lane < E && rank < k;
+    const uint64_t mask = __ballot(chosen);
+    const uint64_t mine = __ballot(chosen && lanes_below(mask) == (int)blockIdx.y);
+    if (mine == 0) return;
+    e = __builtin_amdgcn_readfirstlane(__ffsll((long long)mine) - 1);
+    fused_row = __builtin_amdgcn_readlane(rank, e);
+    m0 = 0;
+    m1 = 1;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
+      // the routing outputs: ids and gates by slot, offsets, grouped rows
+      const float mx = readlane_f(l, __ffsll((long long)__ballot(chosen && rank == 0)) - 1);
+      const float num = chosen ? expf(l - mx) : 0.f;
+      const float sum = wave_sum(num);
+      if (chosen) {
+        fr.topk_ids[rank] = lane;
+        if (fr.gates) fr.gates[rank] = num / sum;
+        fr.sorted_rows[lanes_below(mask)] = rank;
+      }
+      if (lane < E) fr.offsets[lane] = __popcll(mask & ((1ull << lane) - 1));
+      if (lane == 0) {
+        // finite logits always give k experts; a NaN breaks the order
+        const int chosen_n = __popcll(mask);
+        fr.offsets[E] = chosen_n;
+        if (fr.error_word) *fr.error_word = chosen_n == k ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
+      }
+    }
+  } else {
+    if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    m1 = __builtin_amdgcn_readfirstlane(m1);
+  }
   // Never taken (K >= 32): arrays written only by LDS DMA look unwritten to the
   // optimizer, which would then fold their loads away.
   if (K < 0) { xs1[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u); sc1[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u); }
@@ -396,7 +455,9 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     // With one shared token row the output row is not needed until the store:
     // its load then waits behind the weight loads instead of in front of them.
     int src = 0;
-    if (x_per_slot) {
+    if (FUSED) {
+      src = x_per_slot ? fused_row : 0;
+    } else if (x_per_slot) {
       const int r_raw = sorted_rows[mb];
       src = (r_raw < 0 || r_raw >= R) ? 0 : r_raw;
     }
@@ -421,7 +482,7 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
 #pragma unroll
       for (int i = 0; i < kT1Ins; i++) w[q][i] = load_nt(wrow[q] + min(16 * i + j, KB - 1));
     asm volatile("" ::: "memory");
-    const int r_raw = sorted_rows[mb];
+    const int r_raw = FUSED ? fused_row : sorted_rows[mb];
     const int r = (r_raw < 0 || r_raw >= R) ? -1 : r_raw;
     bare_barrier<QUADS * kT1Ins>();  // every wave's DMAs have landed
     const uint8_t* scb = reinterpret_cast<const uint8_t*>(sc1) + sc_base;
@@ -558,8 +619,8 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
                               const int32_t* sorted_rows, float* out, hipStream_t stream) {
   if (T == 1 && K / 32 <= kT1MaxKB) {
     const dim3 grid((N + kT1Rows - 1) / kT1Rows, k < E ? k : E);
-    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves>), grid, dim3(kT1Waves * 64), 0, stream, blocks, scales, bias, E, N, K,
-                       x, x_per_slot, k, offsets, sorted_rows, out);
+    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, false>), grid, dim3(kT1Waves * 64), 0, stream,
+                       blocks, scales, bias, E, N, K, x, x_per_slot, k, offsets, sorted_rows, out, FusedRoute{});
     return hipGetLastError();
   }
 #define MXFP4_GEMV_LAUNCH(MT, W, NCH, NST, KS, OCC)                                                        \
@@ -572,6 +633,18 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
   if (g.nch == 6) MXFP4_GEMV_LAUNCH(16, 8, 6, 2, 1, 2);
   MXFP4_GEMV_LAUNCH(16, 8, 8, 2, 1, 2);
 #undef MXFP4_GEMV_LAUNCH
+}
+
+// One token: routing, grouping and the projection in one launch.
+hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
+                                const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot,
+                                int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
+                                int32_t* error_word, float* out, hipStream_t stream) {
+  const dim3 grid((N + kT1Rows - 1) / kT1Rows, k);
+  const FusedRoute fr{logits, topk_ids, gates, offsets, sorted_rows, error_word};
+  hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true>), grid, dim3(kT1Waves * 64), 0, stream, blocks,
+                     scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, fr);
+  return hipGetLastError();
 }
 
 }  // namespace mxfp4

@@ -63,9 +63,21 @@ class DeviceProblem:
             p = self.p
             B.moe_combine(self.out, self.gates, p.T, p.k, p.N, self.y, stream)
 
+    def decode(self, stream=None, blocks=None, scales=None):
+        """One token from logits: routing, grouping and the projection in one launch."""
+        p = self.p
+        B.mxfp4_moe_decode(self.logits, p.E, p.k, self.blocks if blocks is None else blocks,
+                           self.scales if scales is None else scales, self.bias, p.N, p.K, self.x, p.x_per_slot,
+                           self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.out, self.error_word,
+                           stream)
+
     def run(self, stream=None):
         self.route_group(stream)
         self.expert_proj(stream)
+        self.combine(stream)
+
+    def run_decode(self, stream=None):
+        self.decode(stream)
         self.combine(stream)
 
     def results(self):

@@ -86,6 +86,22 @@ def test_expert_proj_rejects_bad_arguments(kw, status):
     assert _proj(lib, **kw) == status
 
 
+def _decode(lib, E=32, k=4, N=64, K=2880, ptr=16, logits=16):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    lg = ctypes.c_void_p(logits) if logits else None
+    return lib.mxfp4_moe_decode(lg, E, k, p, p, None, N, K, p, 0, p, None, p, p, None, p, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(E=0), dict(E=65), dict(k=0), dict(k=5, E=4), dict(k=33, E=64), dict(N=0), dict(K=0), dict(K=100),
+    dict(K=3104), dict(ptr=0), dict(ptr=8), dict(logits=0),
+])
+def test_moe_decode_rejects_bad_arguments(kw):
+    lib = B.load_library()
+    assert _decode(lib, **kw) == 1, kw
+    assert lib.mxfp4_last_error() != b""
+
+
 def test_expert_proj_t0_is_a_noop():
     lib = B.load_library()
     assert _proj(lib, T=0, ptr=0) == 0

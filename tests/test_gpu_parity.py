@@ -173,6 +173,59 @@ def test_deterministic_and_stream():
 
 
 # ----------------------------------------------------------------- model-size workloads (sampled)
+# ----------------------------------------------------------------- fused one-token decode
+DECODE_CASES = {
+    "gate_up_like": dict(E=32, N=200, K=2880, T=1, k=4, route="logits"),
+    "down_like_per_slot": dict(E=32, N=136, K=2880, T=1, k=4, x_per_slot=True, route="logits"),
+    "k3072_ragged": dict(E=16, N=100, K=3072, T=1, k=3, route="logits"),
+    "k32_top1": dict(E=7, N=5, K=32, T=1, k=1, route="logits"),
+    "all_64_experts": dict(E=64, N=40, K=544, T=1, k=32, x_per_slot=True, route="logits"),
+    "one_expert": dict(E=1, N=17, K=64, T=1, k=1, route="logits"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DECODE_CASES))
+def test_fused_decode(case):
+    """mxfp4_moe_decode against the oracle, and bit for bit against route_group + expert_proj."""
+    p = S.make_custom(**DECODE_CASES[case])
+    p.name = case
+    _announce(f"decode {case}")
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp.out.fill_(float("nan"))
+    dp.run_decode()
+    g = dp.results()
+    assert g["error_word"] == 0
+    check_routing(g, ref)
+    check_close(g["out"], ref["out"], ref["mag"], f"{case} out")
+    if "y" in ref:
+        check_close(g["y"], ref["y"], ref["mag_y"], f"{case} y")
+    dp2 = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp2.run()
+    g2 = dp2.results()
+    for key in ("ids", "offsets", "sorted_rows", "gates", "out", "y"):
+        if g[key] is not None:
+            np.testing.assert_array_equal(g[key], g2[key], err_msg=key)
+
+
+def test_fused_decode_model_size():
+    """The gpt-oss-20b gate_up decode shape, sampled outputs against the oracle."""
+    p = S.make_config(1)
+    _announce(f"{p.name} fused decode (sampled)")
+    ids, gates = O.route_topk(p.logits, p.k)
+    offsets, rows_sorted = O.group_by_expert(ids, p.E)
+    dp = DeviceProblem(p)
+    dp.run_decode()
+    g = dp.results()
+    assert g["error_word"] == 0
+    check_routing(g, dict(ids=ids, gates=gates, offsets=offsets, sorted_rows=rows_sorted))
+    R = p.T * p.k
+    rng = np.random.default_rng(77)
+    rows, cols = _sample_pairs(rng, R, p.N, 2000)
+    vals, mags = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, rows, cols)
+    check_close(g["out"].reshape(R, p.N)[rows, cols], vals, mags, f"{p.name} fused out")
+
+
 def _sample_pairs(rng, R, N, n):
     rows = rng.integers(0, R, n)
     cols = rng.integers(0, N, n)
