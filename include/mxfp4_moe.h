@@ -139,8 +139,9 @@ size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x
  *           e2m1(code) * 2 ** (scales[e, n, j / 32] - 127).  Rows absent from the
  *           grouping are not written.
  *   path    MXFP4_PATH_AUTO / _GEMV / _GEMM.  GEMV multiplies exact bf16
- *           weights (the E2M1 value times the E8M0 factor) by the bf16 inputs on
- *           the bf16 MFMA and sums in fp32; it needs K <= 4096 when T > 4
+ *           weights (the E2M1 value times the E8M0 factor) by the bf16 inputs
+ *           (bf16 dot products for one token with K <= 3072, the bf16 MFMA
+ *           otherwise) and sums in fp32; it needs K <= 4096 when T > 4
  *           (its LDS staging).  GEMM feeds the weights to the MFMA as stored and splits
  *           each bf16 activation block into two MX-FP6 (E2M3) terms; its error
  *           stays within 2e-3 * sum_j |W x| + 1e-5 per output for inputs like
