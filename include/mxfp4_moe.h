@@ -58,6 +58,7 @@ typedef enum {
 /* Library limits. */
 #define MXFP4_MAX_EXPERTS 512
 #define MXFP4_MAX_TOPK 32
+#define MXFP4_GEMM_MAX_K 8192        /* grouped-GEMM path: a weight panel's scale rows staged in LDS */
 #define MXFP4_DECODE_MAX_EXPERTS 64  /* mxfp4_moe_decode: experts routed in one wave */
 #define MXFP4_DECODE_MAX_K 3072      /* mxfp4_moe_decode: all of a row's loads in flight at once */
 
@@ -142,7 +143,7 @@ size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x
  *           weights (the E2M1 value times the E8M0 factor) by the bf16 inputs
  *           (bf16 dot products for one token with K <= 3072, the bf16 MFMA
  *           otherwise) and sums in fp32; it needs K <= 4096 when T > 4
- *           (its LDS staging).  GEMM feeds the weights to the MFMA as stored and splits
+ *           (its LDS staging).  GEMM (K <= MXFP4_GEMM_MAX_K) feeds the weights to the MFMA as stored and splits
  *           each bf16 activation block into two MX-FP6 (E2M3) terms; its error
  *           stays within 2e-3 * sum_j |W x| + 1e-5 per output for inputs like
  *           the model's (see the design notes).

@@ -18,7 +18,7 @@ MXFP4_OK = 0
 MXFP4_PATH_AUTO, MXFP4_PATH_GEMV, MXFP4_PATH_GEMM = 0, 1, 2
 MXFP4_ROUTE_ERR_ID_RANGE, MXFP4_ROUTE_ERR_ID_DUP = 1, 2
 MXFP4_MAX_EXPERTS, MXFP4_MAX_TOPK = 512, 32
-MXFP4_DECODE_MAX_EXPERTS, MXFP4_DECODE_MAX_K = 64, 3072
+MXFP4_DECODE_MAX_EXPERTS, MXFP4_DECODE_MAX_K, MXFP4_GEMM_MAX_K = 64, 3072, 8192
 
 #: the C entry points this binding uses (all declared in include/mxfp4_moe.h)
 ENTRY_POINTS = (

@@ -140,6 +140,10 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
   const int p = resolve_path(path, T, k, E);
   if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
     return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
+  if (p == MXFP4_PATH_GEMM && K > MXFP4_GEMM_MAX_K)
+    return fail(MXFP4_ERR_INVALID_ARG, "K = %d above the grouped GEMM's limit %d", K, MXFP4_GEMM_MAX_K);
+  if (p == MXFP4_PATH_GEMM && (size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull)
+    return fail(MXFP4_ERR_INVALID_ARG, "N * K / 2 = %zu bytes per expert exceeds 4 GiB", (size_t)N * (K / 32) * 16);
   if (p == MXFP4_PATH_GEMM) {
     const size_t need = mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
     if (!workspace || workspace_bytes < need)

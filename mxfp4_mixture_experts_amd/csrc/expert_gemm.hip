@@ -21,18 +21,19 @@
 //    MFMA per term; E2M3 x E2M1 runs at the FP4 MFMA rate on gfx950.
 //  * The pre-pass also gathers the routed rows into row tiles (per expert, in
 //    routed order), written in the register image of the MFMA A operand, so
-//    that a wave fetches one k-step of its 32 rows with three contiguous 1 KB
-//    loads straight into registers, four k-steps ahead.
-//  * Tile = 256 routed rows x 256 weight rows, 8 waves; wave w owns routed
+//    that a wave fetches one k-step of its 32 rows with four contiguous loads
+//    straight into registers, two k-steps ahead.
+//  * Tile = 128 routed rows x 256 weight rows, 4 waves; wave w owns routed
 //    rows 32w .. 32w + 31 and all 256 weight rows (8 accumulators of 32 x 32).
 //    The weight tile is the only operand shared by the waves, and it is the
-//    small one (16 bytes per row and block against 48 for the two activation
-//    terms), so it alone goes through LDS.
-//  * Weight codes reach LDS by LDS DMA in stages of 8 blocks (128 bytes, one
-//    cache line of each weight row): each DMA instruction covers 8 rows x 128
-//    bytes, the lanes of a row taking its blocks in an XOR-swizzled order so
-//    that the MFMA lanes' 16-byte reads (32 rows, one block) hit distinct LDS
-//    banks.  Three stages in flight (96 KB), one barrier per stage.
+//    light one (16 bytes per row and block against 48 for the two activation
+//    terms), so it alone goes through LDS.  Two workgroups share a CU.
+//  * Weight codes are staged 8 blocks (one 128-byte line of each weight row)
+//    at a time: each wave loads 1 KB pieces of 8 rows x 128 bytes into
+//    registers and writes them to LDS, the rows' blocks in an XOR-swizzled
+//    order so that the MFMA lanes' 16-byte reads (32 rows, one block) hit
+//    distinct LDS banks.  Double-buffered, written in two halves while the
+//    current stage is multiplied, one barrier per stage.
 //  * Weight scales are repacked per call (repack_wscales_kernel) into the
 //    per-lane words of a stage: 4 bytes, one per k-step, picked by the MFMA's
 //    scale byte select.
@@ -232,30 +233,67 @@ __global__ __launch_bounds__(kQThreads) void quantize_tiles_kernel(const uint16_
 // ---------------------------------------------------------------------------
 // weight-scale repack: [E][N][KB] bytes -> per (e, n-tile, stage) 64 lanes x
 // 8 sub-tile words; byte j of word c of lane (l32, h) = scale of row
-// 32 c + l32, block 8 s + 2 j + h.  Rows past N repeat row N - 1 and blocks past K repeat block
-// K - 1: they meet zero activations or are never stored.
+// 32 c + l32, block 8 s + 2 j + h.  Rows past N repeat row N - 1 and blocks
+// past K repeat block K - 1: they meet zero activations or are never stored.
 // ---------------------------------------------------------------------------
+
+// Workgroup = one (expert, 256-row panel).  The panel's scale bytes are one
+// contiguous range; the workgroup copies it into LDS with coalesced 4-byte
+// loads (from the 4-byte boundary at or below its start; a last word that
+// would reach past the end of the array is read byte by byte), then thread =
+// one weight row writes, stage by stage, the two lane words of its row: lane
+// (l32, h) with l32 = row % 32, word c = row / 32.
+constexpr int kRepackMaxKB = 256;  // K <= 8192 (LDS: 256 rows x KB bytes + 4)
 
 __global__ __launch_bounds__(kQThreads) void repack_wscales_kernel(const uint8_t* __restrict__ scales, int E, int N,
                                                                    int KB, int NT, int NS,
                                                                    uint32_t* __restrict__ out) {
-  const size_t idx = (size_t)blockIdx.x * kQThreads + threadIdx.x;
-  const size_t total = (size_t)E * NT * NS * kSubN * 64;
-  if (idx >= total) return;
-  const int c = (int)(idx % kSubN);
-  const int lane = (int)((idx / kSubN) & 63);
-  size_t rest = idx / (kSubN * 64);
-  const int s = (int)(rest % NS);
-  rest /= NS;
-  const int nt = (int)(rest % NT);
-  const int e = (int)(rest / NT);
-  const int n = min(nt * kBN + 32 * c + (lane & 31), N - 1);
-  const int h = lane >> 5;
-  const uint8_t* row = scales + ((size_t)e * N + n) * KB;
-  uint32_t v = 0;
+  extern __shared__ uint32_t panel[];  // (kBN * KB + 4) / 4 + 1 words
+  const int nt = blockIdx.x % NT;
+  const int e = blockIdx.x / NT;
+  const int t = threadIdx.x;  // row within the panel
+  const int rows = min(kBN, N - nt * kBN);
+  const size_t total = (size_t)E * N * KB;                   // bytes in the array
+  const size_t first = ((size_t)e * N + (size_t)nt * kBN) * KB;
+  const size_t a0 = first & ~(size_t)3;
+  const int lead = (int)(first - a0);
+  const int nwords = (int)((first + (size_t)rows * KB - a0 + 3) / 4);
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(scales) + a0 / 4;
+  // words wholly inside the array; only the range's last word can fall short
+  const int nsafe = (int)min((size_t)nwords, (total - a0) / 4);
+  constexpr int kU = 24;  // independent loads in flight per thread (one pass for K <= 3072)
+  for (int i0 = t; i0 < nsafe; i0 += kQThreads * kU) {
+    uint32_t v[kU];
 #pragma unroll
-  for (int j = 0; j < kStepsPerStage; j++) v |= (uint32_t)row[min(kStageBlocks * s + 2 * j + h, KB - 1)] << (8 * j);
-  out[idx] = v;
+    for (int u = 0; u < kU; u++) v[u] = src[min(i0 + u * kQThreads, nsafe - 1)];
+#pragma unroll
+    for (int u = 0; u < kU; u++)
+      if (i0 + u * kQThreads < nsafe) panel[i0 + u * kQThreads] = v[u];
+  }
+  if (t == 0 && nsafe < nwords) {
+    const size_t byte = a0 + 4 * (size_t)nsafe;
+    uint32_t v = 0;
+    for (int q = 0; q < 4; q++)
+      if (byte + q < total) v |= (uint32_t)scales[byte + q] << (8 * q);
+    panel[nsafe] = v;
+  }
+  __syncthreads();
+  const uint8_t* prow = reinterpret_cast<const uint8_t*>(panel) + lead + min(t, rows - 1) * KB;
+  const int c = t >> 5, l32 = t & 31;
+  uint32_t* dst = out + ((size_t)e * NT + nt) * NS * (kSubN * 64) + l32 * kSubN + c;
+  for (int s = 0; s < NS; s++) {
+    uint32_t b[kStageBlocks];
+#pragma unroll
+    for (int i = 0; i < kStageBlocks; i++) b[i] = prow[min(kStageBlocks * s + i, KB - 1)];
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < kStepsPerStage; j++) {
+      w0 |= b[2 * j] << (8 * j);
+      w1 |= b[2 * j + 1] << (8 * j);
+    }
+    dst[(size_t)s * (kSubN * 64)] = w0;                // lane l32 (h = 0)
+    dst[(size_t)s * (kSubN * 64) + 32 * kSubN] = w1;   // lane l32 + 32 (h = 1)
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -622,8 +660,9 @@ size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot) {
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
                               int K, const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                               const int32_t* sorted_rows, float* out, void* workspace, hipStream_t stream) {
-  // the GEMM addresses a weight row within its expert with 32-bit offsets
-  if ((size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  // the GEMM addresses a weight row within its expert with 32-bit offsets;
+  // the scale repack stages a panel's scale rows in LDS
+  if ((size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull || K / 32 > kRepackMaxKB) return hipErrorInvalidValue;
   const int NS = stage_count(K);
   const int NKP = NS * kStepsPerStage;
   const int NT = (N + kBN - 1) / kBN;
@@ -638,9 +677,21 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
                      x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, aq, as);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t rep = (size_t)E * NT * NS * kSubN * 64;
-  hipLaunchKernelGGL(repack_wscales_kernel, dim3((unsigned)((rep + kQThreads - 1) / kQThreads)), dim3(kQThreads), 0,
-                     stream, scales, E, N, K / 32, NT, NS, bsc);
+  // dynamic LDS: the panel's scale rows (23 KB at K = 2880, so several
+  // workgroups share a CU)
+  const size_t panel_bytes = ((size_t)(kBN * (K / 32) + 4) / 4 + 1) * 4;
+  if (panel_bytes > 65536) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      err = hipFuncSetAttribute(reinterpret_cast<const void*>(&repack_wscales_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(((kBN * kRepackMaxKB + 4) / 4 + 1) * 4));
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL(repack_wscales_kernel, dim3((unsigned)(E * NT)), dim3(kQThreads), panel_bytes, stream, scales,
+                     E, N, K / 32, NT, NS, bsc);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long tiles_max = (long long)tiles * NT;

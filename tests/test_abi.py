@@ -80,6 +80,7 @@ def _proj(lib, E=32, N=64, K=128, T=4, k=4, path=0, ws=None, ws_bytes=0, ptr=16,
     (dict(path=2, ws=None), 2), (dict(path=2, ws=ctypes.c_void_p(16), ws_bytes=10), 2),
     (dict(path=1, K=8192, T=64, k=4), 1),
     (dict(path=1, K=4128, T=64, k=4), 1),      # GEMV LDS staging: K <= 4096 when T > 4
+    (dict(path=2, K=8224, ws=ctypes.c_void_p(16), ws_bytes=1 << 40), 1),  # GEMM: K <= 8192
 ])
 def test_expert_proj_rejects_bad_arguments(kw, status):
     lib = B.load_library()
