@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(16))) uint8_t sB1[kBN * 128];
   __shared__ __attribute__((aligned(16))) uint32_t sS0[kSubN * 64];
   __shared__ __attribute__((aligned(16))) uint32_t sS1[kSubN * 64];
-  __shared__ int rows_lds[kBM];  // routed row of each tile row, -1 if none
+  __shared__ __attribute__((aligned(16))) int rows_lds[kBM];  // routed row of each tile row, -1 if none
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -607,20 +607,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     pipeline(std::false_type{});
 
   // ---- epilogue: bias and scatter to the routed rows (rows_lds was written
-  // before the first barrier)
+  // before the first barrier).  All loads first (the 8 bias values, the
+  // wave's 16 routed rows as four 16-byte LDS reads), then the stores, so no
+  // store waits on a memory round trip.
   if (!valid) return;
+  float bias_v[kSubN];
+#pragma unroll
+  for (int c = 0; c < kSubN; c++) bias_v[c] = 0.f;
+  if (bias) {  // one uniform branch around all eight loads
+    const uint16_t* brow = bias + (size_t)e * N;
+#pragma unroll
+    for (int c = 0; c < kSubN; c++) bias_v[c] = bf16_bits_to_f32(brow[min(n0 + 32 * c + l32, N - 1)]);
+  }
+  // lane rows 8 q + 4 half + (0..3) of the wave's 32
+  int rr[16];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int4 v = *reinterpret_cast<const int4*>(rows_lds + wave * 32 + 8 * q + 4 * half);
+    rr[4 * q] = v.x; rr[4 * q + 1] = v.y; rr[4 * q + 2] = v.z; rr[4 * q + 3] = v.w;
+  }
+  float* orow[16];
+#pragma unroll
+  for (int j = 0; j < 16; j++) orow[j] = out + (size_t)max(rr[j], 0) * N + n0 + l32;
 #pragma unroll
   for (int c = 0; c < kSubN; c++) {
-    const int n = n0 + 32 * c + l32;
-    if (n >= N) continue;
-    const float bias_v = bias ? bf16_bits_to_f32(bias[(size_t)e * N + n]) : 0.f;
+    if (n0 + 32 * c + l32 >= N) continue;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
-      const int row = wave * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-      const int r = rows_lds[row];
       // streamed out: the outputs must not push the weights and activation
       // tiles other workgroups still read out of the caches
-      if (r >= 0) __builtin_nontemporal_store(acc[c][j] + bias_v, out + (size_t)r * N + n);
+      if (rr[j] >= 0) __builtin_nontemporal_store(acc[c][j] + bias_v[c], orow[j] + 32 * c);
     }
   }
 }
