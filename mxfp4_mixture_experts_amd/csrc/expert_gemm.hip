@@ -311,6 +311,36 @@ struct TileCoord {
 // run on one XCD and share its L2.  Each wave decodes its tile itself (wave
 // scans over 64 experts at a time), so no barrier is needed.
 __device__ __forceinline__ bool locate_tile(const int32_t* offsets, int E, int R, int NT, int lane, TileCoord& c) {
+  if (E <= 64) {
+    // one lane per expert: one read of the offsets and one scan give both the
+    // tile count and this workgroup's tile
+    int b = 0, f = 0, cnt = 0;
+    if (lane < E) {
+      expert_rows(offsets, lane, R, b, f);
+      cnt = (f - b + kBM - 1) / kBM * NT;
+    }
+    const int incl = wave_incl_scan(cnt, lane);
+    const int total = __shfl(incl, 63, 64);
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int j = blockIdx.x / kXcds;
+    if (j >= per_xcd) return false;
+    const int t = (blockIdx.x % kXcds) * per_xcd + j;
+    if (t >= total) return false;
+    const uint64_t hit = wave_ballot(cnt > 0 && incl - cnt <= t && t < incl);
+    const int src = __builtin_ctzll(hit);
+    const int eb = __shfl(b, src, 64), ef = __shfl(f, src, 64);
+    const int before = __shfl(incl, src, 64) - __shfl(cnt, src, 64);
+    const int local = t - before;
+    const int mt = (ef - eb + kBM - 1) / kBM;
+    const int nt = local / mt;
+    const int mi = local - nt * mt;
+    c.e = __builtin_amdgcn_readfirstlane(src);
+    c.m_begin = __builtin_amdgcn_readfirstlane(eb + mi * kBM);
+    c.m_count = __builtin_amdgcn_readfirstlane(min(kBM, ef - (eb + mi * kBM)));
+    c.nt = __builtin_amdgcn_readfirstlane(nt);
+    c.mtile = __builtin_amdgcn_readfirstlane(before / NT + mi);
+    return true;
+  }
   int total = 0;
   for (int base = 0; base < E; base += 64) {
     const int e = base + lane;

@@ -73,6 +73,8 @@ SMALL_CASES = {
     "one_expert": dict(E=1, N=1, K=32, T=5, k=1, route="logits"),
     "one_token_top1": dict(E=16, N=70, K=64, T=1, k=1, route="logits"),
     "wide_k": dict(E=6, N=64, K=4096, T=9, k=2, x_per_slot=True, route="ids"),
+    # more than 64 experts: the multi-chunk expert scans
+    "many_experts": dict(E=100, N=70, K=96, T=60, k=3, route="logits"),
     # one token: the row-streaming kernel up to K = 3072, the MFMA kernel past it
     "one_token_k3072": dict(E=32, N=100, K=3072, T=1, k=4, route="logits"),
     "one_token_k3104": dict(E=4, N=50, K=3104, T=1, k=2, route="logits"),
