@@ -65,6 +65,7 @@ constexpr int kQThreads = 256;           // pre-pass workgroups (one wave per ro
 constexpr int kBM = 128;                 // routed rows per tile: one 32-row sub-tile per wave
 constexpr int kBN = 256;                 // weight rows per tile: 8 sub-tiles of 32
 constexpr int kSubN = kBN / 32;
+static_assert(kThreads == kBN && kThreads >= kBM, "the prologue has one thread per tile column");
 constexpr int kStepsPerStage = 4;        // MFMA k-steps (two MX blocks each) per weight stage
 constexpr int kStageBlocks = 2 * kStepsPerStage;
 constexpr int kStagePad = 2;             // stage counts are padded to a multiple of 2 (the ring)
@@ -424,6 +425,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(16))) uint32_t sS0[kSubN * 64];
   __shared__ __attribute__((aligned(16))) uint32_t sS1[kSubN * 64];
   __shared__ __attribute__((aligned(16))) int rows_lds[kBM];  // routed row of each tile row, -1 if none
+  __shared__ __attribute__((aligned(16))) float bias_lds[kBN];  // bias of each tile column (0 without bias)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -449,6 +451,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     rows_lds[tid] = r;
   }
+  // the tile's bias values, read here so that the epilogue waits on no global load
+  bias_lds[tid] = bias ? bf16_bits_to_f32(bias[(size_t)tc.e * N + min(tc.nt * kBN + tid, N - 1)]) : 0.f;
   const bool valid = wave * 32 < tc.m_count;
 
   // activations: this wave's row sub-tile, k-steps consecutive
@@ -636,18 +640,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   else
     pipeline(std::false_type{});
 
-  // ---- epilogue: bias and scatter to the routed rows (rows_lds was written
-  // before the first barrier).  All loads first (the 8 bias values, the
-  // wave's 16 routed rows as four 16-byte LDS reads), then the stores, so no
-  // store waits on a memory round trip.
+  // ---- epilogue: bias and scatter to the routed rows (rows_lds and
+  // bias_lds were written before the first barrier).  All LDS reads first (the
+  // 8 bias values, the wave's 16 routed rows as four 16-byte reads), then the
+  // stores.
   if (!valid) return;
   float bias_v[kSubN];
 #pragma unroll
-  for (int c = 0; c < kSubN; c++) bias_v[c] = 0.f;
-  if (bias) {  // one uniform branch around all eight loads
-    const uint16_t* brow = bias + (size_t)e * N;
+  for (int c = 0; c < kSubN; c++) bias_v[c] = bias_lds[32 * c + l32];
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    // 16-byte stores: lane (l32 = 4 m + a, half) holds rows 8 q + 4 half + i
+    // (i = 0..3) of column 32 c + l32; a transpose within each lane quad gives
+    // it row 8 q + 4 half + a, columns 32 c + 4 m .. 4 m + 3, so one store
+    // instruction writes 8 rows x 128 contiguous bytes
+    const int a = lane & 3;
+    const int m4 = l32 & ~3;
+    const bool odd1 = (a & 1) != 0, odd2 = (a & 2) != 0;
+    int rq[4];
 #pragma unroll
-    for (int c = 0; c < kSubN; c++) bias_v[c] = bf16_bits_to_f32(brow[min(n0 + 32 * c + l32, N - 1)]);
+    for (int q = 0; q < 4; q++) rq[q] = rows_lds[wave * 32 + 8 * q + 4 * half + a];
+#pragma unroll
+    for (int c = 0; c < kSubN; c++) {
+      const int col = n0 + 32 * c + m4;  // a multiple of 4, so col < N covers all four
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[i] = acc[c][4 * q + i] + bias_v[c];
+        // stage 1 (partner lane a ^ 1), then stage 2 (a ^ 2): an even lane
+        // takes the partner's low pair element into its high one, an odd lane
+        // the partner's high into its low
+#pragma unroll
+        for (int k2 = 0; k2 < 2; k2++) {
+          const int lo = 2 * k2, hi = 2 * k2 + 1;
+          const float snd = odd1 ? v[lo] : v[hi];
+          const float rcv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(snd), 0xB1, 0xF, 0xF, true));
+          if (odd1) v[lo] = rcv; else v[hi] = rcv;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; k2++) {
+          const int lo = k2, hi = k2 + 2;
+          const float snd = odd2 ? v[lo] : v[hi];
+          const float rcv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(snd), 0x4E, 0xF, 0xF, true));
+          if (odd2) v[lo] = rcv; else v[hi] = rcv;
+        }
+        if (rq[q] >= 0 && col < N)
+          __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]},
+                                      reinterpret_cast<f32x4_t*>(out + (size_t)rq[q] * N + col));
+      }
+    }
+    return;
   }
   // lane rows 8 q + 4 half + (0..3) of the wave's 32
   int rr[16];

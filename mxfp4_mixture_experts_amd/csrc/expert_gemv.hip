@@ -360,6 +360,9 @@ struct FusedRoute {
   int32_t* error_word;
 };
 
+// the bias of a projection without one
+__device__ const uint16_t kZeroBf16 = 0;
+
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -451,6 +454,20 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
   const int sc_base = (int)(s_first - s_blk0);
   const uint4* s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
 
+  // the bias values, loaded ahead of the weights (they land with the staged
+  // rows, which every wave waits for anyway), so that the end of the row waits
+  // on no memory round trip.  Unconditional loads (from a zero when there is
+  // no bias: a load under a branch ends in a wait for every load in flight)
+  // through an opaque address (a load through the restrict pointer counts as
+  // invariant and would be sunk to its use, behind the arithmetic).
+  uint32_t bias_bits[QUADS];
+#pragma unroll
+  for (int q = 0; q < QUADS; q++) {
+    const uint16_t* bp = bias ? bias + (size_t)e * N + min(rowq[q], N - 1) : &kZeroBf16;
+    asm volatile("" : "+v"(bp));
+    bias_bits[q] = *(const __attribute__((address_space(1))) uint16_t*)(bp);
+  }
+
   for (int mb = m0; mb < m1; mb++) {  // one routed row per expert unless given ids repeat
     // With one shared token row the output row is not needed until the store:
     // its load then waits behind the weight loads instead of in front of them.
@@ -525,8 +542,12 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     if (j == 0 && r >= 0) {
 #pragma unroll
       for (int q = 0; q < QUADS; q++)
-        if (rowq[q] < N)
-          out[(size_t)r * N + rowq[q]] = acc[q] + (bias ? bf16_bits_to_f32(bias[(size_t)e * N + rowq[q]]) : 0.f);
+        if (rowq[q] < N) {
+          // consumed here, not hoisted (with its wait) in front of the loop
+          uint32_t bb = bias_bits[q];
+          asm volatile("" : "+v"(bb));
+          out[(size_t)r * N + rowq[q]] = acc[q] + bf16_bits_to_f32(bb);
+        }
     }
   }
 }
