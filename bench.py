@@ -68,19 +68,20 @@ def read_traffic(kernel: str):
 
 
 # ------------------------------------------------------------------ accounting
-def algorithmic(p, used):
+def algorithmic(p, used, swiglu=False):
     """Minimum bytes each stage must move and the flops of the projection; `used` is the
-    number of experts that received at least one routed row."""
+    number of experts that received at least one routed row.  swiglu: the projection
+    writes the bf16 gated activation [T, k, N / 2] instead of fp32 [T, k, N]."""
     KB = p.K // 32
     R = p.T * p.k
     weights = used * p.N * (KB * 16 + KB + 2)           # code blocks + scale bytes + bias
     x = (R if p.x_per_slot else p.T) * p.K * 2
-    out = R * p.N * 4
+    out = R * (p.N // 2) * 2 if swiglu else R * p.N * 4
     grouping_in = (p.E + 1) * 4 + R * 4
     proj = weights + x + out + grouping_in
     route = (p.T * p.E * 2 if p.logits is not None else 0) + (R * 4 if p.ids_in is not None else 0)
     route += R * 4 + (R * 4 if p.logits is not None else 0) + (p.E + 1) * 4 + R * 4
-    comb = (R * p.N * 4 + R * 4 + p.T * p.N * 4) if (p.combine and p.logits is not None) else 0
+    comb = (R * p.N * 4 + R * 4 + p.T * p.N * 4) if (p.combine and p.logits is not None and not swiglu) else 0
     flops = 2.0 * R * p.N * p.K
     return {"proj": proj, "route": route, "combine": comb, "step": proj + route + comb, "flops": flops,
             "experts_touched": int(used), "weight_bytes": weights}
@@ -93,17 +94,18 @@ def fusable(p):
 
 
 class Workload:
-    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0, fused: bool = False):
+    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0, fused: bool = False, swiglu: bool = False):
         import torch
         from mxfp4_mixture_experts_amd import synthetic as S
         from mxfp4_mixture_experts_amd.runner import DeviceProblem
         self.torch = torch
         self.p = S.make_config(cfg_index)
-        self.fused = fused and fusable(self.p)
+        self.fused = fused and fusable(self.p) and not swiglu
+        self.swiglu = swiglu
         self.dp = DeviceProblem(self.p, device="cuda:0", path=path)
         self.dp.route_group()            # the device's own routing decides which experts are touched
         counts = torch.diff(self.dp.offsets.to(torch.int64)).cpu().numpy()
-        self.acc = algorithmic(self.p, int((counts > 0).sum()))
+        self.acc = algorithmic(self.p, int((counts > 0).sum()), swiglu)
         touched = max(self.acc["weight_bytes"], 1)
         self.copies = max(1, math.ceil(rotate_bytes / touched))
         self.weights = [(self.dp.blocks, self.dp.scales)]
@@ -115,6 +117,10 @@ class Workload:
         b, s = self.weights[i % self.copies]
         if self.fused:
             self.dp.decode(stream, blocks=b, scales=s)
+        elif self.swiglu:
+            self.dp.route_group(stream)
+            self.dp.expert_proj_swiglu(stream, blocks=b, scales=s)
+            return
         else:
             self.dp.route_group(stream)
             self.dp.expert_proj(stream, blocks=b, scales=s)
@@ -125,6 +131,8 @@ class Workload:
         b, s = self.weights[i % self.copies]
         if self.fused:
             self.dp.decode(stream, blocks=b, scales=s)
+        elif self.swiglu:
+            self.dp.expert_proj_swiglu(stream, blocks=b, scales=s)
         else:
             self.dp.expert_proj(stream, blocks=b, scales=s)
 
@@ -158,10 +166,10 @@ class Workload:
         return e0.elapsed_time(e1), t1 - t0
 
 
-def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fused=False):
+def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fused=False, swiglu=False):
     """Time `steps` whole-path steps and, separately, back-to-back launches of the
     projection alone (for the kernel's roofline)."""
-    w = Workload(cfg_index, rotate_bytes, path, fused)
+    w = Workload(cfg_index, rotate_bytes, path, fused, swiglu)
     for i in range(warmup):
         w.step(i)
     w.torch.cuda.synchronize()
@@ -181,7 +189,7 @@ def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fu
     return res
 
 
-def describe(p):
+def describe(p, swiglu=False):
     name = {
         "tiny": "tiny",
         "gate_up_decode_t1": "gpt-oss-20b gate_up decode",
@@ -189,6 +197,9 @@ def describe(p):
         "gate_up_prefill_t4096": "gpt-oss-20b gate_up prefill",
         "down_prefill_zipf_t2048": "gpt-oss-20b down prefill, Zipf(1.2) routing",
     }[p.name]
+    if swiglu:
+        return (f"{name} + gated activation: E={p.E} N={p.N} K={p.K} T={p.T} top-{p.k}, MXFP4 blocks "
+                f"[{p.E},{p.N},{p.K // 32},16] + E8M0 scales, bf16 x [T,K], bf16 activation out [T,k,N/2]")
     return (f"{name}: E={p.E} N={p.N} K={p.K} T={p.T} top-{p.k}, MXFP4 blocks [{p.E},{p.N},{p.K // 32},16] "
             f"+ E8M0 scales, bf16 x {'[T,k,K]' if p.x_per_slot else '[T,K]'}, fp32 out [T,k,N]"
             + (" + combine [T,N]" if p.combine else ""))
@@ -302,14 +313,16 @@ def main():
         }
     if not args.no_secondary:
         sec = []
-        for cfg, steps in ((2, 100), (3, 20), (4, 40)):
-            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps)
+        # the other model-size workloads, then the two gate_up workloads through
+        # the fused gated activation (bf16 [T, k, N / 2], the down projection's input)
+        for cfg, steps, swiglu in ((2, 100, False), (3, 20, False), (4, 40, False), (1, 200, True), (3, 20, True)):
+            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu)
             a = r["acc"]
             t_step = r["ms_per_step"] * 1e-3
             t_proj = r["proj_us"] * 1e-6
             roof_t = max(a["flops"] / (MXFP4_PEAK_TFLOPS * 1e12), a["step"] / (HBM_PEAK_GBS * 1e9))
             sec.append({
-                "workload": describe(r["p"]),
+                "workload": describe(r["p"], swiglu),
                 "ms_per_step": round(r["ms_per_step"], 4),
                 "step_GBps": round(a["step"] / t_step / 1e9, 1),
                 "step_TFLOPs": round(a["flops"] / t_step / 1e12, 2),

@@ -159,6 +159,29 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
                       int path, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The routed gate/up projection followed by the gpt-oss gated activation,
+ * written as bf16 -- the down projection's per-slot input.
+ * (src/experts.linnet: the gate and up weights share one tensor, interleaved
+ * along its output rows, even rows gate and odd rows multiply; constants
+ * LIMIT = 7 and ALPHA = 1.702 and fn activate: the biased gate clamped from
+ * above at LIMIT, the biased multiplier clamped to [-LIMIT, LIMIT], then
+ * (up + 1) * gate * sigmoid(ALPHA * gate).)
+ *
+ *   Arguments as for mxfp4_expert_proj, with N even, and in place of out:
+ *   act     [T, k, N / 2] bf16 out:
+ *           act[t, s, i] = bf16(swiglu(p[t, s, 2 i], p[t, s, 2 i + 1])), where p
+ *           is what mxfp4_expert_proj would write to out (projection + bias,
+ *           fp32) and swiglu is evaluated in fp32 (expf) and rounded to nearest
+ *           even.  Rows absent from the grouping are not written.
+ *   The same paths, limits, workspace size and errors as mxfp4_expert_proj
+ *   (MXFP4_ERR_INVALID_ARG also for an odd N).
+ */
+int mxfp4_expert_proj_swiglu(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
+                             int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                             const int32_t* expert_offsets, const int32_t* sorted_rows, uint16_t* act,
+                             int path, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode token: routing, grouping and the expert projection in a single
  * launch -- mxfp4_moe_route_group (logits route) followed by mxfp4_expert_proj
  * for T = 1, with the same results bit for bit.  Every workgroup ranks the

@@ -27,6 +27,7 @@ ENTRY_POINTS = (
     "mxfp4_moe_route_group",
     "mxfp4_expert_proj_workspace_size",
     "mxfp4_expert_proj",
+    "mxfp4_expert_proj_swiglu",
     "moe_combine",
     "mxfp4_moe_decode",
 )
@@ -64,6 +65,8 @@ def load_library():
     lib.mxfp4_expert_proj_workspace_size.restype = sz
     lib.mxfp4_expert_proj.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.mxfp4_expert_proj.restype = i32
+    lib.mxfp4_expert_proj_swiglu.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.mxfp4_expert_proj_swiglu.restype = i32
     lib.moe_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.moe_combine.restype = i32
     lib.mxfp4_moe_decode.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -152,6 +155,25 @@ def mxfp4_expert_proj(blocks, scales, bias, E: int, N: int, K: int, x, x_per_slo
         int(E), int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(T), int(k),
         _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
         _ptr(out, "out", _F32, dev), int(path), ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_expert_proj_swiglu(blocks, scales, bias, E: int, N: int, K: int, x, x_per_slot: bool, T: int, k: int,
+                             expert_offsets, sorted_rows, act, path: int = MXFP4_PATH_AUTO, workspace=None,
+                             stream=None):
+    """The routed gate/up projection through the gated activation (mxfp4_expert_proj_swiglu);
+    act [T,k,N/2] bf16 is written in place.  Workspace as for mxfp4_expert_proj."""
+    lib = load_library()
+    dev = act.device
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, "workspace", _U8, dev)
+        ws_bytes = workspace.numel()
+    st = lib.mxfp4_expert_proj_swiglu(
+        _ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev),
+        int(E), int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(T), int(k),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(act, "act", _BF16, dev), int(path), ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream, dev))
     _check(st)
 
 

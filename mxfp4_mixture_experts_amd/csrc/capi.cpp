@@ -74,6 +74,54 @@ int resolve_path(int path, int T, int k, int E) {
 
 bool gemv_fits(int T, int K) { return mxfp4::gemv_lds_bytes(T, K) <= 160 * 1024 - 1024; }  // = kGemvMaxDynLds
 
+// The routed projection; exactly one of out (f32 [T, k, N]) and act (bf16
+// [T, k, N / 2], the gated activation) is written.
+int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
+                     const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
+                     const int32_t* sorted_rows, float* out, uint16_t* act, int path, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
+  if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+  if (act && N % 2 != 0) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be even (gate and up rows in pairs)", N);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "K = %d must be a positive multiple of 32", K);
+  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
+  if (k < 1 || k > E || k > MXFP4_MAX_TOPK)
+    return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, min(E = %d, %d)]", k, E, MXFP4_MAX_TOPK);
+  if ((long long)T * k > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "T * k overflows int32");
+  if ((long long)E * N > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "E * N overflows int32");
+  if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return fail(MXFP4_ERR_INVALID_ARG, "path = %d unknown", path);
+  if (T == 0) return MXFP4_OK;
+  if (!blocks || !scales || !x || !expert_offsets || !sorted_rows || (!out && !act))
+    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
+  const int p = resolve_path(path, T, k, E);
+  if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
+    return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
+  if (p == MXFP4_PATH_GEMM && K > MXFP4_GEMM_MAX_K)
+    return fail(MXFP4_ERR_INVALID_ARG, "K = %d above the grouped GEMM's limit %d", K, MXFP4_GEMM_MAX_K);
+  if (p == MXFP4_PATH_GEMM && (size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull)
+    return fail(MXFP4_ERR_INVALID_ARG, "N * K / 2 = %zu bytes per expert exceeds 4 GiB", (size_t)N * (K / 32) * 16);
+  if (p == MXFP4_PATH_GEMM) {
+    const size_t need = mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
+    if (!workspace || workspace_bytes < need)
+      return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                  need);
+    if (!aligned16(workspace)) return fail(MXFP4_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e;
+  if (p == MXFP4_PATH_GEMV)
+    e = mxfp4::launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
+                                  out, act, static_cast<hipStream_t>(stream));
+  else
+    e = mxfp4::launch_expert_gemm(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
+                                  out, act, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "expert_proj launch");
+  return MXFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,45 +171,18 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
                       const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
                       const int32_t* sorted_rows, float* out, int path, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  g_last_error[0] = '\0';
-  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
-  if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
-  if (K < 32 || K % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "K = %d must be a positive multiple of 32", K);
-  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
-  if (k < 1 || k > E || k > MXFP4_MAX_TOPK)
-    return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, min(E = %d, %d)]", k, E, MXFP4_MAX_TOPK);
-  if ((long long)T * k > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "T * k overflows int32");
-  if ((long long)E * N > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "E * N overflows int32");
-  if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return fail(MXFP4_ERR_INVALID_ARG, "path = %d unknown", path);
-  if (T == 0) return MXFP4_OK;
-  if (!blocks || !scales || !x || !expert_offsets || !sorted_rows || !out)
-    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
-  const int p = resolve_path(path, T, k, E);
-  if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
-    return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
-  if (p == MXFP4_PATH_GEMM && K > MXFP4_GEMM_MAX_K)
-    return fail(MXFP4_ERR_INVALID_ARG, "K = %d above the grouped GEMM's limit %d", K, MXFP4_GEMM_MAX_K);
-  if (p == MXFP4_PATH_GEMM && (size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull)
-    return fail(MXFP4_ERR_INVALID_ARG, "N * K / 2 = %zu bytes per expert exceeds 4 GiB", (size_t)N * (K / 32) * 16);
-  if (p == MXFP4_PATH_GEMM) {
-    const size_t need = mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
-    if (!workspace || workspace_bytes < need)
-      return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
-                  need);
-    if (!aligned16(workspace)) return fail(MXFP4_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  }
-  int st = check_device();
-  if (st != MXFP4_OK) return st;
-  hipError_t e;
-  if (p == MXFP4_PATH_GEMV)
-    e = mxfp4::launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
-                                  out, static_cast<hipStream_t>(stream));
-  else
-    e = mxfp4::launch_expert_gemm(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
-                                  out, workspace, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "expert_proj launch");
-  return MXFP4_OK;
+  if (T > 0 && !out) return fail(MXFP4_ERR_INVALID_ARG, "out is NULL");
+  return expert_proj_impl(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows, out,
+                          nullptr, path, workspace, workspace_bytes, stream);
+}
+
+int mxfp4_expert_proj_swiglu(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
+                             int K, const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
+                             const int32_t* sorted_rows, uint16_t* act, int path, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (T > 0 && !act) return fail(MXFP4_ERR_INVALID_ARG, "act is NULL");
+  return expert_proj_impl(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows, nullptr,
+                          act, path, workspace, workspace_bytes, stream);
 }
 
 int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,

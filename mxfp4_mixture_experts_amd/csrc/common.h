@@ -20,6 +20,33 @@ __device__ __forceinline__ float4 load_nt(const float4* p) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// fp32 -> bf16 bits, rounded to nearest, ties to even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The gpt-oss gated activation of one (gate, up) pair of projection outputs
+// (gpt-oss-20b files page, src/experts.linnet: constants LIMIT = 7 and
+// ALPHA = 1.702, fn activate): the gate clamped from above at LIMIT, the
+// multiplier to [-LIMIT, LIMIT], then (up + 1) * gate * sigmoid(ALPHA * gate).
+// fp32, with sigmoid(ALPHA g) = 1 / (1 + 2^(-ALPHA log2(e) g)) on the
+// hardware exp2 and reciprocal (each within 1 ulp); a very negative gate gives
+// 2^(+large) = inf and a zero product.
+constexpr float kSwigluLimit = 7.0f;
+constexpr float kSwigluAlphaLog2e = (float)(1.702 * 1.4426950408889634);
+__device__ __forceinline__ float swiglu(float gate, float up) {
+  const float g = fminf(gate, kSwigluLimit);
+  const float u = fminf(fmaxf(up, -kSwigluLimit), kSwigluLimit);
+  const float e = __builtin_amdgcn_exp2f(-kSwigluAlphaLog2e * g);
+  return (u + 1.0f) * (g * __builtin_amdgcn_rcpf(1.0f + e));
+}
+
+// The value of lane l ^ 1 (a swap within lane pairs, one DPP move)
+__device__ __forceinline__ float pair_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
 // popcount of the lanes below this one in a 64-bit lane mask
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

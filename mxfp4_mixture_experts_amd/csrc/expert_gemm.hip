@@ -413,11 +413,12 @@ constexpr int kAhead = 2;  // activation k-steps loaded ahead
 // vector-memory counter as out of order and waits for every load before each
 // use.  NS_T > 0: the stage count, known at compile time (straight-line
 // pipeline); NS_T = 0: any K, with a loop.
-template <int NS_T>
+template <int NS_T, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void expert_gemm_kernel(
     const uint8_t* __restrict__ blocks, const uint32_t* __restrict__ wsc, const uint16_t* __restrict__ bias, int E,
     int N, int K, const uint8_t* __restrict__ aq, const uint32_t* __restrict__ as, int T, int k,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
+    uint16_t* __restrict__ act) {
   // weight stages, double-buffered: codes [256 rows][8 swizzled blocks] and
   // scale words [64 lanes][8 sub-tiles]
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kBN * 128];
@@ -648,6 +649,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float bias_v[kSubN];
 #pragma unroll
   for (int c = 0; c < kSubN; c++) bias_v[c] = bias_lds[32 * c + l32];
+  if constexpr (SWIGLU) {
+    // Weight rows 2 i (gate) and 2 i + 1 (up) are the columns of lanes l32 =
+    // 2 i' and 2 i' + 1 (n0 and 32 c are even); the pair's activation column
+    // is n0 / 2 + 16 c + l32 / 2.  Of the tile rows a lane pair holds, the even
+    // lane evaluates those with j / 4 even, the odd lane those with j / 4 odd
+    // (row + 8): one swap within the pair gives each the value it lacks.  Half
+    // the rows (round rnd: j = 8 rnd .. 8 rnd + 7, tile rows 16 rnd .. 16 rnd +
+    // 15) at a time.
+    const int NA = N >> 1;
+    const int a0 = n0 >> 1;
+    const bool odd = (l32 & 1) != 0;
+    // the activation of (c, j = 8 rnd + jj) on the even lane, (c, j + 4) on the odd
+    auto activation = [&](int c, int je) {
+      const float ve = acc[c][je] + bias_v[c];
+      const float vo = acc[c][je + 4] + bias_v[c];
+      const float rcv = pair_swap(odd ? ve : vo);
+      return odd ? swiglu(rcv, vo) : swiglu(ve, rcv);
+    };
+    const int lrow_own = 4 * half + (odd ? 8 : 0);  // + jj: this lane's row within the round
+    if ((NA & 7) == 0 && (reinterpret_cast<uintptr_t>(act) & 15) == 0) {
+      // Staged as this wave's [16 rows][136] bf16 (128 columns + padding that
+      // puts the rows 4, 8 and 12 apart in different banks) in weight slot 0,
+      // which no wave reads after the barrier that ends the next-to-last
+      // stage; then stored as 16-byte pieces, 16 lanes per 256-byte row.
+      constexpr int kStride = 136;
+      uint16_t* st = reinterpret_cast<uint16_t*>(sB0 + wave * (16 * kStride * 2));
+      const int ch = lane & 15;
+#pragma unroll
+      for (int rnd = 0; rnd < 2; rnd++) {
+#pragma unroll
+        for (int c = 0; c < kSubN; c++)
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++)
+            st[(lrow_own + jj) * kStride + 16 * c + (l32 >> 1)] =
+                (uint16_t)f32_to_bf16_bits(activation(c, 8 * rnd + jj));
+#pragma unroll
+        for (int it = 0; it < 4; it++) {
+          const int lrow = 4 * it + (lane >> 4);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + lrow * kStride + ch * 8);
+          const int r = rows_lds[wave * 32 + 16 * rnd + lrow];
+          const int col = a0 + ch * 8;  // NA % 8 == 0: a piece is wholly inside or outside
+          if (r >= 0 && col < NA)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(act + (size_t)r * NA + col));
+        }
+      }
+      return;
+    }
+    // any other width: 2-byte stores from the registers
+#pragma unroll
+    for (int rnd = 0; rnd < 2; rnd++)
+#pragma unroll
+      for (int c = 0; c < kSubN; c++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const float a = activation(c, 8 * rnd + jj);
+          const int r = rows_lds[wave * 32 + 16 * rnd + lrow_own + jj];
+          const int col = a0 + 16 * c + (l32 >> 1);
+          if (r >= 0 && col < NA) act[(size_t)r * NA + col] = (uint16_t)f32_to_bf16_bits(a);
+        }
+    return;
+  }
   if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
     // 16-byte stores: lane (l32 = 4 m + a, half) holds rows 8 q + 4 half + i
     // (i = 0..3) of column 32 c + l32; a transpose within each lane quad gives
@@ -747,7 +809,8 @@ size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot) {
 
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
                               int K, const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
-                              const int32_t* sorted_rows, float* out, void* workspace, hipStream_t stream) {
+                              const int32_t* sorted_rows, float* out, uint16_t* act, void* workspace,
+                              hipStream_t stream) {
   // the GEMM addresses a weight row within its expert with 32-bit offsets;
   // the scale repack stages a panel's scale rows in LDS
   if ((size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull || K / 32 > kRepackMaxKB) return hipErrorInvalidValue;
@@ -785,9 +848,10 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   const long long tiles_max = (long long)tiles * NT;
   const long long grid = (tiles_max + kXcds - 1) / kXcds * kXcds;
   // the gpt-oss-20b widths (K = 2880) have 12 stages
-  auto kern = NS == 12 ? expert_gemm_kernel<12> : expert_gemm_kernel<0>;
+  auto kern = act ? (NS == 12 ? expert_gemm_kernel<12, true> : expert_gemm_kernel<0, true>)
+                  : (NS == 12 ? expert_gemm_kernel<12, false> : expert_gemm_kernel<0, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, blocks, bsc, bias, E, N, K, aq, as, T, k,
-                     offsets, sorted_rows, out);
+                     offsets, sorted_rows, out, act);
   return hipGetLastError();
 }
 

@@ -101,11 +101,12 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-template <int MT, int WAVES, int NCH, int NST, int KS, int OCC>
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void expert_gemv_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int T, int k,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
+    uint16_t* __restrict__ act) {
   // [MT][XS] bf16 token rows, 16 bytes per entry (16 per K group), staged by
   // LDS DMA; entries past K and rows past the pass's count are zeroed in
   // registers when read.
@@ -311,7 +312,28 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     }
 
     // ---- lane l holds tokens 4 * (l / 16) + i of weight row l % 16
-    if (row_ok && kpart == 0) {
+    if constexpr (SWIGLU) {
+      // rows 2 i (gate) and 2 i + 1 (up) sit in lanes l and l ^ 1 (n_base is
+      // a multiple of 16): swap within lane pairs (every lane takes part),
+      // then the even lane writes activation column row / 2
+      float v[4], p[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[i] = tot[i] + bias_v;
+        p[i] = pair_swap(v[i]);
+      }
+      if (row_ok && kpart == 0 && (row & 1) == 0) {
+        const int NA = N >> 1;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = 4 * kq + i;
+          if (m < mc) {
+            const int r = rows_lds[m];
+            if (r >= 0) act[(size_t)r * NA + (row >> 1)] = (uint16_t)f32_to_bf16_bits(swiglu(v[i], p[i]));
+          }
+        }
+      }
+    } else if (row_ok && kpart == 0) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int m = 4 * kq + i;
@@ -373,12 +395,12 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // are chosen, and workgroup row blockIdx.y takes the blockIdx.y-th chosen
 // expert in index order; its slot is its count, its routed row the slot.
 // The same arithmetic as the routing kernel, so the outputs are identical.
-template <int QUADS, int WAVES, bool FUSED>
+template <int QUADS, int WAVES, bool FUSED, bool SWIGLU>
 __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
-    FusedRoute fr) {
+    uint16_t* __restrict__ act, FusedRoute fr) {
   using Sh = T1Shape<QUADS, WAVES>;
   __shared__ uint4 xs1[kT1MaxKB * 4];        // the token row: 4 entries of 8 bf16 per block
   __shared__ uint4 sc1[Sh::kScBlocks];       // the workgroup's scale rows, from their aligned blocks
@@ -539,7 +561,19 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     for (int o = 1; o < 16; o <<= 1)
 #pragma unroll
       for (int q = 0; q < QUADS; q++) acc[q] += __shfl_xor(acc[q], o, 64);
-    if (j == 0 && r >= 0) {
+    if constexpr (SWIGLU) {
+      // rows 4 m + (0, 1) and 4 m + (2, 3) are (gate, up) pairs: row q4 ^ 1
+      // sits 16 lanes away; lanes of even rows write activation column row / 2
+#pragma unroll
+      for (int q = 0; q < QUADS; q++) {
+        uint32_t bb = bias_bits[q];
+        asm volatile("" : "+v"(bb));
+        const float v = acc[q] + bf16_bits_to_f32(bb);
+        const float pv = __shfl_xor(v, 16, 64);
+        if (j == 0 && (q4 & 1) == 0 && r >= 0 && rowq[q] < N)
+          act[(size_t)r * (N >> 1) + (rowq[q] >> 1)] = (uint16_t)f32_to_bf16_bits(swiglu(v, pv));
+      }
+    } else if (j == 0 && r >= 0) {
 #pragma unroll
       for (int q = 0; q < QUADS; q++)
         if (rowq[q] < N) {
@@ -576,14 +610,14 @@ size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K) {
   return xs + sc;
 }
 
-template <int MT, int WAVES, int NCH, int NST, int KS, int OCC>
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU>
 hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                              const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
-                             const int32_t* sorted_rows, float* out, hipStream_t stream) {
+                             const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream) {
   const size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K);
   static bool attr_set = false;  // raise the dynamic LDS limit (to what any K may need) once
   if (!attr_set && lds > 65536) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxDynLds);
     if (err != hipSuccess) return err;
     attr_set = true;
@@ -592,8 +626,8 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
   const int groups = R < E ? R : E;
   const int rows_per_block = WAVES / KS * 16;
   const dim3 grid((N + rows_per_block - 1) / rows_per_block, groups);
-  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC>), grid, dim3(WAVES * 64), lds, stream, blocks, scales, bias, E,
-                     N, K, x, x_per_slot, T, k, offsets, sorted_rows, out);
+  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>), grid, dim3(WAVES * 64), lds, stream, blocks,
+                     scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act);
   return hipGetLastError();
 }
 
@@ -627,6 +661,29 @@ GemvShape gemv_shape(int T, int K) {
   return {16, 8, gemv_pick_chunk(1, 2, K, c16, 3), 2, 1};
 }
 
+template <bool SWIGLU>
+hipError_t launch_gemv_any(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
+                           const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
+                           const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream) {
+  if (T == 1 && K / 32 <= kT1MaxKB) {
+    const dim3 grid((N + kT1Rows - 1) / kT1Rows, k < E ? k : E);
+    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, false, SWIGLU>), grid, dim3(kT1Waves * 64), 0,
+                       stream, blocks, scales, bias, E, N, K, x, x_per_slot, k, offsets, sorted_rows, out, act,
+                       FusedRoute{});
+    return hipGetLastError();
+  }
+#define MXFP4_GEMV_LAUNCH(MT, W, NCH, NST, KS, OCC)                                                               \
+  return launch_gemv_shape<MT, W, NCH, NST, KS, OCC, SWIGLU>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, \
+                                                             offsets, sorted_rows, out, act, stream)
+  const GemvShape g = gemv_shape(T, K);
+  if (g.mt == 1) MXFP4_GEMV_LAUNCH(1, 2, 4, 3, 2, 3);
+  if (g.mt == 4) MXFP4_GEMV_LAUNCH(4, 4, 4, 3, 1, 2);
+  if (g.nch == 4) MXFP4_GEMV_LAUNCH(16, 8, 4, 2, 1, 2);
+  if (g.nch == 6) MXFP4_GEMV_LAUNCH(16, 8, 6, 2, 1, 2);
+  MXFP4_GEMV_LAUNCH(16, 8, 8, 2, 1, 2);
+#undef MXFP4_GEMV_LAUNCH
+}
+
 }  // namespace
 
 size_t gemv_lds_bytes(int T, int K) {
@@ -637,23 +694,12 @@ size_t gemv_lds_bytes(int T, int K) {
 
 hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                               const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
-                              const int32_t* sorted_rows, float* out, hipStream_t stream) {
-  if (T == 1 && K / 32 <= kT1MaxKB) {
-    const dim3 grid((N + kT1Rows - 1) / kT1Rows, k < E ? k : E);
-    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, false>), grid, dim3(kT1Waves * 64), 0, stream,
-                       blocks, scales, bias, E, N, K, x, x_per_slot, k, offsets, sorted_rows, out, FusedRoute{});
-    return hipGetLastError();
-  }
-#define MXFP4_GEMV_LAUNCH(MT, W, NCH, NST, KS, OCC)                                                        \
-  return launch_gemv_shape<MT, W, NCH, NST, KS, OCC>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k,  \
-                                                     offsets, sorted_rows, out, stream)
-  const GemvShape g = gemv_shape(T, K);
-  if (g.mt == 1) MXFP4_GEMV_LAUNCH(1, 2, 4, 3, 2, 3);
-  if (g.mt == 4) MXFP4_GEMV_LAUNCH(4, 4, 4, 3, 1, 2);
-  if (g.nch == 4) MXFP4_GEMV_LAUNCH(16, 8, 4, 2, 1, 2);
-  if (g.nch == 6) MXFP4_GEMV_LAUNCH(16, 8, 6, 2, 1, 2);
-  MXFP4_GEMV_LAUNCH(16, 8, 8, 2, 1, 2);
-#undef MXFP4_GEMV_LAUNCH
+                              const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream) {
+  if (act)
+    return launch_gemv_any<true>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, nullptr,
+                                 act, stream);
+  return launch_gemv_any<false>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out,
+                                nullptr, stream);
 }
 
 // One token: routing, grouping and the projection in one launch.
@@ -663,8 +709,8 @@ hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint
                                 int32_t* error_word, float* out, hipStream_t stream) {
   const dim3 grid((N + kT1Rows - 1) / kT1Rows, k);
   const FusedRoute fr{logits, topk_ids, gates, offsets, sorted_rows, error_word};
-  hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true>), grid, dim3(kT1Waves * 64), 0, stream, blocks,
-                     scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, fr);
+  hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, false>), grid, dim3(kT1Waves * 64), 0, stream,
+                     blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr);
   return hipGetLastError();
 }
 

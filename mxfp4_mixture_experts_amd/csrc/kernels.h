@@ -15,9 +15,11 @@ hipError_t launch_route_group(const uint16_t* logits, const int32_t* ids_in, int
 
 // expert_gemv.hip
 size_t gemv_lds_bytes(int T, int K);
+// act != NULL: the gated activation of (even, odd) output row pairs, bf16
+// [T * k, N / 2], instead of out
 hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
                               int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
-                              const int32_t* offsets, const int32_t* sorted_rows, float* out,
+                              const int32_t* offsets, const int32_t* sorted_rows, float* out, uint16_t* act,
                               hipStream_t stream);
 hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
                                 const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot,
@@ -28,7 +30,7 @@ hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint
 size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
                               int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
-                              const int32_t* offsets, const int32_t* sorted_rows, float* out,
+                              const int32_t* offsets, const int32_t* sorted_rows, float* out, uint16_t* act,
                               void* workspace, hipStream_t stream);
 
 // combine.hip

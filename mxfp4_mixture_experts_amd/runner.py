@@ -38,6 +38,8 @@ class DeviceProblem:
         self.sorted_rows = torch.empty((T * k,), dtype=torch.int32, device=dev)
         self.error_word = torch.zeros((1,), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, k, N), dtype=torch.float32, device=dev)
+        # the gated activation of a gate/up projection (even N): bf16 [T, k, N / 2]
+        self.act = torch.zeros((T, k, N // 2), dtype=torch.bfloat16, device=dev) if N % 2 == 0 else None
         self.y = torch.empty((T, N), dtype=torch.float32, device=dev) if (p.combine and self.gates is not None) else None
         self.set_path(path)
 
@@ -57,6 +59,13 @@ class DeviceProblem:
         B.mxfp4_expert_proj(self.blocks if blocks is None else blocks, self.scales if scales is None else scales,
                             self.bias, p.E, p.N, p.K, self.x, p.x_per_slot, p.T, p.k, self.offsets,
                             self.sorted_rows, self.out, self.path, self.workspace, stream)
+
+    def expert_proj_swiglu(self, stream=None, blocks=None, scales=None):
+        p = self.p
+        B.mxfp4_expert_proj_swiglu(self.blocks if blocks is None else blocks,
+                                   self.scales if scales is None else scales, self.bias, p.E, p.N, p.K, self.x,
+                                   p.x_per_slot, p.T, p.k, self.offsets, self.sorted_rows, self.act, self.path,
+                                   self.workspace, stream)
 
     def combine(self, stream=None):
         if self.y is not None:
@@ -91,4 +100,5 @@ class DeviceProblem:
         }
         r["gates"] = self.gates.cpu().numpy() if self.gates is not None else None
         r["y"] = self.y.cpu().numpy() if self.y is not None else None
+        r["act"] = self.act.view(torch.int16).cpu().numpy().view(np.uint16) if self.act is not None else None
         return r

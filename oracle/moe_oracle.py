@@ -24,7 +24,12 @@ without blocking, fusion or reordering:
   gate_up and down products);
 * combine: y[t, n] = sum over slots of gate[t, s] * out[t, s, n]
   (src/experts.linnet ``forward_topk``: the f32 sum over k and the down bias
-  carried by the router weights).
+  carried by the router weights);
+* gated activation of the gate/up projection: even output rows are the gate,
+  odd rows the multiplier; the gate is clamped from above at LIMIT = 7, the
+  multiplier to [-7, 7], and the result is (up + 1) * gate *
+  sigmoid(1.702 * gate) (src/experts.linnet: constants ``LIMIT`` and
+  ``ALPHA``, fn ``activate``, the interleave comment on ``gate_up_blocks``).
 
 Every function also returns, where the tolerance needs it, the magnitude
 M = sum_j |W x| used by the parity bound |gpu - oracle| <= 2e-3 * M + 1e-5.
@@ -233,6 +238,89 @@ def combine(out: np.ndarray, gates: np.ndarray, mag: np.ndarray | None = None):
     y = np.einsum("ts,tsn->tn", g, out)
     mag_y = None if mag is None else np.einsum("ts,tsn->tn", np.abs(g), np.asarray(mag, dtype=np.float64))
     return y, mag_y
+
+
+# ---------------------------------------------------------------------------
+# gated activation (the gate/up projection's output -> the down projection's input)
+# ---------------------------------------------------------------------------
+
+#: ``swiglu_limit`` and the gate's sigmoid slope (src/experts.linnet, ``LIMIT`` and ``ALPHA``)
+SWIGLU_LIMIT = 7.0
+SWIGLU_ALPHA = 1.702
+
+
+def gate_term(g: np.ndarray) -> np.ndarray:
+    """h(g) = g * sigmoid(ALPHA * g) in float64; the logistic function is
+    evaluated as 1 / (1 + e^-z) for z >= 0 and e^z / (1 + e^z) for z < 0, so
+    no exponent overflows."""
+    g = np.asarray(g, dtype=np.float64)
+    z = SWIGLU_ALPHA * g
+    ez = np.exp(-np.abs(z))
+    sig = np.where(z >= 0, 1.0 / (1.0 + ez), ez / (1.0 + ez))
+    return g * sig
+
+
+def swiglu(gate_up: np.ndarray) -> np.ndarray:
+    """activated[..., i] = (up + 1) * h(gate) with gate = min(p[..., 2 i], LIMIT)
+    and up = clip(p[..., 2 i + 1], -LIMIT, LIMIT), for the biased gate/up
+    projection p (fn ``activate``).  float64, last axis halved."""
+    p = np.asarray(gate_up, dtype=np.float64)
+    assert p.shape[-1] % 2 == 0
+    g = np.minimum(p[..., 0::2], SWIGLU_LIMIT)
+    u = np.clip(p[..., 1::2], -SWIGLU_LIMIT, SWIGLU_LIMIT)
+    return (u + 1.0) * gate_term(g)
+
+
+def _gate_term_argmin() -> float:
+    """The g where h(g) = g * sigmoid(ALPHA * g) is smallest: h'(g) = 0 means
+    1 + z * (1 - sigmoid(z)) = 0 for z = ALPHA * g, solved by bisection on
+    [-3, 0] (h falls before it and rises after)."""
+    lo, hi = -3.0, 0.0
+    for _ in range(200):
+        z = 0.5 * (lo + hi)
+        if 1.0 + z * (1.0 - 1.0 / (1.0 + np.exp(-z))) > 0.0:
+            hi = z
+        else:
+            lo = z
+    return 0.5 * (lo + hi) / SWIGLU_ALPHA
+
+
+GATE_TERM_ARGMIN = _gate_term_argmin()
+
+
+def swiglu_range(gate_up_lo: np.ndarray, gate_up_hi: np.ndarray):
+    """Exact range [min, max] of the activation over every projection between
+    gate_up_lo and gate_up_hi (element-wise boxes).  The factor up + 1 is
+    monotone in up; h(min(g, LIMIT)) is monotone except for its one minimum at
+    GATE_TERM_ARGMIN; the range of a product of two intervals lies at the
+    products of their ends."""
+    lo = np.asarray(gate_up_lo, dtype=np.float64)
+    hi = np.asarray(gate_up_hi, dtype=np.float64)
+    a_lo = np.clip(lo[..., 1::2], -SWIGLU_LIMIT, SWIGLU_LIMIT) + 1.0
+    a_hi = np.clip(hi[..., 1::2], -SWIGLU_LIMIT, SWIGLU_LIMIT) + 1.0
+    g_lo = np.minimum(lo[..., 0::2], SWIGLU_LIMIT)
+    g_hi = np.minimum(hi[..., 0::2], SWIGLU_LIMIT)
+    h_lo_end, h_hi_end = gate_term(g_lo), gate_term(g_hi)
+    inside = (g_lo <= GATE_TERM_ARGMIN) & (GATE_TERM_ARGMIN <= g_hi)
+    b_lo = np.where(inside, gate_term(np.float64(GATE_TERM_ARGMIN)), np.minimum(h_lo_end, h_hi_end))
+    b_hi = np.maximum(h_lo_end, h_hi_end)
+    corners = np.stack([a_lo * b_lo, a_lo * b_hi, a_hi * b_lo, a_hi * b_hi])
+    return corners.min(axis=0), corners.max(axis=0)
+
+
+def swiglu_bound(gate_up: np.ndarray, mag: np.ndarray) -> np.ndarray:
+    """|gpu - swiglu(p)| allowed per bf16 activation when each fp32 projection
+    output may be off by parity_bound(mag): the activation's exact deviation
+    over that error box, plus the final rounding to bf16 (half a unit in the
+    last of 8 significant bits, <= 2^-8 relative), plus fp32 evaluation
+    (the fp32 rounding of ALPHA * log2(e) * gate and hardware exp2 and
+    reciprocal within 1 ulp each: 4e-6 relative, and 2e-5 absolute)."""
+    p = np.asarray(gate_up, dtype=np.float64)
+    e = parity_bound(mag)
+    f = swiglu(p)
+    f_min, f_max = swiglu_range(p - e, p + e)
+    dev = np.maximum(f_max - f, f - f_min)
+    return dev + (2.0 ** -8 + 4e-6) * (np.abs(f) + dev) + 2e-5
 
 
 def parity_bound(mag: np.ndarray) -> np.ndarray:

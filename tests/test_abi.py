@@ -87,6 +87,26 @@ def test_expert_proj_rejects_bad_arguments(kw, status):
     assert _proj(lib, **kw) == status
 
 
+def _proj_swiglu(lib, E=32, N=64, K=128, T=4, k=4, path=0, ptr=16, act=16):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    a = ctypes.c_void_p(act) if act else None
+    return lib.mxfp4_expert_proj_swiglu(p, p, None, E, N, K, p, 0, T, k, p, p, a, path, None, ctypes.c_size_t(0),
+                                        None)
+
+
+@pytest.mark.parametrize("kw", [dict(N=63), dict(N=1), dict(act=0), dict(K=100), dict(E=0), dict(ptr=0),
+                                dict(path=2)])
+def test_expert_proj_swiglu_rejects_bad_arguments(kw):
+    lib = B.load_library()
+    assert _proj_swiglu(lib, **kw) in (1, 2), kw
+    assert lib.mxfp4_last_error() != b""
+
+
+def test_expert_proj_swiglu_t0_is_a_noop():
+    lib = B.load_library()
+    assert _proj_swiglu(lib, T=0, ptr=0, act=0) == 0
+
+
 def _decode(lib, E=32, k=4, N=64, K=2880, ptr=16, logits=16):
     p = ctypes.c_void_p(ptr) if ptr else None
     lg = ctypes.c_void_p(logits) if logits else None

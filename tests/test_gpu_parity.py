@@ -266,3 +266,82 @@ def test_model_size_config(cfg, path):
             y_ref += gates[toks, s] * v
             m_ref += gates[toks, s] * m
         check_close(g["y"][toks, cols], y_ref, m_ref, f"{p.name} y")
+
+
+# ----------------------------------------------------------------- gated activation
+def check_act(act_bits, proj_ref, mag_ref, what):
+    """bf16 activations against the oracle's activation of its own projection,
+    within swiglu_bound (the projection's parity bound carried through the
+    activation, plus the bf16 rounding)."""
+    gpu = O.bf16_to_f64(act_bits)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite activation"
+    ref = O.swiglu(proj_ref)
+    bound = O.swiglu_bound(proj_ref, mag_ref)
+    err = np.abs(gpu - ref)
+    bad = np.argwhere(err > bound)
+    worst = float((err / bound).max()) if err.size else 0.0
+    assert bad.size == 0, f"{what}: {len(bad)} activations outside the bound, worst {worst:.3g}, first {bad[:3].tolist()}"
+    return worst
+
+
+SWIGLU_CASES = {
+    "tiny": None,                                                             # the tiny workload (N = 256)
+    "wide_vector_stores": dict(E=8, N=512, K=320, T=37, k=3, route="logits"),  # N / 2 % 8 == 0, two panels
+    "ragged_narrow": dict(E=8, N=200, K=320, T=37, k=3, route="logits"),       # N / 2 = 100: 2-byte stores
+    "ragged_panel": dict(E=4, N=260, K=416, T=300, k=2, route="logits"),
+    "per_slot_ids": dict(E=8, N=136, K=2880, T=50, k=4, x_per_slot=True, route="ids+logits"),
+    "many_experts": dict(E=100, N=70, K=96, T=60, k=3, route="logits"),
+    "few_tokens": dict(E=8, N=64, K=256, T=3, k=2, route="logits"),
+    "one_token": dict(E=32, N=100, K=3072, T=1, k=4, route="logits"),
+    "one_token_k3104": dict(E=4, N=50, K=3104, T=1, k=2, route="logits"),
+}
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("case", sorted(SWIGLU_CASES))
+def test_swiglu_small(case, path):
+    kw = SWIGLU_CASES[case]
+    p = S.make_config(0) if kw is None else S.make_custom(**kw)
+    p.name = case
+    _announce(f"swiglu {case} path={PATHS[path]}")
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p, path=path)
+    dp.route_group()
+    dp.expert_proj_swiglu()
+    g = dp.results()
+    check_routing(g, ref)
+    check_act(g["act"], ref["out"], ref["mag"], f"{case} act")
+
+
+def test_swiglu_matches_own_projection():
+    """The fused activation equals the activation of the same path's fp32
+    projection, up to fp32 evaluation and the bf16 rounding."""
+    p = S.make_custom(E=8, N=512, K=2880, T=40, k=4, route="logits")
+    _announce("swiglu vs own projection")
+    for path in (1, 2):
+        dp = DeviceProblem(p, path=path)
+        dp.run()
+        dp.expert_proj_swiglu()
+        g = dp.results()
+        out = g["out"].astype(np.float64)
+        check_act(g["act"], out, np.zeros_like(out), f"path {PATHS[path]} act vs own out")
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_swiglu_model_size(cfg):
+    """The gate_up workloads through the activation, on sampled activations."""
+    p = S.make_config(cfg)
+    _announce(f"swiglu {p.name} (sampled)")
+    ids, _ = O.route_topk(p.logits, p.k)
+    dp = DeviceProblem(p)
+    dp.route_group()
+    dp.expert_proj_swiglu()
+    g = dp.results()
+    R, NA = p.T * p.k, p.N // 2
+    rng = np.random.default_rng(2000 + cfg)
+    rows, cols = _sample_pairs(rng, R, NA, 800)
+    vg, mg = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, rows, 2 * cols)
+    vu, mu = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, rows, 2 * cols + 1)
+    proj = np.stack([vg, vu], axis=-1)
+    mag = np.stack([mg, mu], axis=-1)
+    check_act(g["act"].reshape(R, NA)[rows, cols][:, None], proj, mag, f"{p.name} act")

@@ -299,6 +299,120 @@ def test_pins_catch_tie_to_higher_index(monkeypatch):
         test_routing_tie_fixture()
 
 
+# ----------------------------------------------------------------- gated activation
+def test_swiglu_constants_match_page_fixture():
+    """src/experts.linnet: LIMIT and ALPHA."""
+    vals = dict(r.split() for r in read_golden("swiglu_constants.txt"))
+    assert O.SWIGLU_LIMIT == float(vals["LIMIT"]) and O.SWIGLU_ALPHA == float(vals["ALPHA"])
+
+
+def _swiglu_scalar(g, u):
+    """fn activate, one (gate, up) pair, with the math module."""
+    import math
+    g = min(g, 7.0)
+    u = min(max(u, -7.0), 7.0)
+    z = -1.702 * g
+    if z > 700.0:
+        return 0.0 * (u + 1.0)
+    return (u + 1.0) * g / (1.0 + math.exp(z))
+
+
+def test_swiglu_interleave_and_formula():
+    """Even rows gate, odd rows multiply (the gate_up_blocks comment), fn activate's formula."""
+    rng = np.random.default_rng(7)
+    p = np.concatenate([rng.normal(0, 4, (5, 40)), [[9.0, 0.5, -9.0, 8.0, 0.3, -8.0, 7.5, 7.5, -1e4, 3.0, 1e4, -1.0]
+                                                    + [0.0] * 28]], axis=0)
+    f = O.swiglu(p)
+    assert f.shape == (6, 20)
+    for r in range(6):
+        for i in range(20):
+            assert f[r, i] == pytest.approx(_swiglu_scalar(p[r, 2 * i], p[r, 2 * i + 1]), rel=1e-13, abs=1e-300)
+
+
+def test_swiglu_gate_term_matches_torch_silu():
+    """g * sigmoid(ALPHA g) = silu(ALPHA g) / ALPHA, torch's float64 silu as the library routine."""
+    import torch
+    g = np.linspace(-60.0, 60.0, 2001)
+    ref = torch.nn.functional.silu(torch.tensor(1.702 * g, dtype=torch.float64)).numpy() / 1.702
+    np.testing.assert_allclose(O.gate_term(g), ref, rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_special_cases():
+    """fn activate: no gate gives nothing; an up of -1 cancels the + 1; the clamps."""
+    h = lambda g: g / (1.0 + np.exp(-1.702 * g))
+    cases = [((0.0, 3.0), 0.0), ((2.0, -1.0), 0.0), ((50.0, 0.0), h(7.0)), ((7.0, 100.0), 8.0 * h(7.0)),
+             ((1.5, -100.0), -6.0 * h(1.5)), ((-1e6, 5.0), 0.0), ((-0.5, 2.0), 3.0 * h(-0.5))]
+    for (g, u), want in cases:
+        got = O.swiglu(np.array([g, u]))[0]
+        assert np.isfinite(got) and got == pytest.approx(want, rel=1e-14, abs=1e-300), (g, u)
+
+
+def test_gate_term_minimum():
+    """The one minimum of g * sigmoid(ALPHA g), against scipy's bounded scalar minimizer."""
+    from scipy.optimize import minimize_scalar
+    res = minimize_scalar(lambda g: float(O.gate_term(np.float64(g))), bounds=(-3.0, 0.0), method="bounded",
+                          options={"xatol": 1e-10})
+    assert abs(res.x - O.GATE_TERM_ARGMIN) < 1e-6
+    d = 1e-4
+    assert O.gate_term(O.GATE_TERM_ARGMIN - d) > O.gate_term(O.GATE_TERM_ARGMIN)
+    assert O.gate_term(O.GATE_TERM_ARGMIN + d) > O.gate_term(O.GATE_TERM_ARGMIN)
+
+
+def test_swiglu_range_is_exact_on_boxes():
+    """Brute force: the activation over a dense grid of each error box stays inside
+    swiglu_range, and the range's ends are reached (to the grid's resolution)."""
+    rng = np.random.default_rng(3)
+    centers = np.concatenate([rng.normal(0, 3, (300, 2)), [[-0.75, 1.0], [6.9, 6.9], [-7.2, -6.9], [0.0, -1.0]]])
+    half = np.concatenate([rng.uniform(0, 1.5, (300, 2)), [[0.3, 0.2], [0.3, 0.3], [0.5, 0.5], [0.4, 0.4]]])
+    lo, hi = O.swiglu_range(centers - half, centers + half)
+    t = np.linspace(0.0, 1.0, 81)
+    for i in range(len(centers)):
+        gg = centers[i, 0] - half[i, 0] + 2 * half[i, 0] * t
+        uu = centers[i, 1] - half[i, 1] + 2 * half[i, 1] * t
+        G, U = np.meshgrid(gg, uu)
+        vals = O.swiglu(np.stack([G.ravel(), U.ravel()], axis=-1))[:, 0]
+        assert vals.min() >= lo[i, 0] - 1e-12 and vals.max() <= hi[i, 0] + 1e-12, i
+        span = hi[i, 0] - lo[i, 0]
+        assert vals.min() <= lo[i, 0] + 0.02 * span + 1e-12 and vals.max() >= hi[i, 0] - 0.02 * span - 1e-12, i
+
+
+def test_swiglu_bound_covers_bf16_rounding():
+    """Exact projections: the bound is at least the bf16 rounding of the activation."""
+    rng = np.random.default_rng(5)
+    p = rng.normal(0, 3, (50, 64))
+    f = O.swiglu(p)
+    rounded = O.bf16_to_f64(S.f32_to_bf16_bits(f.astype(np.float32)))
+    assert np.all(np.abs(rounded - f) <= O.swiglu_bound(p, np.zeros_like(p)))
+
+
+def test_pins_catch_swapped_gate_and_up(monkeypatch):
+    def wrong(gate_up):
+        p = np.asarray(gate_up, dtype=np.float64)
+        g = np.minimum(p[..., 1::2], 7.0)
+        u = np.clip(p[..., 0::2], -7.0, 7.0)
+        return (u + 1.0) * O.gate_term(g)
+    monkeypatch.setattr(O, "swiglu", wrong)
+    with pytest.raises(AssertionError):
+        test_swiglu_interleave_and_formula()
+
+
+def test_pins_catch_two_sided_gate_clamp(monkeypatch):
+    def wrong(gate_up):
+        p = np.asarray(gate_up, dtype=np.float64)
+        g = np.clip(p[..., 0::2], -7.0, 7.0)
+        u = np.clip(p[..., 1::2], -7.0, 7.0)
+        return (u + 1.0) * O.gate_term(g)
+    monkeypatch.setattr(O, "swiglu", wrong)
+    with pytest.raises(AssertionError):
+        test_swiglu_interleave_and_formula()
+
+
+def test_pins_catch_wrong_slope(monkeypatch):
+    monkeypatch.setattr(O, "SWIGLU_ALPHA", 1.0)
+    with pytest.raises(AssertionError):
+        test_swiglu_gate_term_matches_torch_silu()
+
+
 # ----------------------------------------------------------------- inputs
 def test_bf16_rounding_is_nearest_even():
     v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], np.float32)
