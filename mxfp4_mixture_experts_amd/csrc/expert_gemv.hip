@@ -96,6 +96,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// the bias of a projection without one
+__device__ const uint16_t kZeroBf16 = 0;
+
 __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   // 2^(s - 127) as an fp32 bit pattern; s = 0 is the subnormal 2^-127
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
@@ -106,10 +109,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int T, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
-    uint16_t* __restrict__ act) {
+    uint16_t* __restrict__ act, int sc_blk) {
   // [MT][XS] bf16 token rows, 16 bytes per entry (16 per K group), staged by
   // LDS DMA; entries past K and rows past the pass's count are zeroed in
-  // registers when read.
+  // registers when read.  Then, per row block of the workgroup, sc_blk
+  // entries of weight scales.
   extern __shared__ uint4 xs[];
   __shared__ int rows_lds[MT];
   // KS > 1: the KS waves of a row group split K and add their partial sums here
@@ -128,10 +132,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   const int R = T * k;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  // after the token rows: the workgroup's weight-scale rows (16 * WAVES rows x
-  // KB bytes, contiguous in memory), staged once as the aligned 16-byte blocks
-  // covering them
-  uint4* sc_lds = xs + MT * XS;
 
   int e, m0, m1;
   if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
@@ -139,36 +139,46 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   m0 = __builtin_amdgcn_readfirstlane(m0);
   m1 = __builtin_amdgcn_readfirstlane(m1);
 
-  const int wg_row0 = blockIdx.x * RW * 16;
+  // Row blocks of RW * 16 weight rows: this workgroup takes blocks
+  // blockIdx.x + j * gridDim.x, j < nb, and streams them back to back (the
+  // first chunks of block j + 1 are requested while block j finishes), so
+  // the token rows are staged once for all of them.
+  const int nblk = (N + RW * 16 - 1) / (RW * 16);
+  const int nb = (nblk - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int rw = wave / KS, kpart = wave % KS;
-  const int n_base = wg_row0 + rw * 16;
-  const int row = n_base + (lane & 15);
   const int kq = lane >> 4;
-  const bool row_ok = row < N;
-  // rows past N and blocks past K read real (clamped) weights and meet zero activations
-  const uint4* wrow = reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(row, N - 1)) * KB;
-  const float bias_v = (bias && row_ok) ? bf16_bits_to_f32(bias[(size_t)e * N + row]) : 0.f;
-
-  auto load_chunk = [&](int c0, uint4 (&w)[NCH]) {
+  auto block_row0 = [&](int j) { return ((int)blockIdx.x + j * (int)gridDim.x) * RW * 16; };
+  // this lane's weight row in block j (rows past N re-read row N - 1 and meet zero activations)
+  auto lane_row = [&](int j) { return block_row0(j) + rw * 16 + (lane & 15); };
+  auto wrow_of = [&](int j) {
+    return reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(lane_row(j), N - 1)) * KB;
+  };
+  // step 1: the chunk's NCH groups; step 0: NCH reads of the same 16 bytes
+  // (a placeholder request, almost free)
+  auto load_chunk = [&](const uint4* wr, int c0, uint4 (&w)[NCH], int step = 1) {
     // groups past K re-read the row's last block; they meet zero activations
 #pragma unroll
-    for (int i = 0; i < NCH; i++) w[i] = load_nt(wrow + min((c0 + i) * 4 + kq, KB - 1));
+    for (int i = 0; i < NCH; i++) w[i] = load_nt(wr + min((c0 + i * step) * 4 + kq, KB - 1));
   };
 
-  // ---- weight scales of rows wg_row0 .. wg_row0 + 16 * WAVES - 1 (clamped to
-  // N - 1) into LDS: the aligned 16-byte blocks from the one holding the first
-  // byte to the one holding the last (an aligned block that holds a valid byte
-  // never leaves that byte's page).  Lane byte (row, kb) then sits at
-  // sc_base + (row - wg_row0) * KB + kb.
-  const int rows_wg = min(RW * 16, N - wg_row0);
+  // ---- weight scales of block j: rows row0 .. row0 + RW * 16 - 1 (clamped to
+  // N - 1), contiguous in memory: the aligned 16-byte blocks from the one
+  // holding the first byte to the one holding the last (an aligned block that
+  // holds a valid byte never leaves that byte's page).  Lane byte (row, kb)
+  // then sits at sc_base + (row - row0) * KB + kb of the block's LDS region.
   const uintptr_t sbase = reinterpret_cast<uintptr_t>(scales);
-  const uintptr_t s_first = sbase + ((size_t)e * N + wg_row0) * KB;
-  const uintptr_t s_blk0 = s_first & ~(uintptr_t)15;
-  const uintptr_t s_blk1 = (s_first + (size_t)rows_wg * KB - 1) & ~(uintptr_t)15;
-  const int n_sblk = (int)((s_blk1 - s_blk0) >> 4) + 1;
-  const int sc_base = (int)(s_first - s_blk0);
-  // the same blocks through the (global) scales pointer, so loads stay global
-  const uint4* s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
+  auto sc_span = [&](int j, int& n_sblk, int& sc_base, const uint4*& s_blocks) {
+    const int row0 = block_row0(j);
+    const int rows_b = min(RW * 16, N - row0);
+    const uintptr_t s_first = sbase + ((size_t)e * N + row0) * KB;
+    const uintptr_t s_blk0 = s_first & ~(uintptr_t)15;
+    const uintptr_t s_blk1 = (s_first + (size_t)rows_b * KB - 1) & ~(uintptr_t)15;
+    n_sblk = (int)((s_blk1 - s_blk0) >> 4) + 1;
+    sc_base = (int)(s_first - s_blk0);
+    // the same blocks through the (global) scales pointer, so loads stay global
+    s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
+  };
+  uint4* sc_lds = xs + MT * XS;
   auto sorted_rows_checked = [&](int i) {
     const int r = sorted_rows[i];
     return (r < 0 || r >= R) ? -1 : r;
@@ -176,9 +186,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 
   for (int mb = m0; mb < m1; mb += MT) {
     const int mc = min(MT, m1 - mb);
-    // ---- prologue.  The token rows and the weight-scale blocks go to LDS by
-    // LDS DMA (no registers), issued before all of this wave's first NST
-    // chunks of weights; the wave then waits for its DMAs only (the weight
+    // ---- prologue.  The token rows and every block's weight-scale blocks go
+    // to LDS by LDS DMA (no registers), issued before all of this wave's first
+    // NST chunks of weights; the wave then waits for its DMAs only (the weight
     // loads are younger, and the counter is in order) and meets the others.
     // Every wave issues the same number of DMAs (a wave with fewer real ones
     // repeats one: the same bytes to the same place).  Lanes past the data
@@ -198,12 +208,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     if (threadIdx.x < MT) rows_lds[threadIdx.x] = threadIdx.x < mc ? sorted_rows_checked(mb + threadIdx.x) : -1;
     {
       // scale blocks: 64 per DMA, instructions spread over the waves
-      const int n_si = (n_sblk + 63) >> 6;
-      const int per_wave = (n_si + WAVES - 1) / WAVES;
-      for (int q = 0; q < per_wave; q++) {
-        const int ins = (q * WAVES + wave) % n_si;
-        const int b = min(ins * 64 + lane, n_sblk - 1);
-        dma16(s_blocks + b, reinterpret_cast<uint8_t*>(sc_lds + ins * 64));
+      for (int j = 0; j < nb; j++) {
+        int n_sblk, sc_base;
+        const uint4* s_blocks;
+        sc_span(j, n_sblk, sc_base, s_blocks);
+        const int n_si = (n_sblk + 63) >> 6;
+        const int per_wave = (n_si + WAVES - 1) / WAVES;
+        for (int q = 0; q < per_wave; q++) {
+          const int ins = (q * WAVES + wave) % n_si;
+          const int b = min(ins * 64 + lane, n_sblk - 1);
+          dma16(s_blocks + b, reinterpret_cast<uint8_t*>(sc_lds + j * sc_blk + ins * 64));
+        }
       }
       // token rows: 64 entries per DMA
       const int x_per_row = (NITC * 16 + 63) >> 6;
@@ -211,25 +226,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       const int xper_wave = (n_xi + WAVES - 1) / WAVES;
       for (int q = 0; q < xper_wave; q++) {
         const int ins = (q * WAVES + wave) % n_xi;
-        const int m = ins / x_per_row, j = ins - m * x_per_row;
-        const int c = min(j * 64 + lane, K8 - 1);
+        const int m = ins / x_per_row, jx = ins - m * x_per_row;
+        const int c = min(jx * 64 + lane, K8 - 1);
         dma16(reinterpret_cast<const uint4*>(x + (size_t)src[m] * K) + c,
-              reinterpret_cast<uint8_t*>(xs + m * XS + j * 64));
+              reinterpret_cast<uint8_t*>(xs + m * XS + jx * 64));
       }
     }
     asm volatile("" ::: "memory");  // the weight loads stay behind the DMAs
     uint4 wa[NCH], wb[NCH], wc[NCH];
     const int g_first = kpart * (NITC / KS);  // this wave's first K group
-    load_chunk(g_first, wa);
-    load_chunk(g_first + NCH, wb);
-    if (NST == 3) load_chunk(g_first + 2 * NCH, wc);
+    {
+      const uint4* wr0 = wrow_of(0);
+      load_chunk(wr0, g_first, wa);
+      load_chunk(wr0, g_first + NCH, wb);
+      if (NST == 3) load_chunk(wr0, g_first + 2 * NCH, wc);
+    }
     bare_barrier<NST * NCH>();  // every wave's DMAs have landed
-    const uint8_t* srow = reinterpret_cast<const uint8_t*>(sc_lds) + sc_base +
-                          (size_t)min(row - wg_row0, rows_wg - 1) * KB;
 
-    f32x4_v acc[4];
-#pragma unroll
-    for (int d = 0; d < 4; d++) acc[d] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     const bool xrow_ok = (lane & 15) < mc;
     const uint4* xrow = xs + min(lane & 15, mc - 1) * XS + kq * 4;
     // rows past the pass's count and entries past K (LDS padding) read as zero
@@ -239,107 +252,150 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     };
 
-    // ---- NST chunks of NCH K groups in flight: a chunk is converted and
-    // multiplied while the later ones load (4 MFMAs per 128-bit load into four
-    // independent accumulators; A = token rows, lane l: row l % 16; B = weights)
-    // At 3 waves per SIMD the next group's token rows are not prefetched from
-    // LDS (the registers are needed for the weights in flight; the other waves
-    // cover the LDS latency).
-    constexpr bool kXPrefetch = OCC < 3;
-    auto compute_chunk = [&](int c0, const uint4 (&w)[NCH]) {
-      uint32_t s[NCH];
-#pragma unroll
-      for (int i = 0; i < NCH; i++) s[i] = srow[min((c0 + i) * 4 + kq, KB - 1)];
-      uint4 xv[4], xn[4];
-#pragma unroll
-      for (int d = 0; d < 4; d++) xv[d] = xread(c0 * 16 + d);
-#pragma unroll
-      for (int i = 0; i < NCH; i++) {
-        if (kXPrefetch && i + 1 < NCH) {
-#pragma unroll
-          for (int d = 0; d < 4; d++) xn[d] = xread((c0 + i + 1) * 16 + d);
-        }
-        if (!kXPrefetch && i > 0) {
-#pragma unroll
-          for (int d = 0; d < 4; d++) xv[d] = xread((c0 + i) * 16 + d);
-        }
-        const float sf = e8m0_to_float(s[i]);
-        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 0);
-          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 1);
-          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 2);
-          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 3);
-          const bf16x8_t bw = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[d]), bw, acc[d], 0, 0, 0);
-        }
-        if (kXPrefetch && i + 1 < NCH) {
-#pragma unroll
-          for (int d = 0; d < 4; d++) xv[d] = xn[d];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < nb; j++) {
+      const int row0 = block_row0(j);
+      const int row = lane_row(j);
+      const bool row_ok = row < N;
+      const uint4* wrow = wrow_of(j);
+      const bool more = j + 1 < nb;  // uniform
+      const uint4* wnext = wrow_of(min(j + 1, nb - 1));
+      const int nstep = more ? 1 : 0;   // after the last block: placeholder requests
+      const int nfirst = more ? g_first : 0;
+      // the row's bias, loaded unconditionally (from a zero without bias: a
+      // load under a branch ends in a wait for every load in flight) through
+      // an opaque address (so it is not sunk to its use), consumed at the end
+      uint32_t bias_bits;
+      {
+        const uint16_t* bp = bias ? bias + (size_t)e * N + min(row, N - 1) : &kZeroBf16;
+        asm volatile("" : "+v"(bp));
+        bias_bits = *(const __attribute__((address_space(1))) uint16_t*)(bp);
       }
-    };
-    // rounds of NST chunks: every round but the last requests the next round
-    // (unconditionally, so the compiler's wait counts stay exact)
-    const int rounds = NITC / (KS * NST * NCH);
-    for (int rd = 0; rd + 1 < rounds; rd++) {
-      const int c0 = g_first + rd * NST * NCH;
-      compute_chunk(c0, wa);
-      load_chunk(c0 + NST * NCH, wa);
-      compute_chunk(c0 + NCH, wb);
-      load_chunk(c0 + (NST + 1) * NCH, wb);
-      if (NST == 3) {
-        compute_chunk(c0 + 2 * NCH, wc);
-        load_chunk(c0 + 5 * NCH, wc);
+      int sc_base;
+      {
+        int n_sblk;
+        const uint4* s_blocks;
+        sc_span(j, n_sblk, sc_base, s_blocks);
       }
-    }
-    {
-      const int c0 = g_first + (rounds - 1) * NST * NCH;
-      compute_chunk(c0, wa);
-      compute_chunk(c0 + NCH, wb);
-      if (NST == 3) compute_chunk(c0 + 2 * NCH, wc);
-    }
-    f32x4_v tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    if (KS > 1) {  // K parts 1.. hand their sums to part 0 (fixed order: deterministic)
-      if (kpart > 0) red[(rw * (KS - 1) + kpart - 1) * 64 + lane] = tot;
-      lds_barrier();
-      if (kpart == 0) {
-#pragma unroll
-        for (int j = 0; j < KS - 1; j++) tot += red[(rw * (KS - 1) + j) * 64 + lane];
-      }
-    }
+      const int rows_b = min(RW * 16, N - row0);
+      const uint8_t* srow = reinterpret_cast<const uint8_t*>(sc_lds + j * sc_blk) + sc_base +
+                            (size_t)min(row - row0, rows_b - 1) * KB;
 
-    // ---- lane l holds tokens 4 * (l / 16) + i of weight row l % 16
-    if constexpr (SWIGLU) {
-      // rows 2 i (gate) and 2 i + 1 (up) sit in lanes l and l ^ 1 (n_base is
-      // a multiple of 16): swap within lane pairs (every lane takes part),
-      // then the even lane writes activation column row / 2
-      float v[4], p[4];
+      f32x4_v acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        v[i] = tot[i] + bias_v;
-        p[i] = pair_swap(v[i]);
+      for (int d = 0; d < 4; d++) acc[d] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+      // ---- NST chunks of NCH K groups in flight: a chunk is converted and
+      // multiplied while the later ones load (4 MFMAs per 128-bit load into four
+      // independent accumulators; A = token rows, lane l: row l % 16; B = weights)
+      // At 3 waves per SIMD the next group's token rows are not prefetched from
+      // LDS (the registers are needed for the weights in flight; the other waves
+      // cover the LDS latency).
+      constexpr bool kXPrefetch = OCC < 3;
+      auto compute_chunk = [&](int c0, const uint4 (&w)[NCH]) {
+        uint32_t sv[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; i++) sv[i] = srow[min((c0 + i) * 4 + kq, KB - 1)];
+        uint4 xv[4], xn[4];
+#pragma unroll
+        for (int d = 0; d < 4; d++) xv[d] = xread(c0 * 16 + d);
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+          if (kXPrefetch && i + 1 < NCH) {
+#pragma unroll
+            for (int d = 0; d < 4; d++) xn[d] = xread((c0 + i + 1) * 16 + d);
+          }
+          if (!kXPrefetch && i > 0) {
+#pragma unroll
+            for (int d = 0; d < 4; d++) xv[d] = xread((c0 + i) * 16 + d);
+          }
+          const float sf = e8m0_to_float(sv[i]);
+          const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+          for (int d = 0; d < 4; d++) {
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 0);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 1);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 2);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 3);
+            const bf16x8_t bw = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[d]), bw, acc[d], 0, 0, 0);
+          }
+          if (kXPrefetch && i + 1 < NCH) {
+#pragma unroll
+            for (int d = 0; d < 4; d++) xv[d] = xn[d];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // rounds of NST chunks: every round but the last requests the next round,
+      // the last one the first round of the next block (the requests are
+      // unconditional, so the compiler's wait counts stay exact: after the last
+      // block they re-read its first chunks, which its own loads just brought in)
+      const int rounds = NITC / (KS * NST * NCH);
+      for (int rd = 0; rd + 1 < rounds; rd++) {
+        const int c0 = g_first + rd * NST * NCH;
+        compute_chunk(c0, wa);
+        load_chunk(wrow, c0 + NST * NCH, wa);
+        compute_chunk(c0 + NCH, wb);
+        load_chunk(wrow, c0 + (NST + 1) * NCH, wb);
+        if (NST == 3) {
+          compute_chunk(c0 + 2 * NCH, wc);
+          load_chunk(wrow, c0 + 5 * NCH, wc);
+        }
       }
-      if (row_ok && kpart == 0 && (row & 1) == 0) {
-        const int NA = N >> 1;
+      {
+        const int c0 = g_first + (rounds - 1) * NST * NCH;
+        compute_chunk(c0, wa);
+        load_chunk(wnext, nfirst, wa, nstep);
+        compute_chunk(c0 + NCH, wb);
+        load_chunk(wnext, nfirst + NCH * nstep, wb, nstep);
+        if (NST == 3) {
+          compute_chunk(c0 + 2 * NCH, wc);
+          load_chunk(wnext, nfirst + 2 * NCH * nstep, wc, nstep);
+        }
+      }
+      asm volatile("" : "+v"(bias_bits));
+      const float bias_v = row_ok ? bf16_bits_to_f32(bias_bits) : 0.f;
+      f32x4_v tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      if (KS > 1) {  // K parts 1.. hand their sums to part 0 (fixed order: deterministic)
+        if (kpart > 0) red[(rw * (KS - 1) + kpart - 1) * 64 + lane] = tot;
+        lds_barrier();
+        if (kpart == 0) {
+#pragma unroll
+          for (int q = 0; q < KS - 1; q++) tot += red[(rw * (KS - 1) + q) * 64 + lane];
+        }
+        lds_barrier();  // the partial sums are read before the next block writes them
+      }
+
+      // ---- lane l holds tokens 4 * (l / 16) + i of weight row l % 16
+      if constexpr (SWIGLU) {
+        // rows 2 i (gate) and 2 i + 1 (up) sit in lanes l and l ^ 1 (row0 is a
+        // multiple of 16): swap within lane pairs (every lane takes part),
+        // then the even lane writes activation column row / 2
+        float v[4], pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          v[i] = tot[i] + bias_v;
+          pv[i] = pair_swap(v[i]);
+        }
+        if (row_ok && kpart == 0 && (row & 1) == 0) {
+          const int NA = N >> 1;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int m = 4 * kq + i;
+            if (m < mc) {
+              const int r = rows_lds[m];
+              if (r >= 0) act[(size_t)r * NA + (row >> 1)] = (uint16_t)f32_to_bf16_bits(swiglu(v[i], pv[i]));
+            }
+          }
+        }
+      } else if (row_ok && kpart == 0) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int m = 4 * kq + i;
           if (m < mc) {
             const int r = rows_lds[m];
-            if (r >= 0) act[(size_t)r * NA + (row >> 1)] = (uint16_t)f32_to_bf16_bits(swiglu(v[i], p[i]));
+            if (r >= 0) out[(size_t)r * N + row] = tot[i] + bias_v;
           }
-        }
-      }
-    } else if (row_ok && kpart == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = 4 * kq + i;
-        if (m < mc) {
-          const int r = rows_lds[m];
-          if (r >= 0) out[(size_t)r * N + row] = tot[i] + bias_v;
         }
       }
     }
@@ -381,9 +437,6 @@ struct FusedRoute {
   int32_t* sorted_rows;
   int32_t* error_word;
 };
-
-// the bias of a projection without one
-__device__ const uint16_t kZeroBf16 = 0;
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -599,22 +652,41 @@ constexpr int kT1Rows = T1Shape<kT1Quads, kT1Waves>::kRows;
 // largest dynamic LDS a launch may use (the rest of the 160 KB holds rows_lds)
 constexpr int kGemvMaxDynLds = 160 * 1024 - 1024;
 
-// Dynamic LDS of one workgroup: the MT staged token rows, then the
-// weight-scale rows of its 16 * WAVES weight rows (+2 blocks of alignment slack).
-size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K) {
+// LDS of one workgroup, in 16-byte entries: the MT staged token rows, and the
+// weight-scale rows of one row block of 16 * WAVES / KS weight rows (+2
+// blocks of alignment slack, in whole 64-entry DMAs).
+size_t gemv_xs_entries(int MT, int NCH, int NST, int KS, int K) {
   const int nit = (K / 32 + 3) / 4;
   const int r = KS * NST * NCH;
-  const size_t xs = (size_t)MT * (((nit + r - 1) / r * r * 16 + 63) / 64 * 64 + 1) * 16;
+  return (size_t)MT * (((nit + r - 1) / r * r * 16 + 63) / 64 * 64 + 1);
+}
+size_t gemv_sc_entries(int WAVES, int KS, int K) {
   const size_t blocks = ((size_t)(WAVES / KS) * 16 * (K / 32) + 15) / 16 + 2;
-  const size_t sc = (blocks + 63) / 64 * 64 * 16;
-  return xs + sc;
+  return (blocks + 63) / 64 * 64;
+}
+size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K, int nbpw) {
+  return (gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)nbpw * gemv_sc_entries(WAVES, KS, K)) * 16;
 }
 
 template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU>
 hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                              const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                              const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream) {
-  const size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K);
+  // Row blocks per workgroup: enough workgroups for one wave of them over the
+  // 256 CUs (as many per CU as the waves allow), each streaming its share of
+  // an expert's row blocks with the token rows staged once, within the LDS.
+  const int R = T * k;
+  const int groups = R < E ? R : E;
+  constexpr int RW = WAVES / KS;
+  const int nblk = (N + RW * 16 - 1) / (RW * 16);
+  const size_t xs = gemv_xs_entries(MT, NCH, NST, KS, K), sc = gemv_sc_entries(WAVES, KS, K);
+  const int nbpw_max = (int)((kGemvMaxDynLds / 16 - xs) / sc);  // >= 1: checked by the caller
+  constexpr int kPerCu = (OCC * 4) / WAVES > 0 ? (OCC * 4) / WAVES : 1;
+  int G = (256 * kPerCu + groups - 1) / groups;
+  G = G < (nblk + nbpw_max - 1) / nbpw_max ? (nblk + nbpw_max - 1) / nbpw_max : G;
+  G = G > nblk ? nblk : G;
+  const int nbpw = (nblk + G - 1) / G;
+  const size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K, nbpw);
   static bool attr_set = false;  // raise the dynamic LDS limit (to what any K may need) once
   if (!attr_set && lds > 65536) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>),
@@ -622,12 +694,9 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  const int R = T * k;
-  const int groups = R < E ? R : E;
-  const int rows_per_block = WAVES / KS * 16;
-  const dim3 grid((N + rows_per_block - 1) / rows_per_block, groups);
+  const dim3 grid(G, groups);
   hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>), grid, dim3(WAVES * 64), lds, stream, blocks,
-                     scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act);
+                     scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act, (int)sc);
   return hipGetLastError();
 }
 
@@ -689,7 +758,7 @@ hipError_t launch_gemv_any(const uint8_t* blocks, const uint8_t* scales, const u
 size_t gemv_lds_bytes(int T, int K) {
   if (T == 1 && K / 32 <= kT1MaxKB) return 0;  // static LDS only
   const GemvShape g = gemv_shape(T, K);
-  return gemv_lds_for(g.mt, g.waves, g.nch, g.nst, g.ks, K);
+  return gemv_lds_for(g.mt, g.waves, g.nch, g.nst, g.ks, K, 1);
 }
 
 hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,

@@ -60,49 +60,47 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Route token t with the calling wave; returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
-template <int EC>
-__device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int t, int E,
-                           int k, int lane, int32_t* __restrict__ topk_ids, float* __restrict__ gates,
-                           int32_t* ids_copy) {
+// Token t with given expert ids: lane s < k holds the id e of slot s and, for
+// the gates, the logit at e (lg).  Checks range and repeats, writes the ids
+// (a repeat flagged in bit 30 for the grouping) and the softmax over the k
+// logits.  Returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
+__device__ int route_given(int e, float lg, int t, int E, int k, int lane, int32_t* __restrict__ topk_ids,
+                           float* __restrict__ gates, bool with_gates, int32_t* ids_copy) {
   int32_t* ids = topk_ids + (size_t)t * k;
   int32_t* idc = ids_copy ? ids_copy + t * k : nullptr;  // the grouping's copy (LDS), if any
-  const uint16_t* lrow = logits ? logits + (size_t)t * E : nullptr;
-  if (ids_in) {
-    // lane s < k holds the given id of slot s
-    const int32_t* given = ids_in + (size_t)t * k;
-    const int e = lane < k ? given[lane] : -1;
-    const bool in_range = lane < k && (unsigned)e < (unsigned)E;
-    bool dup = false;
-    for (int j = 0; j < k; j++) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      dup |= (lane < k && j != lane && ej == e && in_range);
-    }
-    const uint64_t bad = __ballot(lane < k && !in_range);
-    const uint64_t dups = __ballot(dup);
-    const int idv = in_range ? (e | (dup ? kDupFlag : 0)) : -1;
-    if (lane < k) {
-      ids[lane] = idv;
-      if (idc) idc[lane] = idv;
-    }
-    if (gates && lrow && bad == 0) {
-      const float l = lane < k ? bf16_bits_to_f32(lrow[in_range ? e : 0]) : -INFINITY;
-      const float mx = wave_max(l);
-      const float num = lane < k ? expf(l - mx) : 0.f;
-      const float sum = wave_sum(num);
-      if (lane < k) gates[(size_t)t * k + lane] = num / sum;
-    }
-    return (bad ? MXFP4_ROUTE_ERR_ID_RANGE : 0) | (dups ? MXFP4_ROUTE_ERR_ID_DUP : 0);
+  const bool in_range = lane < k && (unsigned)e < (unsigned)E;
+  bool dup = false;
+  for (int j = 0; j < k; j++) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    dup |= (lane < k && j != lane && ej == e && in_range);
   }
-  float l[EC];
+  const uint64_t bad = __ballot(lane < k && !in_range);
+  const uint64_t dups = __ballot(dup);
+  const int idv = in_range ? (e | (dup ? kDupFlag : 0)) : -1;
+  if (lane < k) {
+    ids[lane] = idv;
+    if (idc) idc[lane] = idv;
+  }
+  if (with_gates && bad == 0) {
+    const float l = lane < k ? lg : -INFINITY;
+    const float mx = wave_max(l);
+    const float num = lane < k ? expf(l - mx) : 0.f;
+    const float sum = wave_sum(num);
+    if (lane < k) gates[(size_t)t * k + lane] = num / sum;
+  }
+  return (bad ? MXFP4_ROUTE_ERR_ID_RANGE : 0) | (dups ? MXFP4_ROUTE_ERR_ID_DUP : 0);
+}
+
+// Token t routed from its logits l (lane e + 64 i holds expert e + 64 i's
+// logit, -inf past E); returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
+template <int EC>
+__device__ int route_ranked(const float (&l)[EC], int t, int E, int k, int lane, int32_t* __restrict__ topk_ids,
+                            float* __restrict__ gates, int32_t* ids_copy) {
+  int32_t* ids = topk_ids + (size_t)t * k;
+  int32_t* idc = ids_copy ? ids_copy + t * k : nullptr;
   int rank[EC];
 #pragma unroll
-  for (int i = 0; i < EC; i++) {
-    const int e = lane + 64 * i;
-    l[i] = bf16_bits_to_f32(lrow[min(e, E - 1)]);  // unconditional load: no branch per load
-    if (e >= E) l[i] = -INFINITY;
-    rank[i] = 0;
-  }
+  for (int i = 0; i < EC; i++) rank[i] = 0;
   // rank[e] = #{j : l_j > l_e or (l_j == l_e and j < e)}
 #pragma unroll
   for (int jc = 0; jc < EC; jc++) {
@@ -153,6 +151,59 @@ __device__ int route_token(const uint16_t* __restrict__ logits, const int32_t* _
   for (int i = 0; i < EC; i++) seen += __popcll(__ballot(lane + 64 * i < E && rank[i] < k));
   return seen == k ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
 }
+
+// Route the NB tokens t0 + stride * b (b < NB; those past T are skipped) with
+// the calling wave.  Every load of the batch is issued before any token is
+// ranked (tokens past T re-read token T - 1), so the batch pays one memory
+// round trip (two with given ids and gates: the ids, then their logits).
+template <int EC, int NB>
+__device__ int route_tokens(const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int t0,
+                            int stride, int T, int E, int k, int lane, int32_t* __restrict__ topk_ids,
+                            float* __restrict__ gates, int32_t* ids_copy) {
+  int err = 0;
+  if (ids_in) {
+    int e[NB];
+    float lg[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      const int tc = min(t0 + stride * b, T - 1);
+      e[b] = ids_in[(size_t)tc * k + min(lane, k - 1)];
+      if (lane >= k) e[b] = -1;
+    }
+    const bool with_gates = gates && logits;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      const int tc = min(t0 + stride * b, T - 1);
+      lg[b] = with_gates ? bf16_bits_to_f32(logits[(size_t)tc * E + ((unsigned)e[b] < (unsigned)E ? e[b] : 0)]) : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      const int t = t0 + stride * b;
+      if (t < T) err |= route_given(e[b], lg[b], t, E, k, lane, topk_ids, gates, with_gates, ids_copy);
+    }
+    return err;
+  }
+  float l[NB][EC];
+#pragma unroll
+  for (int b = 0; b < NB; b++) {
+    const uint16_t* lrow = logits + (size_t)min(t0 + stride * b, T - 1) * E;
+#pragma unroll
+    for (int i = 0; i < EC; i++) {
+      const int e = lane + 64 * i;
+      l[b][i] = bf16_bits_to_f32(lrow[min(e, E - 1)]);  // unconditional load: no branch per load
+      if (e >= E) l[b][i] = -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; b++) {
+    const int t = t0 + stride * b;
+    if (t < T) err |= route_ranked<EC>(l[b], t, E, k, lane, topk_ids, gates, ids_copy);
+  }
+  return err;
+}
+
+// tokens a wave routes per batch
+constexpr int kRouteBatch = 4;
 
 // Grouping of the R = T * k rows by the single workgroup that calls it.
 // ids_src: where the ids are read (an LDS copy of topk_ids, or topk_ids
@@ -292,8 +343,8 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_tiny_kernel(
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
   int errbits = 0;
-  for (int t = wave; t < T; t += nwaves)
-    errbits |= route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates, ids_lds);
+  for (int t0 = wave; t0 < T; t0 += kRouteBatch * nwaves)
+    errbits |= route_tokens<EC, kRouteBatch>(logits, ids_in, t0, nwaves, T, E, k, lane, topk_ids, gates, ids_lds);
   if (lane == 0) err_lds[wave] = errbits;
   __syncthreads();
   if (wave != 0) return;
@@ -345,8 +396,9 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_small_kernel(
   for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) cnt[i] = 0;
   if (tid == 0) err_sh = 0;
   int errbits = 0;
-  for (int t = wave; t < T; t += kGroupWaves)
-    errbits |= route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates, ids_lds);
+  for (int t0 = wave; t0 < T; t0 += kRouteBatch * kGroupWaves)
+    errbits |= route_tokens<EC, kRouteBatch>(logits, ids_in, t0, kGroupWaves, T, E, k, lane, topk_ids, gates,
+                                             ids_lds);
   __syncthreads();  // the routed ids of every token visible to the whole workgroup
   errbits |= group_rows(topk_ids, ids_lds, T * k, E, offsets, sorted_rows, cnt, start, &total_sh);
   if (errbits) atomicOr(&err_sh, errbits);
@@ -362,10 +414,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const uint16_t* __
                                                              float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
   const int w = (blockIdx.x * kRouteThreads + threadIdx.x) >> 6;
-  for (int i = 0; i < kTokensPerRouteWave; i++) {
-    const int t = w * kTokensPerRouteWave + i;
-    if (t < T) route_token<EC>(logits, ids_in, t, E, k, lane, topk_ids, gates, nullptr);
-  }
+  route_tokens<EC, kTokensPerRouteWave>(logits, ids_in, w * kTokensPerRouteWave, 1, T, E, k, lane, topk_ids, gates,
+                                        nullptr);
 }
 
 // T > kSmallT, second launch: grouping (range errors show as -1 ids, repeats as flagged ids).
