@@ -15,22 +15,22 @@
 // above is evaluated directly and in parallel.  The lane whose rank is s
 // writes slot s; the gates come from a wave max and a wave sum.
 //
-// Grouping, in one workgroup of 16 waves: each wave owns a contiguous range of
-// rows and loads its ids up front; per 64-row tile a ballot per id bit gives
-// each lane the mask of lanes sharing its expert; the tile's lowest such lane
-// adds the count into the wave's LDS counter of that expert.  An exclusive scan
-// over experts, plus the counts of earlier waves, turns the counters into
-// bases; a second walk scatters row r to base + (peers below it).  Waves own
-// row ranges in order and lanes are ranked by index, so each expert's rows
-// come out in ascending order.
+// Grouping (more than 64 rows): workgroup c of 16 waves places the rows of
+// its 1024-row chunk.  Every workgroup reads all ids; per 64-row tile a ballot
+// per id bit gives each lane the mask of lanes sharing its expert, and the
+// lowest such lane adds the count into its wave's LDS counters (all rows,
+// rows before the chunk, the wave's own chunk tile).  An exclusive scan over
+// experts gives the offsets; the counts before the chunk and of the chunk's
+// lower waves give each wave's bases; row r goes to base + (peers below it).
+// Tiles are ranked by index and lanes within a tile too, so each expert's
+// rows come out in ascending order.
 //
-// Tiny batches (T * k <= 64) group in a single wave without LDS counters.
-// Small batches (T <= 256) run both parts in one single-workgroup kernel,
-// which keeps a copy of the routed ids in LDS for the grouping.
-// Larger batches route with many workgroups and then group in a second,
-// single-workgroup launch.  A row whose given id is out of range is written
-// as -1 and left out of the grouping; a repeated given id is flagged to the
-// grouping pass in bit 30 of the id (cleared again there).
+// Tiny batches (T * k <= 64) route and group in a single workgroup, the
+// grouping in one wave without LDS counters.  Larger batches route with many
+// workgroups (a token per wave) and then group with ceil(T * k / 1024)
+// workgroups.  A row whose given id is out of range is written as -1 and left
+// out of the grouping; a repeated given id is flagged to the grouping pass in
+// bit 30 of the id (cleared again there).
 
 #include "kernels.h"
 #include "common.h"
@@ -44,7 +44,6 @@ constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kTilesPerLoad = 16;       // 64-row tiles whose ids a wave loads at once
 constexpr int kExpertChunks = 8;        // 64 experts per lane chunk: E <= 512
-constexpr int kSmallT = 256;            // single-kernel path up to this many tokens
 constexpr int kRouteThreads = 256;      // multi-workgroup routing: 4 waves, 4 tokens per wave
 constexpr int kTokensPerRouteWave = 4;
 constexpr int32_t kDupFlag = 1 << 30;
@@ -205,126 +204,137 @@ __device__ int route_tokens(const uint16_t* __restrict__ logits, const int32_t* 
 // tokens a wave routes per batch
 constexpr int kRouteBatch = 4;
 
-// Grouping of the R = T * k rows by the single workgroup that calls it.
-// ids_src: where the ids are read (an LDS copy of topk_ids, or topk_ids
-// itself); cnt: LDS [kGroupWaves][E] zeroed; start: LDS [E].  Returns the
-// error bits found in the ids (range: negative ids; dup: flagged ids, whose
-// flag is cleared in topk_ids and in ids_src).
-__device__ int group_rows(int32_t* __restrict__ topk_ids, int32_t* ids_src, int R, int E,
-                          int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows, int* cnt, int* start,
-                          int* total_sh) {
+// Grouping of the R = T * k routed rows by G workgroups of 16 waves.
+// Workgroup c places the rows of its chunk [c * kChunk, (c + 1) * kChunk)
+// (wave w: the chunk's 64-row tile w).  Every workgroup reads all R ids
+// (wave w: tiles w, w + 16, ...): the per-expert totals give the offsets (the
+// exclusive scan), the counts in tiles before the chunk and in the chunk's
+// tiles of lower waves give each expert's base for this wave's rows; a lane's
+// place is then that base plus the lanes below it with the same id (one
+// ballot per id bit).  Rows are placed in ascending order within an expert,
+// so the result is the stable counting sort.  Workgroup 0 writes the offsets
+// and the error word; a chunk's owner clears the repeat flags of its rows.
+constexpr int kChunk = kGroupThreads;
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restrict__ topk_ids, int R, int E,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_rows,
+                                                              int32_t* __restrict__ error_word) {
+  extern __shared__ int lds[];
+  int* cnt_all = lds;                          // [waves][E]: rows per expert (all tiles of the wave)
+  int* cnt_pre = cnt_all + kGroupWaves * E;    // [waves][E]: rows per expert in tiles before the chunk
+  int* cnt_own = cnt_pre + kGroupWaves * E;    // [waves][E]: rows per expert in the wave's chunk tile
+  int* base = cnt_own + kGroupWaves * E;       // [E]
+  __shared__ int err_sh;
+  __shared__ int total_sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  for (int i = tid; i < 3 * kGroupWaves * E; i += kGroupThreads) lds[i] = 0;
+  if (tid == 0) err_sh = 0;
+  __syncthreads();
   int ebits = 1;
   while ((1 << ebits) < E) ebits++;
-  const int per_wave = (R + kGroupWaves * 64 - 1) / (kGroupWaves * 64) * 64;
-  const int w_begin = min(R, wave * per_wave);
-  const int w_end = min(R, w_begin + per_wave);
+  const int tiles = (R + 63) >> 6;
+  const int own_tile = (int)blockIdx.x * kGroupWaves + wave;  // this wave's chunk tile
   int errbits = 0;
 
-  // ---- count (and clean the repeat flags)
-  for (int base = w_begin; base < w_end; base += 64 * kTilesPerLoad) {
+  // one row per lane of tile t: its id with the repeat flag cleared (-1 past R or out of range)
+  auto peers_of = [&](int e) {
+    const bool valid = e >= 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < ebits; b++) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    return peers;
+  };
+
+  // ---- counts over every tile (waves take tiles w, w + 16, ...)
+  for (int t0 = wave; t0 < tiles; t0 += kGroupWaves * kTilesPerLoad) {
     int ev[kTilesPerLoad];
 #pragma unroll
     for (int i = 0; i < kTilesPerLoad; i++) {
-      const int r = base + 64 * i + lane;
-      ev[i] = ids_src[min(r, w_end - 1)];  // unconditional load, masked below
-      if (r >= w_end) ev[i] = -1;
+      const int r = (t0 + i * kGroupWaves) * 64 + lane;
+      ev[i] = topk_ids[min(r, R - 1)];  // unconditional load, masked below
+      if (r >= R) ev[i] = -1;
     }
 #pragma unroll
     for (int i = 0; i < kTilesPerLoad; i++) {
-      if (base + 64 * i >= w_end) continue;  // wave-uniform
-      const int r = base + 64 * i + lane;
-      if (r < w_end) {
-        if (ev[i] < 0) errbits |= MXFP4_ROUTE_ERR_ID_RANGE;
-        if (ev[i] >= 0 && (ev[i] & kDupFlag)) {
+      const int t = t0 + i * kGroupWaves;
+      if (t >= tiles) break;  // wave-uniform
+      const int r = t * 64 + lane;
+      int e = ev[i];
+      if (r < R) {
+        if (e < 0) errbits |= MXFP4_ROUTE_ERR_ID_RANGE;
+        if (e >= 0 && (e & kDupFlag)) {
           errbits |= MXFP4_ROUTE_ERR_ID_DUP;
-          ev[i] &= ~kDupFlag;
-          topk_ids[r] = ev[i];
-          ids_src[r] = ev[i];
+          e &= ~kDupFlag;
+          if (t == own_tile) topk_ids[r] = e;  // the chunk's owner clears the flag
         }
       }
-      const int e = ev[i];
-      const bool valid = e >= 0;
-      uint64_t peers = __ballot(valid);
-      for (int b = 0; b < ebits; b++) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
+      const uint64_t peers = peers_of(e);
+      if (e >= 0 && lanes_below(peers) == 0) {
+        const int n = __popcll(peers);
+        cnt_all[wave * E + e] += n;
+        if (t < (int)blockIdx.x * kGroupWaves) cnt_pre[wave * E + e] += n;
+        if (t == own_tile) cnt_own[wave * E + e] += n;
       }
-      if (valid && lanes_below(peers) == 0) cnt[wave * E + e] += __popcll(peers);
     }
   }
+  if (errbits) atomicOr(&err_sh, errbits);
   __syncthreads();
 
-  // ---- expert starts and per-wave running bases
+  // ---- offsets (exclusive scan of the totals) and this chunk's bases
   if (wave == 0) {
     int carry = 0;
     for (int c0 = 0; c0 < E; c0 += 64) {
       const int e = c0 + lane;
-      int tot = 0;
+      int tot = 0, pre = 0;
       if (e < E)
-        for (int w = 0; w < kGroupWaves; w++) tot += cnt[w * E + e];
+        for (int w = 0; w < kGroupWaves; w++) {
+          tot += cnt_all[w * E + e];
+          pre += cnt_pre[w * E + e];
+        }
       int inc = tot;
       for (int d = 1; d < 64; d <<= 1) {
         const int o = __shfl_up(inc, d, 64);
         if (lane >= d) inc += o;
       }
-      if (e < E) start[e] = carry + inc - tot;
+      if (e < E) {
+        const int start = carry + inc - tot;
+        base[e] = start + pre;
+        if (blockIdx.x == 0) offsets[e] = start;
+      }
       carry += __shfl(inc, 63, 64);
     }
-    if (lane == 0) *total_sh = carry;
+    if (lane == 0) total_sh = carry;
   }
   __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) {
+    offsets[E] = total_sh;
+    if (error_word) *error_word = err_sh;
+  }
+  // per wave: the base of its chunk tile's rows of expert e (the chunk's lower waves first)
   for (int e = tid; e < E; e += kGroupThreads) {
-    int b = start[e];
-    offsets[e] = b;
+    int b = base[e];
     for (int w = 0; w < kGroupWaves; w++) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = b;
+      const int c = cnt_own[w * E + e];
+      cnt_own[w * E + e] = b;
       b += c;
     }
   }
-  if (tid == 0) offsets[E] = *total_sh;
   __syncthreads();
 
-  // ---- stable scatter
-  for (int base = w_begin; base < w_end; base += 64 * kTilesPerLoad) {
-    int ev[kTilesPerLoad];
-#pragma unroll
-    for (int i = 0; i < kTilesPerLoad; i++) {
-      const int r = base + 64 * i + lane;
-      ev[i] = ids_src[min(r, w_end - 1)];
-      if (r >= w_end) ev[i] = -1;
-    }
-#pragma unroll
-    for (int i = 0; i < kTilesPerLoad; i++) {
-      if (base + 64 * i >= w_end) continue;  // wave-uniform
-      const int r = base + 64 * i + lane;
-      const int e = ev[i];
-      const bool valid = e >= 0;
-      uint64_t peers = __ballot(valid);
-      for (int b = 0; b < ebits; b++) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
-      }
-      const int below = lanes_below(peers);
-      int pos = 0;
-      if (valid) pos = cnt[wave * E + e] + below;
-      // every lane's read of its counter precedes the lowest peer's update (LDS
-      // instructions of a wave run in order; wait for the reads themselves only)
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
-      if (valid) {
-        sorted_rows[pos] = r;
-        if (below == 0) cnt[wave * E + e] = pos + __popcll(peers);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
+  // ---- stable scatter of this wave's chunk tile
+  if (own_tile < tiles) {
+    const int r = own_tile * 64 + lane;
+    int e = r < R ? topk_ids[r] : -1;  // flag cleared above by this wave (program order)
+    if (e >= 0) e &= ~kDupFlag;
+    const uint64_t peers = peers_of(e);
+    if (e >= 0) sorted_rows[cnt_own[wave * E + e] + lanes_below(peers)] = r;
   }
-  return errbits;
 }
 
 // T * k <= 64: up to 16 waves route a token each, then one wave groups the
@@ -378,96 +388,49 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_tiny_kernel(
   if (lane == 0 && error_word) *error_word = err;
 }
 
-// T <= kSmallT: routing and grouping in one workgroup.
-template <int EC>
-__global__ __launch_bounds__(kGroupThreads) void route_group_small_kernel(
-    const uint16_t* __restrict__ logits, const int32_t* __restrict__ ids_in, int T, int E, int k,
-    int32_t* __restrict__ topk_ids, float* __restrict__ gates, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ error_word) {
-  extern __shared__ int lds[];
-  int* cnt = lds;
-  int* start = lds + kGroupWaves * E;
-  int* ids_lds = start + E;  // [T * k]: the routed ids, read back by the grouping
-  __shared__ int err_sh;
-  __shared__ int total_sh;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) cnt[i] = 0;
-  if (tid == 0) err_sh = 0;
-  int errbits = 0;
-  for (int t0 = wave; t0 < T; t0 += kRouteBatch * kGroupWaves)
-    errbits |= route_tokens<EC, kRouteBatch>(logits, ids_in, t0, kGroupWaves, T, E, k, lane, topk_ids, gates,
-                                             ids_lds);
-  __syncthreads();  // the routed ids of every token visible to the whole workgroup
-  errbits |= group_rows(topk_ids, ids_lds, T * k, E, offsets, sorted_rows, cnt, start, &total_sh);
-  if (errbits) atomicOr(&err_sh, errbits);
-  __syncthreads();
-  if (tid == 0 && error_word) *error_word = err_sh;
-}
-
-// T > kSmallT, first launch: routing, one wave per token, many workgroups.
-template <int EC>
+// R > 64, first launch: routing, NB tokens per wave, many workgroups.
+template <int EC, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const uint16_t* __restrict__ logits,
                                                              const int32_t* __restrict__ ids_in, int T, int E,
                                                              int k, int32_t* __restrict__ topk_ids,
                                                              float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
   const int w = (blockIdx.x * kRouteThreads + threadIdx.x) >> 6;
-  route_tokens<EC, kTokensPerRouteWave>(logits, ids_in, w * kTokensPerRouteWave, 1, T, E, k, lane, topk_ids, gates,
-                                        nullptr);
-}
-
-// T > kSmallT, second launch: grouping (range errors show as -1 ids, repeats as flagged ids).
-__global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restrict__ topk_ids, int R, int E,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ sorted_rows,
-                                                              int32_t* __restrict__ error_word) {
-  extern __shared__ int lds[];
-  int* cnt = lds;
-  int* start = lds + kGroupWaves * E;
-  __shared__ int err_sh;
-  __shared__ int total_sh;
-  for (int i = threadIdx.x; i < kGroupWaves * E; i += kGroupThreads) cnt[i] = 0;
-  if (threadIdx.x == 0) err_sh = 0;
-  __syncthreads();
-  const int errbits = group_rows(topk_ids, topk_ids, R, E, offsets, sorted_rows, cnt, start, &total_sh);
-  if (errbits) atomicOr(&err_sh, errbits);
-  __syncthreads();
-  if (threadIdx.x == 0 && error_word) *error_word = err_sh;
+  route_tokens<EC, NB>(logits, ids_in, w * NB, 1, T, E, k, lane, topk_ids, gates, nullptr);
 }
 
 template <int EC>
 hipError_t launch_ec(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k, int32_t* topk_ids,
                      float* gates, int32_t* offsets, int32_t* sorted_rows, int32_t* error_word, hipStream_t stream) {
-  const size_t lds_bytes = (size_t)(kGroupWaves + 1) * E * sizeof(int);
   if ((long long)T * k <= 64) {
     const int waves = T < 1 ? 1 : (T < kGroupWaves ? T : kGroupWaves);  // T = 0 still writes the zero offsets
     hipLaunchKernelGGL(route_group_tiny_kernel<EC>, dim3(1), dim3(64 * waves), 0, stream, logits, ids_in, T, E, k,
                        topk_ids, gates, offsets, sorted_rows, error_word);
     return hipGetLastError();
   }
-  if (T <= kSmallT) {
-    const size_t small_lds = lds_bytes + (size_t)T * k * sizeof(int);
-    static bool attr_set = false;  // up to (16 + 1) * 512 + 256 * 32 ints: raise the dynamic LDS limit once
-    if (!attr_set && small_lds > 65536) {
-      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_group_small_kernel<EC>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)((kGroupWaves + 1) * kMaxRouteE + kSmallT * kMaxRouteK) * 4);
-      if (err != hipSuccess) return err;
-      attr_set = true;
-    }
-    hipLaunchKernelGGL(route_group_small_kernel<EC>, dim3(1), dim3(kGroupThreads), small_lds, stream, logits, ids_in,
-                       T, E, k, topk_ids, gates, offsets, sorted_rows, error_word);
-    return hipGetLastError();
-  }
-  const int tokens_per_block = (kRouteThreads / 64) * kTokensPerRouteWave;
-  hipLaunchKernelGGL(route_kernel<EC>, dim3((T + tokens_per_block - 1) / tokens_per_block), dim3(kRouteThreads), 0,
-                     stream, logits, ids_in, T, E, k, topk_ids, gates);
+  // one token per wave while that fills the chip, four beyond
+  const bool one = T <= 16384;
+  const int per_block = (kRouteThreads / 64) * (one ? 1 : kTokensPerRouteWave);
+  const dim3 rgrid((T + per_block - 1) / per_block);
+  if (one)
+    hipLaunchKernelGGL((route_kernel<EC, 1>), rgrid, dim3(kRouteThreads), 0, stream, logits, ids_in, T, E, k, topk_ids,
+                       gates);
+  else
+    hipLaunchKernelGGL((route_kernel<EC, kTokensPerRouteWave>), rgrid, dim3(kRouteThreads), 0, stream, logits,
+                       ids_in, T, E, k, topk_ids, gates);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds_bytes, stream, topk_ids, T * k, E, offsets,
-                     sorted_rows, error_word);
+  const size_t glds = ((size_t)3 * kGroupWaves * E + E) * sizeof(int);
+  static bool attr_set = false;  // up to 3 * 16 * 512 + 512 ints: raise the dynamic LDS limit once
+  if (!attr_set && glds > 65536) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)((3 * kGroupWaves + 1) * kMaxRouteE * sizeof(int)));
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  const long long R = (long long)T * k;
+  hipLaunchKernelGGL(group_kernel, dim3((unsigned)((R + kChunk - 1) / kChunk)), dim3(kGroupThreads), glds, stream,
+                     topk_ids, (int)R, E, offsets, sorted_rows, error_word);
   return hipGetLastError();
 }
 

@@ -106,11 +106,10 @@ def test_paths_agree_closely():
 
 
 # ----------------------------------------------------------------- routing paths
-# one-wave grouping (T * k <= 64), single-workgroup routing + grouping
-# (T <= 256), multi-workgroup routing then grouping (T > 256); 1, 2 and 8
-# lane chunks of experts
+# one-wave grouping (T * k <= 64), else multi-workgroup routing then grouping
+# by one or more 1024-row chunks; 1, 2 and 8 lane chunks of experts
 ROUTE_CASES = [(16, 4, 32), (13, 5, 32), (64, 1, 100), (65, 1, 100), (256, 4, 32), (257, 4, 32),
-               (40, 7, 300), (300, 3, 300), (1, 32, 512)]
+               (40, 7, 300), (300, 3, 300), (1, 32, 512), (1024, 1, 8), (700, 3, 300), (2000, 4, 32)]
 
 
 @pytest.mark.parametrize("route", ["logits", "ids+logits"])
@@ -155,6 +154,32 @@ def test_given_ids_errors_are_flagged():
     vals, mags = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, False, np.where(g["ids"] < 0, 0, g["ids"]),
                                        np.repeat(valid_rows, 64), np.tile(np.arange(64), len(valid_rows)))
     check_close(g["out"].reshape(8, 64)[valid_rows].reshape(-1), vals, mags, "valid rows")
+
+
+def test_given_ids_errors_flagged_multiworkgroup():
+    """The same with more than 64 rows and 2 chunks (the multi-workgroup grouping)."""
+    _announce("bad given ids, multi-workgroup grouping")
+    T, k, E = 600, 2, 8
+    p = S.make_custom(E=E, N=64, K=64, T=T, k=k, route="ids+logits")
+    ids = np.stack([np.arange(T) % E, (np.arange(T) + 3) % E], axis=1).astype(np.int32)
+    ids[5] = [2, 2]        # repeat
+    ids[550] = [9, 1]      # out of range
+    ids[599] = [7, 7]      # repeat in the second chunk
+    p.ids_in = ids
+    dp = DeviceProblem(p, path=1)
+    dp.run()
+    g = dp.results()
+    assert g["error_word"] == (B.MXFP4_ROUTE_ERR_ID_RANGE | B.MXFP4_ROUTE_ERR_ID_DUP)
+    want = ids.copy()
+    want[550, 0] = -1
+    np.testing.assert_array_equal(g["ids"], want)
+    flat = want.reshape(-1)
+    valid = np.nonzero(flat >= 0)[0]
+    assert g["offsets"][-1] == valid.size
+    # the stable order among valid rows: by expert, then by row
+    order = valid[np.argsort(flat[valid], kind="stable")]
+    np.testing.assert_array_equal(g["sorted_rows"][:valid.size], order)
+    np.testing.assert_array_equal(g["offsets"][:-1], np.searchsorted(np.sort(flat[valid]), np.arange(E)))
 
 
 def test_deterministic_and_stream():
