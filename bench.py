@@ -205,6 +205,37 @@ def describe(p, swiglu=False):
             + (" + combine [T,N]" if p.combine else ""))
 
 
+def measure_dequant(cfg_index, reps, rotate_bytes):
+    """mxfp4_dequantize of a workload's whole expert weight tensor to bf16 (the
+    load-time dequantization), weights rotated over copies; graph of `reps`
+    launches.  Returns (us per launch, bytes per launch)."""
+    import torch
+    from mxfp4_mixture_experts_amd import binding as B
+    from mxfp4_mixture_experts_amd import synthetic as S
+    p = S.make_config(cfg_index)
+    blocks = torch.from_numpy(p.blocks).cuda()
+    scales = torch.from_numpy(p.scales).cuda()
+    copies = max(1, math.ceil(rotate_bytes / (blocks.numel() + scales.numel())))
+    ws = [(blocks, scales)] + [(blocks.clone(), scales.clone()) for _ in range(copies - 1)]
+    out = torch.empty((p.E, p.N, p.K), dtype=torch.bfloat16, device="cuda")
+    B.mxfp4_dequantize(blocks, scales, out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            B.mxfp4_dequantize(ws[i % copies][0], ws[i % copies][1], out)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = blocks.numel() + scales.numel() + out.numel() * 2
+    del g, ws, out
+    return us, nbytes, copies
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(cfg_index, reps=2):
     """The oracle as it stands, on this host, one BLAS thread, on the whole headline workload."""
@@ -334,6 +365,17 @@ def main():
                 "step_frac_combined_roofline": round(roof_t / t_step, 4),
                 "weight_copies_rotated": r["copies"],
             })
+        # the standalone dequantization of the gate_up weights (load-time mirror)
+        us, nbytes, copies = measure_dequant(1, 20, args.rotate_bytes)
+        sec.append({
+            "workload": "gpt-oss-20b gate_up weights MXFP4 [32,5760,90,16] + scales -> bf16 [32,5760,2880] "
+                        "(mxfp4_dequantize)",
+            "kernel_us": round(us, 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": nbytes,
+            "weight_copies_rotated": copies,
+        })
         line["secondary"] = sec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config)

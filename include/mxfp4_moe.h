@@ -209,6 +209,25 @@ int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks
                      void* stream);
 
 /*
+ * MXFP4 -> bf16 dequantization of a weight tensor, in its own layout.
+ * (README "MXFP4": rows of 32-element blocks, 16 code bytes per block with the
+ * even element in the low nibble, one E8M0 scale byte per block, a weight is
+ * its E2M1 value times 2 ** (scale - 127), and the values are exact in bf16;
+ * dequantize_mxfp4 returns the checkpoint's [Experts, Rows, N] layout.)
+ *
+ *   blocks  [rows, K/32, 16] u8, 16-byte aligned (any leading dimensions
+ *           flattened into rows, e.g. rows = E * N).
+ *   scales  [rows, K/32] u8.
+ *   rows >= 0, K >= 32 and K % 32 == 0.
+ *   out     [rows, K] bf16 out, 16-byte aligned:
+ *           out[r, j] = e2m1(code of element j) * 2 ** (scales[r, j / 32] - 127),
+ *           exact (for scale bytes 0..252 every code's value is a bf16).
+ * rows = 0 returns MXFP4_OK and enqueues nothing.
+ */
+int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, long long rows, int K, uint16_t* out,
+                     void* stream);
+
+/*
  * Gate-weighted combine of the k projections of each token.
  * (src/experts.linnet fn forward_topk: the sum over k in f32; fn down_bias_of:
  * the down bias carries the router weights -- here the bias is already inside

@@ -9,6 +9,8 @@ fallback.  If the library is missing, the first call raises.
 from __future__ import annotations
 
 import ctypes
+
+import numpy as np
 import os
 from typing import Optional
 
@@ -30,6 +32,7 @@ ENTRY_POINTS = (
     "mxfp4_expert_proj_swiglu",
     "moe_combine",
     "mxfp4_moe_decode",
+    "mxfp4_dequantize",
 )
 
 _lib_handle = None
@@ -71,6 +74,8 @@ def load_library():
     lib.moe_combine.restype = i32
     lib.mxfp4_moe_decode.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.mxfp4_moe_decode.restype = i32
+    lib.mxfp4_dequantize.argtypes = [vp, vp, ctypes.c_longlong, i32, vp, vp]
+    lib.mxfp4_dequantize.restype = i32
     _lib_handle = lib
     return lib
 
@@ -199,4 +204,20 @@ def mxfp4_moe_decode(logits, E: int, k: int, blocks, scales, bias, N: int, K: in
         int(bool(x_per_slot)), _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
         _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
         _ptr(error_word, "error_word", _I32, dev), _ptr(out, "out", _F32, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_dequantize(blocks, scales, out, stream=None):
+    """MXFP4 -> bf16 (mxfp4_dequantize): blocks [..., KB, 16] u8 and scales [..., KB] u8 into
+    out [..., KB * 32] bf16 (written in place), in the same layout."""
+    lib = load_library()
+    dev = out.device
+    KB = int(blocks.shape[-2])
+    if tuple(blocks.shape[:-1]) != tuple(scales.shape) or blocks.shape[-1] != 16:
+        raise ValueError("blocks must be [..., KB, 16] and scales [..., KB]")
+    if tuple(out.shape) != tuple(scales.shape[:-1]) + (KB * 32,):
+        raise ValueError("out must be [..., KB * 32]")
+    rows = int(np.prod(scales.shape[:-1])) if scales.dim() > 1 else 1
+    st = lib.mxfp4_dequantize(_ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev),
+                              ctypes.c_longlong(rows), KB * 32, _ptr(out, "out", _BF16, dev), _stream(stream, dev))
     _check(st)

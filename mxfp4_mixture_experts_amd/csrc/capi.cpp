@@ -210,6 +210,22 @@ int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks
   return MXFP4_OK;
 }
 
+int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, long long rows, int K, uint16_t* out,
+                     void* stream) {
+  g_last_error[0] = '\0';
+  if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "rows = %lld must be >= 0", rows);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "K = %d must be a positive multiple of 32", K);
+  if (rows == 0) return MXFP4_OK;
+  if (!blocks || !scales || !out) return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(blocks) || !aligned16(out)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and out must be 16-byte aligned");
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_dequantize(blocks, scales, (size_t)rows * (size_t)(K / 32), out,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return MXFP4_OK;
+}
+
 int moe_combine(const float* proj, const float* gates, int T, int k, int N, float* y, void* stream) {
   g_last_error[0] = '\0';
   if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);

@@ -33,6 +33,11 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
                               const int32_t* offsets, const int32_t* sorted_rows, float* out, uint16_t* act,
                               void* workspace, hipStream_t stream);
 
+// dequantize.hip: nblocks MXFP4 blocks (16 code bytes + 1 scale byte each) ->
+// 32 bf16 weights each
+hipError_t launch_dequantize(const uint8_t* blocks, const uint8_t* scales, size_t nblocks, uint16_t* out,
+                             hipStream_t stream);
+
 // combine.hip
 hipError_t launch_combine(const float* proj, const float* gates, int T, int k, int N, float* y,
                           hipStream_t stream);

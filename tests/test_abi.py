@@ -161,3 +161,15 @@ def test_combine_rejects_bad_arguments():
     assert lib.moe_combine(p, p, 4, 4, 0, p, None) == 1
     assert lib.moe_combine(None, p, 4, 4, 8, p, None) == 1
     assert lib.moe_combine(None, None, 0, 4, 8, None, None) == 0
+
+
+def test_dequantize_rejects_bad_arguments():
+    lib = B.load_library()
+    p = ctypes.c_void_p(16)
+    assert lib.mxfp4_dequantize(p, p, ctypes.c_longlong(-1), 64, p, None) == 1
+    assert lib.mxfp4_dequantize(p, p, ctypes.c_longlong(4), 100, p, None) == 1
+    assert lib.mxfp4_dequantize(p, p, ctypes.c_longlong(4), 0, p, None) == 1
+    assert lib.mxfp4_dequantize(None, p, ctypes.c_longlong(4), 64, p, None) == 1
+    assert lib.mxfp4_dequantize(ctypes.c_void_p(8), p, ctypes.c_longlong(4), 64, p, None) == 1
+    assert lib.mxfp4_dequantize(None, None, ctypes.c_longlong(0), 64, None, None) == 0
+

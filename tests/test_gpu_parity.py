@@ -370,3 +370,53 @@ def test_swiglu_model_size(cfg):
     proj = np.stack([vg, vu], axis=-1)
     mag = np.stack([mg, mu], axis=-1)
     check_act(g["act"].reshape(R, NA)[rows, cols][:, None], proj, mag, f"{p.name} act")
+
+
+# ----------------------------------------------------------------- dequantization
+def _dequant_gpu(blocks, scales):
+    b = torch.from_numpy(np.ascontiguousarray(blocks)).cuda()
+    s = torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    out = torch.empty(scales.shape[:-1] + (scales.shape[-1] * 32,), dtype=torch.bfloat16, device="cuda")
+    B.mxfp4_dequantize(b, s, out)
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _bf16_of(values_f64):
+    """The oracle's exact values as bf16 bit patterns (exact for the scales used)."""
+    f32 = np.asarray(values_f64, dtype=np.float64).astype(np.float32)
+    bits = S.f32_to_bf16_bits(f32)
+    assert np.array_equal(O.bf16_to_f64(bits), np.asarray(values_f64)), "value not exact in bf16"
+    return bits
+
+
+def test_dequantize_every_byte_and_scale():
+    """Every code byte under every scale byte 0..252: bit-exact bf16."""
+    _announce("dequantize: all bytes x scales 0..252")
+    scl = np.arange(0, 253, dtype=np.uint8)
+    blocks = np.broadcast_to(np.arange(256, dtype=np.uint8).reshape(16, 16), (scl.size, 16, 16))
+    scales = np.broadcast_to(scl[:, None], (scl.size, 16)).copy()
+    got = _dequant_gpu(blocks.copy(), scales)
+    want = _bf16_of(O.dequantize_mxfp4(blocks, scales))
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("shape", [(4, 256, 4), (3, 37, 90), (1, 1, 1), (2, 1000, 7)])
+def test_dequantize_random(shape):
+    _announce(f"dequantize random {shape}")
+    rng = np.random.default_rng(sum(shape))
+    blocks = rng.integers(0, 256, shape + (16,), dtype=np.uint8)
+    scales = rng.integers(100, 150, shape, dtype=np.uint8)
+    np.testing.assert_array_equal(_dequant_gpu(blocks, scales), _bf16_of(O.dequantize_mxfp4(blocks, scales)))
+
+
+def test_dequantize_model_size_sampled():
+    """The gpt-oss-20b gate_up weights [32, 5760, 90, 16] -> [32, 5760, 2880] bf16, sampled rows."""
+    p = S.make_config(1)
+    _announce("dequantize gate_up weights (sampled rows)")
+    got = _dequant_gpu(p.blocks, p.scales)
+    assert got.shape == (32, 5760, 2880)
+    rng = np.random.default_rng(11)
+    for e, n in zip(rng.integers(0, 32, 40).tolist() + [0, 31], rng.integers(0, 5760, 40).tolist() + [0, 5759]):
+        np.testing.assert_array_equal(got[e, n], _bf16_of(O.dequantize_mxfp4(p.blocks[e, n], p.scales[e, n])))
+
