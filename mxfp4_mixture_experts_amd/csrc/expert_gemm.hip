@@ -73,6 +73,9 @@ constexpr int kAUnit = 3 * 1024;         // activation codes of one (row sub-til
 constexpr int kFmtFp6E2M3 = 2;           // MFMA operand format codes
 constexpr int kFmtFp4E2M1 = 4;
 constexpr int kXcds = 8;
+// word 3 of a raw buffer resource (stride 0, byte offsets, 32-bit data format)
+constexpr int kBufferFlags = 0x00020000;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
@@ -406,6 +409,16 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 constexpr int kAhead = 2;  // activation k-steps loaded ahead
+// Keeps the main loop in the order it is written: no memory access crosses
+// it (compiler fence) and no instruction at all (scheduling barrier).  Left
+// free, the scheduler moves each MFMA up to the LDS read or activation load
+// that feeds it, to shorten register lifetimes, and exposes their latency;
+// with the operands addressed by buffer resources (one VGPR per stream) the
+// written order fits in the registers of two waves per SIMD.
+__device__ __forceinline__ void pipeline_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Every global read of the main loop is an ordinary load into registers (the
 // weight stages are then written to LDS with ds_write): with LDS DMAs in
@@ -456,34 +469,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   bias_lds[tid] = bias ? bf16_bits_to_f32(bias[(size_t)tc.e * N + min(tc.nt * kBN + tid, N - 1)]) : 0.f;
   const bool valid = wave * 32 < tc.m_count;
 
-  // activations: this wave's row sub-tile, k-steps consecutive
+  // activations: this wave's row sub-tile, k-steps consecutive.  Buffer
+  // loads: the wave's records as one resource (SGPRs), a 32-bit lane offset
+  // in a VGPR and the k-step in the scalar offset.
   const size_t unit0 = ((size_t)tc.mtile * kWaves + wave) * NKP;
-  const uint8_t* a_ptr = aq + unit0 * kAUnit;
-  const uint32_t* as_ptr = as + unit0 * 64 + lane;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(aq + unit0 * kAUnit), (short)0, NKP * kAUnit, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(as + unit0 * 64), (short)0, NKP * 256, kBufferFlags);
 
   // weight stage pieces: piece i = wave + 4q (q < 8) covers tile rows 8i ..
   // 8i + 7 (1 KB); lane L takes row 8i + L / 8 and LDS slot L % 8, which holds
   // block (L % 8) ^ swizzle(row) of the stage (rows past N re-read row N - 1,
   // blocks past K re-read block K - 1)
   const int n0 = tc.nt * kBN;
-  const uint8_t* b_exp = blocks + (size_t)e * N * KB * 16;
+  // the expert's codes as one resource (at most 4 GiB, checked on the host)
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(blocks + (size_t)e * N * KB * 16), (short)0, N * KB * 16, kBufferFlags);
   const int b_r0 = n0 + 8 * wave + (lane >> 3);  // row of piece q: b_r0 + 32 q
   // swizzle(8 i + L / 8) = (L / 8) ^ (i & 1), and i = wave + 4 q has the parity of wave
   const int b_blk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
   // weight-scale words: the 2 KB of a stage as two 1 KB halves; waves of equal
   // parity move the same half (the same bytes to the same place)
-  const uint8_t* bs_ptr = reinterpret_cast<const uint8_t*>(wsc + ((size_t)e * NT + tc.nt) * NS * kSubN * 64) +
-                          (wave & 1) * 1024 + lane * 16;
+  const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(wsc + ((size_t)e * NT + tc.nt) * NS * kSubN * 64), (short)0, NS * kSubN * 256,
+      kBufferFlags);
+  const int bs_off = (wave & 1) * 1024 + lane * 16;
 
   // A stage's weights move in two halves (pieces q = 4h .. 4h + 3), the
   // second with the scale words, through 4 (5) registers of 16 bytes.
   u32x4_t rb[5];
   auto load_b = [&](int s, int h) {
-    const uint32_t blk = (uint32_t)min(kStageBlocks * s + b_blk, KB - 1) * 16;
+    const int blk = min(kStageBlocks * s + b_blk, KB - 1) * 16;
 #pragma unroll
     for (int q = 0; q < 4; q++)
-      rb[q] = *reinterpret_cast<const u32x4_t*>(b_exp + (uint32_t)min(b_r0 + 32 * (4 * h + q), N - 1) * (KB * 16) + blk);
-    if (h) rb[4] = *reinterpret_cast<const u32x4_t*>(bs_ptr + (size_t)s * (kSubN * 64 * 4));
+      rb[q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(b_r0 + 32 * (4 * h + q), N - 1) * (KB * 16) + blk, 0,
+                                                    0);
+    if (h) rb[4] = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, bs_off, s * (kSubN * 64 * 4), 0);
   };
   auto store_b = [&](uint8_t* sb, uint32_t* ss, int h) {
 #pragma unroll
@@ -511,14 +533,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   uint32_t rs[kAhead];
   auto load_a = [&](int g, auto jc) {
     constexpr int J = decltype(jc)::value % kAhead;
-    const uint8_t* p = a_ptr + (size_t)g * kAUnit;
-    const u32x4_t h0 = *reinterpret_cast<const u32x4_t*>(p + lane * 16);
-    const uint2 h1 = *reinterpret_cast<const uint2*>(p + 1024 + lane * 8);
-    const u32x4_t l0 = *reinterpret_cast<const u32x4_t*>(p + 1536 + lane * 16);
-    const uint2 l1 = *reinterpret_cast<const uint2*>(p + 2560 + lane * 8);
+    const int so = g * kAUnit;
+    const u32x4_t h0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16, so, 0);
+    const u32x2_t h1 = __builtin_amdgcn_raw_buffer_load_b64(a_rsrc, lane * 8 + 1024, so, 0);
+    const u32x4_t l0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16 + 1536, so, 0);
+    const u32x2_t l1 = __builtin_amdgcn_raw_buffer_load_b64(a_rsrc, lane * 8 + 2560, so, 0);
     rh[J] = v6i{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y};
     rl[J] = v6i{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y};
-    rs[J] = as_ptr[(size_t)g * 64];
+    rs[J] = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc, lane * 4, g * 256, 0);
   };
 
   using J0 = std::integral_constant<int, 0>;
@@ -548,9 +570,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo, bq[c], acc[c], kFmtFp6E2M3, kFmtFp4E2M1, 1,
                                                                rs[A], J, bsc[c]);
       if (next) read_b(sb, c, (J + 1) & 3);
-      // a compiler fence: the read stays here (under pressure the compiler
-      // would sink every read next to its use and expose its latency)
-      asm volatile("" ::: "memory");
+      // the read stays here, 7 sub-tiles ahead of its MFMAs
+      pipeline_fence();
     }
   };
 
@@ -585,29 +606,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int c = 0; c < kSubN; c++) read_b(sb, c, 0);
         const int g = s * kStepsPerStage;
-        asm volatile("" ::: "memory");  // the reads are issued before the first MFMA
+        pipeline_fence();  // the reads are issued before the first MFMA
         if (!last) {
           kstep(sb, bsc, J0{}, true);
           load_a(g + 2, J2{});
-          asm volatile("" ::: "memory");
+          pipeline_fence();
           kstep(sb, bsc, J1{}, true);
           load_a(g + 3, J3{});
           mid();
-          asm volatile("" ::: "memory");
+          pipeline_fence();
           kstep(sb, bsc, J2{}, true);
           load_a(g + 4, J0{});
-          asm volatile("" ::: "memory");
+          pipeline_fence();
           kstep(sb, bsc, J3{}, false);
           load_a(g + 5, J1{});
-          asm volatile("" ::: "memory");
+          pipeline_fence();
         } else {
           // the last stage: k-steps past the last real block are skipped
           kstep(sb, bsc, J0{}, true);
           load_a(g + 2, J2{});
-          asm volatile("" ::: "memory");
+          pipeline_fence();
           if (g + 1 < nks) kstep(sb, bsc, J1{}, true);
           load_a(g + 3, J3{});
-          asm volatile("" ::: "memory");
+          pipeline_fence();
           if (g + 2 < nks) kstep(sb, bsc, J2{}, true);
           if (g + 3 < nks) kstep(sb, bsc, J3{}, false);
         }
