@@ -110,6 +110,24 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
                           int32_t* sorted_rows, int32_t* error_word, void* stream);
 
 /*
+ * Dense router weights: every expert's probability, exactly zero outside each
+ * token's top k -- the weights of the dense-routing form, which evaluates every
+ * expert on every token (a validation mode of the sparse path: with all E
+ * experts as given ids, mxfp4_expert_proj and moe_combine with these weights
+ * give the sparse result up to fp32 rounding).
+ * (README "Dense routing"; src/experts.linnet fn route: the experts ranked k or
+ * worse are floored to -1e30 and the softmax taken over all E, so the floored
+ * entries are exactly zero and the kept ones the softmax over the kept logits.)
+ *
+ *   logits  [T, E] bf16, finite.  T >= 0, 1 <= E <= MXFP4_MAX_EXPERTS, 1 <= k <= E.
+ *   probs   [T, E] f32 out: probs[t, e] = exp(l_e - max) / sum over the kept of
+ *           exp(l_j - max) if e ranks below k (ranking as mxfp4_moe_route_group),
+ *           else 0.  The kept values equal mxfp4_moe_route_group's gates bit for bit.
+ * T = 0 returns MXFP4_OK and enqueues nothing.
+ */
+int mxfp4_moe_dense_route(const uint16_t* logits, int T, int E, int k, float* probs, void* stream);
+
+/*
  * Workspace bytes mxfp4_expert_proj needs for these sizes and this path
  * (MXFP4_PATH_AUTO resolves exactly as mxfp4_expert_proj does).  0 means none.
  * Returns (size_t)-1 for invalid sizes.

@@ -33,6 +33,7 @@ ENTRY_POINTS = (
     "moe_combine",
     "mxfp4_moe_decode",
     "mxfp4_dequantize",
+    "mxfp4_moe_dense_route",
 )
 
 _lib_handle = None
@@ -76,6 +77,8 @@ def load_library():
     lib.mxfp4_moe_decode.restype = i32
     lib.mxfp4_dequantize.argtypes = [vp, vp, ctypes.c_longlong, i32, vp, vp]
     lib.mxfp4_dequantize.restype = i32
+    lib.mxfp4_moe_dense_route.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.mxfp4_moe_dense_route.restype = i32
     _lib_handle = lib
     return lib
 
@@ -221,3 +224,13 @@ def mxfp4_dequantize(blocks, scales, out, stream=None):
     st = lib.mxfp4_dequantize(_ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev),
                               ctypes.c_longlong(rows), KB * 32, _ptr(out, "out", _BF16, dev), _stream(stream, dev))
     _check(st)
+
+
+def mxfp4_moe_dense_route(logits, T: int, E: int, k: int, probs, stream=None):
+    """Dense router weights (mxfp4_moe_dense_route): probs [T,E] f32, zero outside each token's top k."""
+    lib = load_library()
+    dev = probs.device
+    st = lib.mxfp4_moe_dense_route(_ptr(logits, "logits", _BF16, dev), int(T), int(E), int(k),
+                                   _ptr(probs, "probs", _F32, dev), _stream(stream, dev))
+    _check(st)
+

@@ -159,6 +159,20 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
   return MXFP4_OK;
 }
 
+int mxfp4_moe_dense_route(const uint16_t* logits, int T, int E, int k, float* probs, void* stream) {
+  g_last_error[0] = '\0';
+  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
+  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
+  if (k < 1 || k > E) return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, E = %d]", k, E);
+  if (T == 0) return MXFP4_OK;
+  if (!logits || !probs) return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_dense_route(logits, T, E, k, probs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense_route launch");
+  return MXFP4_OK;
+}
+
 size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x_per_slot, int path) {
   if (E < 1 || E > MXFP4_MAX_EXPERTS || N < 1 || T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
   if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return (size_t)-1;

@@ -13,6 +13,10 @@ hipError_t launch_route_group(const uint16_t* logits, const int32_t* ids_in, int
                               int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
                               int32_t* error_word, hipStream_t stream);
 
+// dense router weights [T, E]: softmax over the logits with every expert
+// ranked k or worse floored (exactly zero)
+hipError_t launch_dense_route(const uint16_t* logits, int T, int E, int k, float* probs, hipStream_t stream);
+
 // expert_gemv.hip
 size_t gemv_lds_bytes(int T, int K);
 // act != NULL: the gated activation of (even, odd) output row pairs, bf16

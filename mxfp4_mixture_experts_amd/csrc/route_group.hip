@@ -434,7 +434,76 @@ hipError_t launch_ec(const uint16_t* logits, const int32_t* ids_in, int T, int E
   return hipGetLastError();
 }
 
+// Dense router weights (src/experts.linnet fn route, README "Dense routing"):
+// one wave per token ranks its logits as above, floors every expert ranked k
+// or worse to -1e30 and takes the softmax over all E, whose floored entries
+// are exactly zero, so the kept ones equal the gates of the sparse routing.
+template <int EC>
+__global__ __launch_bounds__(kRouteThreads) void dense_route_kernel(const uint16_t* __restrict__ logits, int T, int E,
+                                                                   int k, float* __restrict__ probs) {
+  const int lane = threadIdx.x & 63;
+  const int t = (blockIdx.x * kRouteThreads + threadIdx.x) >> 6;
+  if (t >= T) return;  // whole waves
+  const uint16_t* lrow = logits + (size_t)t * E;
+  float l[EC];
+  int rank[EC];
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const int e = lane + 64 * i;
+    l[i] = bf16_bits_to_f32(lrow[min(e, E - 1)]);
+    if (e >= E) l[i] = -INFINITY;
+    rank[i] = 0;
+  }
+#pragma unroll
+  for (int jc = 0; jc < EC; jc++) {
+    const int jn = min(64, E - 64 * jc);
+    for (int jj = 0; jj < jn; jj++) {
+      const float lj = readlane_f(l[jc], jj);
+      const int j = 64 * jc + jj;
+#pragma unroll
+      for (int i = 0; i < EC; i++) {
+        const int e = lane + 64 * i;
+        rank[i] += (lj > l[i] || (lj == l[i] && j < e)) ? 1 : 0;
+      }
+    }
+  }
+  // the largest kept logit (rank 0) is the softmax's maximum
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const uint64_t m = __ballot(lane + 64 * i < E && rank[i] == 0);
+    if (m) mx = readlane_f(l[i], __ffsll((long long)m) - 1);
+  }
+  float num[EC];
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const int e = lane + 64 * i;
+    // floored logits: exp(-1e30 - mx) is exactly 0 in fp32
+    num[i] = (e < E && rank[i] < k) ? expf(l[i] - mx) : 0.f;
+    part += num[i];
+  }
+  const float sum = wave_sum(part);
+#pragma unroll
+  for (int i = 0; i < EC; i++) {
+    const int e = lane + 64 * i;
+    if (e < E) probs[(size_t)t * E + e] = num[i] / sum;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dense_route(const uint16_t* logits, int T, int E, int k, float* probs, hipStream_t stream) {
+  const dim3 grid((T + kRouteThreads / 64 - 1) / (kRouteThreads / 64));
+  if (E <= 64)
+    hipLaunchKernelGGL(dense_route_kernel<1>, grid, dim3(kRouteThreads), 0, stream, logits, T, E, k, probs);
+  else if (E <= 128)
+    hipLaunchKernelGGL(dense_route_kernel<2>, grid, dim3(kRouteThreads), 0, stream, logits, T, E, k, probs);
+  else
+    hipLaunchKernelGGL(dense_route_kernel<kExpertChunks>, grid, dim3(kRouteThreads), 0, stream, logits, T, E, k,
+                       probs);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_group(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k,
                               int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,

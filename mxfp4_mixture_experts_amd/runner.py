@@ -80,6 +80,31 @@ class DeviceProblem:
                            self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.out, self.error_word,
                            stream)
 
+    def run_dense(self, stream=None):
+        """The dense-routing form (a validation mode): every expert on every token,
+        weighed by the dense router weights, through the same kernels.  Returns
+        y [T, N] f32 (gate/up-style problems: one input per token)."""
+        p = self.p
+        assert p.logits is not None and not p.x_per_slot
+        T, E, N = p.T, p.E, p.N
+        dev = self.device
+        probs = torch.empty((T, E), dtype=torch.float32, device=dev)
+        B.mxfp4_moe_dense_route(self.logits, T, E, p.k, probs, stream)
+        all_ids = torch.arange(E, dtype=torch.int32, device=dev).repeat(T, 1).contiguous()
+        ids = torch.empty((T, E), dtype=torch.int32, device=dev)
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        rows = torch.empty((T * E,), dtype=torch.int32, device=dev)
+        B.mxfp4_moe_route_group(None, all_ids, T, E, E, ids, None, offsets, rows, None, stream)
+        out = torch.empty((T, E, N), dtype=torch.float32, device=dev)
+        nbytes = B.mxfp4_expert_proj_workspace_size(E, N, T, E, p.K, False, self.path)
+        ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev) if nbytes else None
+        B.mxfp4_expert_proj(self.blocks, self.scales, self.bias, E, N, p.K, self.x, False, T, E, offsets, rows, out,
+                            self.path, ws, stream)
+        y = torch.empty((T, N), dtype=torch.float32, device=dev)
+        B.moe_combine(out, probs, T, E, N, y, stream)
+        torch.cuda.synchronize(dev)
+        return probs.cpu().numpy(), y.cpu().numpy()
+
     def run(self, stream=None):
         self.route_group(stream)
         self.expert_proj(stream)

@@ -147,6 +147,16 @@ def softmax_at(logits_f64: np.ndarray, ids: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
+def dense_route(logits_bits: np.ndarray, k: int) -> np.ndarray:
+    """The dense-routing weights [T, E] (``route``; README "Dense routing"): every
+    expert ranked k or worse is floored to -1e30 and the softmax is taken over
+    all E, in float64; the floored entries come out exactly zero."""
+    l = bf16_to_f64(logits_bits)
+    floored = np.where(expert_ranks(l) < k, l, -1e30)
+    z = np.exp(floored - floored.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
 def gates_for_ids(logits_bits: np.ndarray, ids: np.ndarray) -> np.ndarray:
     """Router weights for given expert ids: softmax over the chosen logits."""
     return softmax_at(bf16_to_f64(logits_bits), ids)

@@ -173,3 +173,14 @@ def test_dequantize_rejects_bad_arguments():
     assert lib.mxfp4_dequantize(ctypes.c_void_p(8), p, ctypes.c_longlong(4), 64, p, None) == 1
     assert lib.mxfp4_dequantize(None, None, ctypes.c_longlong(0), 64, None, None) == 0
 
+
+def test_dense_route_rejects_bad_arguments():
+    lib = B.load_library()
+    p = ctypes.c_void_p(16)
+    assert lib.mxfp4_moe_dense_route(p, -1, 32, 4, p, None) == 1
+    assert lib.mxfp4_moe_dense_route(p, 4, 0, 1, p, None) == 1
+    assert lib.mxfp4_moe_dense_route(p, 4, 513, 4, p, None) == 1
+    assert lib.mxfp4_moe_dense_route(p, 4, 32, 33, p, None) == 1
+    assert lib.mxfp4_moe_dense_route(None, 4, 32, 4, p, None) == 1
+    assert lib.mxfp4_moe_dense_route(None, 0, 32, 4, None, None) == 0
+

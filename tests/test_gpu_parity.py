@@ -420,3 +420,38 @@ def test_dequantize_model_size_sampled():
     for e, n in zip(rng.integers(0, 32, 40).tolist() + [0, 31], rng.integers(0, 5760, 40).tolist() + [0, 5759]):
         np.testing.assert_array_equal(got[e, n], _bf16_of(O.dequantize_mxfp4(p.blocks[e, n], p.scales[e, n])))
 
+
+# ----------------------------------------------------------------- dense-routing validation mode
+@pytest.mark.parametrize("path", [1, 2])
+def test_dense_routing_mode(path):
+    """README "Dense routing": the dense router weights (zero outside the top k) and
+    every expert on every token through the same kernels give the sparse result."""
+    p = S.make_custom(E=8, N=256, K=320, T=37, k=2, route="logits")
+    _announce(f"dense routing mode path={PATHS[path]}")
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p, path=path)
+    dp.run()
+    g = dp.results()
+    probs, y_dense = dp.run_dense()
+    # the dense weights: the sparse gates scattered (bit for bit), zeros elsewhere
+    want = np.zeros((p.T, p.E), np.float32)
+    np.put_along_axis(want, g["ids"].astype(np.int64), g["gates"], axis=1)
+    np.testing.assert_array_equal(probs, want)
+    assert np.abs(probs - O.dense_route(p.logits, p.k)).max() <= GATE_TOL
+    ref_y, ref_m = O.combine(ref["out"], ref["gates"], ref["mag"])
+    check_close(y_dense, ref_y, ref_m, "dense-routing y")
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 32, 4), (64, 32, 4), (300, 100, 7)])
+def test_dense_route_weights(T, E, k):
+    p = S.make_custom(E=E, N=1, K=32, T=T, k=k, route="logits")
+    _announce(f"dense route T={T} E={E} k={k}")
+    lg = torch.from_numpy(p.logits.view(np.int16)).cuda().view(torch.bfloat16)
+    probs = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    B.mxfp4_moe_dense_route(lg, T, E, k, probs)
+    torch.cuda.synchronize()
+    got = probs.cpu().numpy()
+    ref = O.dense_route(p.logits, k)
+    assert np.all((got != 0) == (ref != 0))
+    assert np.abs(got - ref).max() <= GATE_TOL
+

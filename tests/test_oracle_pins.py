@@ -217,6 +217,21 @@ def test_gates_equal_floored_full_softmax():
     assert np.all(np.diff(gates, axis=1) <= 0)      # highest first
 
 
+def test_dense_route_is_scattered_gates():
+    """The oracle's dense weights: the sparse gates at the top-k ids, exact zeros
+    elsewhere, rows summing to 1 (and ties ranked like the sparse routing)."""
+    rng = np.random.default_rng(8)
+    bits = _bf16(rng.standard_normal((200, 32)))
+    bits[:20, 5] = bits[:20, 9]                          # ties
+    ids, gates = O.route_topk(bits, 4)
+    dense = O.dense_route(bits, 4)
+    want = np.zeros_like(dense)
+    np.put_along_axis(want, ids.astype(np.int64), gates, axis=1)
+    np.testing.assert_allclose(dense, want, rtol=1e-15, atol=0)
+    assert np.count_nonzero(dense, axis=1).max() == 4
+    np.testing.assert_allclose(dense.sum(axis=1), 1.0, rtol=1e-15)
+
+
 # ----------------------------------------------------------------- grouping
 @pytest.mark.parametrize("T,E,k", [(0, 4, 2), (1, 32, 4), (37, 8, 3), (500, 32, 4)])
 def test_grouping_bruteforce(T, E, k):
