@@ -11,7 +11,7 @@
 //    the checkpoint stores them: a lane of the B operand holds one 16-byte
 //    MXFP4 block (32 E2M1 codes, low nibble first) of one weight row, and its
 //    E8M0 byte is that lane's B scale.  No dequantization anywhere.
-//  * bf16 activations have no MX form, so a pre-pass (quantize_tiles_kernel)
+//  * bf16 activations have no MX form, so a pre-pass (quantize_tile in prepare_kernel)
 //    splits every 32-element block of every routed row once into two MX-FP6
 //    (E2M3) terms, hi + lo, each with its own E8M0 scale, using the gfx950
 //    converts v_cvt_scalef32_pk32_fp6_bf16 (round to nearest even of x/2^e)
@@ -34,7 +34,7 @@
 //    order so that the MFMA lanes' 16-byte reads (32 rows, one block) hit
 //    distinct LDS banks.  Double-buffered, written in two halves while the
 //    current stage is multiplied, one barrier per stage.
-//  * Weight scales are repacked per call (repack_wscales_kernel) into the
+//  * Weight scales are repacked per call (repack_panel in prepare_kernel) into the
 //    per-lane words of a stage: 4 bytes, one per k-step, picked by the MFMA's
 //    scale byte select.
 //  * The tile schedule is derived on the device from expert_offsets (wave
@@ -193,13 +193,12 @@ __device__ __forceinline__ bool locate_row_tile(const int32_t* offsets, int E, i
 // 8-byte load into its own six registers; and 64 u32 scales (hi | lo << 8).
 // The k-steps of a sub-tile are consecutive.  Rows past the expert's last routed row, and blocks
 // past K, are zero codes with scale 127.
-__global__ __launch_bounds__(kQThreads) void quantize_tiles_kernel(const uint16_t* __restrict__ x, int x_per_slot,
-                                                                   int k, int R, int E, int K, int NKP,
-                                                                   const int32_t* __restrict__ offsets,
-                                                                   const int32_t* __restrict__ sorted_rows,
-                                                                   uint8_t* __restrict__ q, uint32_t* __restrict__ s) {
-  const int t = blockIdx.x / NKP;
-  const int g = blockIdx.x - t * NKP;
+__device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restrict__ x, int x_per_slot, int k, int R,
+                                              int E, int K, int NKP, const int32_t* __restrict__ offsets,
+                                              const int32_t* __restrict__ sorted_rows, uint8_t* __restrict__ q,
+                                              uint32_t* __restrict__ s) {
+  const int t = blk / NKP;
+  const int g = blk - t * NKP;
   const int lane = threadIdx.x & 63;
   const int sub = threadIdx.x >> 6;
   int e, b, f, tb;
@@ -249,12 +248,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_tiles_kernel(const uint16_
 // (l32, h) with l32 = row % 32, word c = row / 32.
 constexpr int kRepackMaxKB = 256;  // K <= 8192 (LDS: 256 rows x KB bytes + 4)
 
-__global__ __launch_bounds__(kQThreads) void repack_wscales_kernel(const uint8_t* __restrict__ scales, int E, int N,
-                                                                   int KB, int NT, int NS,
-                                                                   uint32_t* __restrict__ out) {
-  extern __shared__ uint32_t panel[];  // (kBN * KB + 4) / 4 + 1 words
-  const int nt = blockIdx.x % NT;
-  const int e = blockIdx.x / NT;
+__device__ __forceinline__ void repack_panel(int blk, uint32_t* panel, const uint8_t* __restrict__ scales, int E,
+                                             int N, int KB, int NT, int NS, uint32_t* __restrict__ out) {
+  const int nt = blk % NT;
+  const int e = blk / NT;
   const int t = threadIdx.x;  // row within the panel
   const int rows = min(kBN, N - nt * kBN);
   const size_t total = (size_t)E * N * KB;                   // bytes in the array
@@ -298,6 +295,24 @@ __global__ __launch_bounds__(kQThreads) void repack_wscales_kernel(const uint8_t
     dst[(size_t)s * (kSubN * 64)] = w0;                // lane l32 (h = 0)
     dst[(size_t)s * (kSubN * 64) + 32 * kSubN] = w1;   // lane l32 + 32 (h = 1)
   }
+}
+
+// The two passes before the GEMM in one launch (they are independent, so
+// their workgroups run side by side): workgroups [0, nrep) repack the weight
+// scales of one (expert, panel) each, the rest quantize one (row tile,
+// k-step) each.  Dynamic LDS: a panel's scale rows.
+__global__ __launch_bounds__(kQThreads) void prepare_kernel(const uint8_t* __restrict__ scales, int E, int N, int KB,
+                                                            int NT, int NS, uint32_t* __restrict__ wsc, int nrep,
+                                                            const uint16_t* __restrict__ x, int x_per_slot, int k,
+                                                            int R, int K, int NKP,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ sorted_rows,
+                                                            uint8_t* __restrict__ q, uint32_t* __restrict__ qs) {
+  extern __shared__ uint32_t panel[];  // (kBN * KB + 4) / 4 + 1 words
+  if ((int)blockIdx.x < nrep)
+    repack_panel(blockIdx.x, panel, scales, E, N, KB, NT, NS, wsc);
+  else
+    quantize_tile(blockIdx.x - nrep, x, x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, q, qs);
 }
 
 // ---------------------------------------------------------------------------
@@ -845,25 +860,24 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   uint32_t* bsc = reinterpret_cast<uint32_t*>(ws + l.wscales);
   const int R = T * k;
   const size_t tiles = row_tiles_max(E, T, k);
-  hipLaunchKernelGGL(quantize_tiles_kernel, dim3((unsigned)(tiles * NKP)), dim3(kQThreads), 0, stream, x,
-                     x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, aq, as);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // dynamic LDS: the panel's scale rows (23 KB at K = 2880, so several
+  // dynamic LDS: a panel's scale rows (23 KB at K = 2880, so several
   // workgroups share a CU)
   const size_t panel_bytes = ((size_t)(kBN * (K / 32) + 4) / 4 + 1) * 4;
+  hipError_t err;
   if (panel_bytes > 65536) {
     static bool attr_set = false;
     if (!attr_set) {
-      err = hipFuncSetAttribute(reinterpret_cast<const void*>(&repack_wscales_kernel),
+      err = hipFuncSetAttribute(reinterpret_cast<const void*>(&prepare_kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)(((kBN * kRepackMaxKB + 4) / 4 + 1) * 4));
       if (err != hipSuccess) return err;
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL(repack_wscales_kernel, dim3((unsigned)(E * NT)), dim3(kQThreads), panel_bytes, stream, scales,
-                     E, N, K / 32, NT, NS, bsc);
+  const long long nrep = (long long)E * NT;
+  const long long nq = (long long)tiles * NKP;
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(nrep + nq)), dim3(kQThreads), panel_bytes, stream, scales, E, N,
+                     K / 32, NT, NS, bsc, (int)nrep, x, x_per_slot, k, R, K, NKP, offsets, sorted_rows, aq, as);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long tiles_max = (long long)tiles * NT;

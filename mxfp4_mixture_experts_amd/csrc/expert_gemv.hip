@@ -10,7 +10,9 @@
 //
 // Work decomposition.  A workgroup serves one expert that has routed rows
 // (blockIdx.y = the g-th such expert, found with one ballot over the expert
-// offsets) and WAVES * 16 consecutive weight rows, 16 per wave.  Lane l of a
+// offsets) and row blocks of WAVES * 16 consecutive weight rows, 16 per wave:
+// blocks blockIdx.x, blockIdx.x + gridDim.x, ... streamed back to back with
+// the token rows staged once.  Lane l of a
 // wave streams weight row (16-row base + l % 16), MX block 4 * i + l / 16 for
 // i = 0, 1, ...: one 128-bit load per lane per i, and every load of the wave
 // covers 16 rows x 64 contiguous bytes.  The loads run a two-stage pipeline
