@@ -92,6 +92,16 @@ def test_small_cases(case, path):
     full_parity(p, path)
 
 
+@pytest.mark.parametrize("case", [
+    dict(E=4, N=64, K=8192, T=20, k=2, route="logits"),                  # the GEMM's K limit (32 stages)
+    dict(E=3, N=516, K=1024, T=70, k=2, x_per_slot=True, route="ids"),    # N % 256 = 4: a 4-row last panel
+])
+def test_gemm_limits(case):
+    p = S.make_custom(**case)
+    p.name = f"gemm K={case['K']} N={case['N']}"
+    full_parity(p, 2)
+
+
 def test_paths_agree_closely():
     """GEMV (exact products) and GEMM (two-term MX-FP6 activations) on the same input."""
     p = S.make_custom(E=8, N=256, K=2880, T=24, k=4, route="logits")
