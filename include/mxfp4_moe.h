@@ -103,7 +103,9 @@ const char* mxfp4_last_error(void);
  *               not written.
  *   error_word  [1] i32 out, or NULL: overwritten with the MXFP4_ROUTE_ERR_* bits
  *               found (0 = none).
- * One kernel launch (a single workgroup).  T = 0 writes zero offsets.
+ * T * k <= 64: one kernel launch (a single workgroup); more rows: a routing
+ * launch (one token per wave) and a grouping launch (ceil(T * k / 1024)
+ * workgroups).  T = 0 writes zero offsets.
  */
 int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, int E, int k,
                           int32_t* topk_ids, float* gates, int32_t* expert_offsets,
