@@ -8,9 +8,12 @@
 //
 // MI355X design:
 //  * The weight codes are fed to v_mfma_scale_f32_32x32x64_f8f6f4 exactly as
-//    the checkpoint stores them: a lane of the B operand holds one 16-byte
+//    the checkpoint stores them: a lane of the A operand holds one 16-byte
 //    MXFP4 block (32 E2M1 codes, low nibble first) of one weight row, and its
-//    E8M0 byte is that lane's B scale.  No dequantization anywhere.
+//    E8M0 byte is that lane's A scale.  No dequantization anywhere.  The
+//    activations are the B operand, so the accumulators hold the transposed
+//    product: a lane ends with runs of 4 consecutive output columns of one
+//    routed row.
 //  * bf16 activations have no MX form, so a pre-pass (quantize_tile in prepare_kernel)
 //    splits every 32-element block of every routed row once into two MX-FP6
 //    (E2M3) terms, hi + lo, each with its own E8M0 scale, using the gfx950
@@ -20,7 +23,7 @@
 //    (exact, and exactly a bf16) quantized the same way.  The GEMM issues one
 //    MFMA per term; E2M3 x E2M1 runs at the FP4 MFMA rate on gfx950.
 //  * The pre-pass also gathers the routed rows into row tiles (per expert, in
-//    routed order), written in the register image of the MFMA A operand, so
+//    routed order), written in the register image of the MFMA B operand, so
 //    that a wave fetches one k-step of its 32 rows with four contiguous loads
 //    straight into registers, two k-steps ahead.
 //  * Tile = 128 routed rows x 256 weight rows, 4 waves; wave w owns routed
@@ -41,8 +44,9 @@
 //    scans), ordered so that the row tiles sharing a weight panel run back to
 //    back on one XCD and read the panel from its L2.  Surplus workgroups exit
 //    at once.  No host synchronisation; any skew of rows per expert.
-//  * The results are scattered through sorted_rows in the epilogue (bias
-//    added there).
+//  * The accumulators start at the bias.  The epilogue passes each wave's
+//    results through LDS so that every store instruction writes whole
+//    128-byte lines (4 rows x 256 bytes), scattered through sorted_rows.
 
 #include <type_traits>
 
@@ -187,7 +191,7 @@ __device__ __forceinline__ bool locate_row_tile(const int32_t* offsets, int E, i
 }
 
 // Workgroup = one (row tile t, k-step g); wave = row sub-tile sub; lane (l32, h) = row 32 sub + l32, block 2 g + h.
-// Writes the register image of the MFMA A operand: per (t, sub, g) 3 KB =
+// Writes the register image of the MFMA B operand: per (t, sub, g) 3 KB =
 // hi bytes 0..15 [lane][16 B] | hi 16..23 [lane][8 B] | lo 0..15 [lane][16 B]
 // | lo 16..23 [lane][8 B], so that each 24-byte operand is one 16-byte and one
 // 8-byte load into its own six registers; and 64 u32 scales (hi | lo << 8).
@@ -536,11 +540,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int j = 0; j < kStepsPerStage; j++) b_off[j] = l32 * 128 + (((2 * j + half) ^ swz) << 4);
 
+  // Accumulator c is the 32 x 32 product block (weight rows 32 c .. 32 c + 31)
+  // x (the wave's routed rows): the weights are the MFMA's A operand, the
+  // activations its B operand.  Lane (l32, half) holds routed row l32 and, in
+  // elements 4 q + i, weight rows 32 c + 8 q + 4 half + i: four consecutive
+  // output columns of one row, as the stores want them.
   v16f acc[kSubN];
-#pragma unroll
-  for (int c = 0; c < kSubN; c++)
-#pragma unroll
-    for (int q = 0; q < 16; q++) acc[c][q] = 0.f;
 
   // activation ring: k-step g lives in slot g % 2 from its load (two k-steps
   // ahead) until it is multiplied
@@ -580,10 +585,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const v8i alo = __builtin_shufflevector(rl[A], rl[A], 0, 1, 2, 3, 4, 5, -1, -1);
 #pragma unroll
     for (int c = 0; c < kSubN; c++) {
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi, bq[c], acc[c], kFmtFp6E2M3, kFmtFp4E2M1, 0,
-                                                               rs[A], J, bsc[c]);
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo, bq[c], acc[c], kFmtFp6E2M3, kFmtFp4E2M1, 1,
-                                                               rs[A], J, bsc[c]);
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[c], ahi, acc[c], kFmtFp4E2M1, kFmtFp6E2M3, J,
+                                                               bsc[c], 0, rs[A]);
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[c], alo, acc[c], kFmtFp4E2M1, kFmtFp6E2M3, J,
+                                                               bsc[c], 1, rs[A]);
       if (next) read_b(sb, c, (J + 1) & 3);
       // the read stays here, 7 sub-tiles ahead of its MFMAs
       pipeline_fence();
@@ -663,6 +668,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     load_b(0, 1);
     store_b(sB0, sS0, 1);
     lds_barrier();
+    if (V) {
+      // the sums start at the bias of their columns (bias_lds is complete)
+#pragma unroll
+      for (int c = 0; c < kSubN; c++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const f32x4_t b = *reinterpret_cast<const f32x4_t*>(bias_lds + 32 * c + 8 * q + 4 * half);
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[c][4 * q + i] = b[i];
+        }
+    }
     int s = 0;
 #pragma unroll
     for (; s + 2 < NS; s += 2) {
@@ -677,138 +693,116 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   else
     pipeline(std::false_type{});
 
-  // ---- epilogue: bias and scatter to the routed rows (rows_lds and
-  // bias_lds were written before the first barrier).  All LDS reads first (the
-  // 8 bias values, the wave's 16 routed rows as four 16-byte reads), then the
-  // stores.
+  // ---- epilogue: scatter to the routed rows (bias included).  Each lane
+  // holds one routed row and, per accumulator, 4 runs of 4 consecutive
+  // columns.  The wide paths pass the wave's results through its own 8 KB of
+  // weight slot 0 (no wave reads that slot after the barrier that ends the
+  // next-to-last stage), so that each store instruction writes 4 rows x 256
+  // contiguous bytes: whole 128-byte lines, as HBM wants them (stores of 32
+  // bytes per row slow down every workgroup still streaming its operands).
   if (!valid) return;
-  float bias_v[kSubN];
+  uint8_t* st = sB0 + wave * 8192;  // [32 rows][16 pieces of 16 bytes], XOR-swizzled
+  auto st_at = [&](int row, int piece) { return st + row * 256 + ((piece ^ (row & 15)) << 4); };
+  // the rows a lane stores: row 4 i + lane / 16 of the wave's 32, piece lane % 16
+  auto out_rows = [&](int (&rr)[8]) {
 #pragma unroll
-  for (int c = 0; c < kSubN; c++) bias_v[c] = bias_lds[32 * c + l32];
+    for (int i = 0; i < 8; i++) rr[i] = rows_lds[wave * 32 + 4 * i + (lane >> 4)];  // -1 past the tile's rows
+  };
+  const int piece = lane & 15;
   if constexpr (SWIGLU) {
-    // Weight rows 2 i (gate) and 2 i + 1 (up) are the columns of lanes l32 =
-    // 2 i' and 2 i' + 1 (n0 and 32 c are even); the pair's activation column
-    // is n0 / 2 + 16 c + l32 / 2.  Of the tile rows a lane pair holds, the even
-    // lane evaluates those with j / 4 even, the odd lane those with j / 4 odd
-    // (row + 8): one swap within the pair gives each the value it lacks.  Half
-    // the rows (round rnd: j = 8 rnd .. 8 rnd + 7, tile rows 16 rnd .. 16 rnd +
-    // 15) at a time.
+    // Weight rows 2 i (gate) and 2 i + 1 (up) give activation column i; n0 and
+    // 8 q + 4 half are even, so elements (4 q, 4 q + 1) and (4 q + 2, 4 q + 3)
+    // are two pairs: activation columns a0 + 16 c + 4 q + 2 half + (0, 1).
     const int NA = N >> 1;
     const int a0 = n0 >> 1;
-    const bool odd = (l32 & 1) != 0;
-    // the activation of (c, j = 8 rnd + jj) on the even lane, (c, j + 4) on the odd
-    auto activation = [&](int c, int je) {
-      const float ve = acc[c][je] + bias_v[c];
-      const float vo = acc[c][je + 4] + bias_v[c];
-      const float rcv = pair_swap(odd ? ve : vo);
-      return odd ? swiglu(rcv, vo) : swiglu(ve, rcv);
+    auto pair_word = [&](int c, int q) {
+      const float g0 = acc[c][4 * q], u0 = acc[c][4 * q + 1];
+      const float g1 = acc[c][4 * q + 2], u1 = acc[c][4 * q + 3];
+      return f32_to_bf16_bits(swiglu(g0, u0)) | (f32_to_bf16_bits(swiglu(g1, u1)) << 16);
     };
-    const int lrow_own = 4 * half + (odd ? 8 : 0);  // + jj: this lane's row within the round
     if ((NA & 7) == 0 && (reinterpret_cast<uintptr_t>(act) & 15) == 0) {
-      // Staged as this wave's [16 rows][136] bf16 (128 columns + padding that
-      // puts the rows 4, 8 and 12 apart in different banks) in weight slot 0,
-      // which no wave reads after the barrier that ends the next-to-last
-      // stage; then stored as 16-byte pieces, 16 lanes per 256-byte row.
-      constexpr int kStride = 136;
-      uint16_t* st = reinterpret_cast<uint16_t*>(sB0 + wave * (16 * kStride * 2));
-      const int ch = lane & 15;
+      // per accumulator, lane half 0 assembles activation columns 16 c + 0 .. 7
+      // of its row and half 1 columns 16 c + 8 .. 15 (the partner lane, 32
+      // away, holds the other half of each run of 4): piece 2 c + half
 #pragma unroll
-      for (int rnd = 0; rnd < 2; rnd++) {
+      for (int c = 0; c < kSubN; c++) {
+        uint32_t w[4];
 #pragma unroll
-        for (int c = 0; c < kSubN; c++)
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++)
-            st[(lrow_own + jj) * kStride + 16 * c + (l32 >> 1)] =
-                (uint16_t)f32_to_bf16_bits(activation(c, 8 * rnd + jj));
-#pragma unroll
-        for (int it = 0; it < 4; it++) {
-          const int lrow = 4 * it + (lane >> 4);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + lrow * kStride + ch * 8);
-          const int r = rows_lds[wave * 32 + 16 * rnd + lrow];
-          const int col = a0 + ch * 8;  // NA % 8 == 0: a piece is wholly inside or outside
-          if (r >= 0 && col < NA)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(act + (size_t)r * NA + col));
-        }
+        for (int q = 0; q < 4; q++) w[q] = pair_word(c, q);
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)(half ? w[0] : w[2]), 32, 64);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)(half ? w[1] : w[3]), 32, 64);
+        *reinterpret_cast<u32x4_t*>(st_at(l32, 2 * c + half)) =
+            half ? u32x4_t{r0, w[2], r1, w[3]} : u32x4_t{w[0], r0, w[1], r1};
       }
+      int rr[8];
+      out_rows(rr);
+      asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
+      const int col = a0 + 8 * piece;  // NA % 8 == 0: a piece is wholly inside or outside
+      u32x4_t v[8];  // all reads first: one wait, not one per store
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = *reinterpret_cast<const u32x4_t*>(st_at(4 * i + (lane >> 4), piece));
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (rr[i] >= 0 && col < NA)
+          __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4_t*>(act + (size_t)rr[i] * NA + col));
       return;
     }
     // any other width: 2-byte stores from the registers
+    const int r = rows_lds[wave * 32 + l32];
+    if (r < 0) return;
 #pragma unroll
-    for (int rnd = 0; rnd < 2; rnd++)
-#pragma unroll
-      for (int c = 0; c < kSubN; c++)
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const float a = activation(c, 8 * rnd + jj);
-          const int r = rows_lds[wave * 32 + 16 * rnd + lrow_own + jj];
-          const int col = a0 + 16 * c + (l32 >> 1);
-          if (r >= 0 && col < NA) act[(size_t)r * NA + col] = (uint16_t)f32_to_bf16_bits(a);
-        }
-    return;
-  }
-  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-    // 16-byte stores: lane (l32 = 4 m + a, half) holds rows 8 q + 4 half + i
-    // (i = 0..3) of column 32 c + l32; a transpose within each lane quad gives
-    // it row 8 q + 4 half + a, columns 32 c + 4 m .. 4 m + 3, so one store
-    // instruction writes 8 rows x 128 contiguous bytes
-    const int a = lane & 3;
-    const int m4 = l32 & ~3;
-    const bool odd1 = (a & 1) != 0, odd2 = (a & 2) != 0;
-    int rq[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) rq[q] = rows_lds[wave * 32 + 8 * q + 4 * half + a];
-#pragma unroll
-    for (int c = 0; c < kSubN; c++) {
-      const int col = n0 + 32 * c + m4;  // a multiple of 4, so col < N covers all four
+    for (int c = 0; c < kSubN; c++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) v[i] = acc[c][4 * q + i] + bias_v[c];
-        // stage 1 (partner lane a ^ 1), then stage 2 (a ^ 2): an even lane
-        // takes the partner's low pair element into its high one, an odd lane
-        // the partner's high into its low
-#pragma unroll
-        for (int k2 = 0; k2 < 2; k2++) {
-          const int lo = 2 * k2, hi = 2 * k2 + 1;
-          const float snd = odd1 ? v[lo] : v[hi];
-          const float rcv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(snd), 0xB1, 0xF, 0xF, true));
-          if (odd1) v[lo] = rcv; else v[hi] = rcv;
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; k2++) {
-          const int lo = k2, hi = k2 + 2;
-          const float snd = odd2 ? v[lo] : v[hi];
-          const float rcv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(snd), 0x4E, 0xF, 0xF, true));
-          if (odd2) v[lo] = rcv; else v[hi] = rcv;
-        }
-        if (rq[q] >= 0 && col < N)
-          __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]},
-                                      reinterpret_cast<f32x4_t*>(out + (size_t)rq[q] * N + col));
+        const uint32_t w = pair_word(c, q);
+        const int col = a0 + 16 * c + 4 * q + 2 * half;
+        if (col < NA) act[(size_t)r * NA + col] = (uint16_t)(w & 0xffffu);
+        if (col + 1 < NA) act[(size_t)r * NA + col + 1] = (uint16_t)(w >> 16);
       }
+    return;
+  }
+  // streamed out: the outputs must not push the weights and activation tiles
+  // other workgroups still read out of the caches
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    // four rounds of 64 columns (accumulators 2 rnd, 2 rnd + 1): element run
+    // (c, q) of a lane is piece 8 (c - 2 rnd) + 2 q + half of its row; the
+    // columns are a multiple of 4, so col < N covers a whole piece
+    int rr[8];
+    out_rows(rr);
+#pragma unroll
+    for (int rnd = 0; rnd < 4; rnd++) {
+#pragma unroll
+      for (int cc = 0; cc < 2; cc++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int c = 2 * rnd + cc;
+          *reinterpret_cast<f32x4_t*>(st_at(l32, 8 * cc + 2 * q + half)) =
+              f32x4_t{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]};
+        }
+      asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
+      const int col = n0 + 64 * rnd + 4 * piece;
+      f32x4_t v[8];  // all reads first: one wait, not one per store
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = *reinterpret_cast<const f32x4_t*>(st_at(4 * i + (lane >> 4), piece));
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (rr[i] >= 0 && col < N)
+          __builtin_nontemporal_store(v[i], reinterpret_cast<f32x4_t*>(out + (size_t)rr[i] * N + col));
     }
     return;
   }
-  // lane rows 8 q + 4 half + (0..3) of the wave's 32
-  int rr[16];
+  // any other width or alignment: 4-byte stores from the registers
+  const int r = rows_lds[wave * 32 + l32];
+  if (r < 0) return;
+  float* orow = out + (size_t)r * N + n0 + 4 * half;
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int4 v = *reinterpret_cast<const int4*>(rows_lds + wave * 32 + 8 * q + 4 * half);
-    rr[4 * q] = v.x; rr[4 * q + 1] = v.y; rr[4 * q + 2] = v.z; rr[4 * q + 3] = v.w;
-  }
-  float* orow[16];
+  for (int c = 0; c < kSubN; c++)
 #pragma unroll
-  for (int j = 0; j < 16; j++) orow[j] = out + (size_t)max(rr[j], 0) * N + n0 + l32;
+    for (int q = 0; q < 4; q++)
 #pragma unroll
-  for (int c = 0; c < kSubN; c++) {
-    if (n0 + 32 * c + l32 >= N) continue;
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      // streamed out: the outputs must not push the weights and activation
-      // tiles other workgroups still read out of the caches
-      if (rr[j] >= 0) __builtin_nontemporal_store(acc[c][j] + bias_v[c], orow[j] + 32 * c);
-    }
-  }
+      for (int i = 0; i < 4; i++)
+        if (n0 + 32 * c + 8 * q + 4 * half + i < N) __builtin_nontemporal_store(acc[c][4 * q + i], orow + 32 * c + 8 * q + i);
 }
 
 struct GemmLayout {
