@@ -12,14 +12,16 @@
 // (blockIdx.y = the g-th such expert, found with one ballot over the expert
 // offsets) and row blocks of WAVES * 16 consecutive weight rows, 16 per wave:
 // blocks blockIdx.x, blockIdx.x + gridDim.x, ... streamed back to back with
-// the token rows staged once.  Lane l of a
-// wave streams weight row (16-row base + l % 16), MX block 4 * i + l / 16 for
-// i = 0, 1, ...: one 128-bit load per lane per i, and every load of the wave
-// covers 16 rows x 64 contiguous bytes.  The loads run a two-stage pipeline
-// over chunks of NCH 128-element K groups (the next chunk is in flight while
-// the current one is multiplied), and the first chunk is issued before the
-// expert's token rows (up to MT per pass) are staged in LDS as bf16; the four
-// MFMAs of a load accumulate into four independent accumulators.
+// the token rows staged once.  A wave streams
+// its 16 weight rows in squares of 16 rows x 8 MX blocks: each 128-bit load
+// of the wave covers 8 rows x 128 contiguous bytes (whole lines), and the
+// square then passes through the wave's LDS so that lane l holds row l % 16,
+// block 4 g + l / 16 of K group g, as the MFMA wants it.  The loads run a
+// pipeline of two or three chunks of NCH 128-element K groups (the next
+// chunks are in flight while the current one is multiplied), and the first
+// chunks are issued before the expert's token rows (up to MT per pass) are
+// staged in LDS as bf16; the four MFMAs of a group accumulate into four
+// independent accumulators.
 //
 // Arithmetic.  Each 32-bit word of a block (8 codes) becomes 8 bf16 weights
 // through the gfx950 convert v_cvt_scalef32_pk_bf16_fp4 with the block's E8M0
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   const int NITC = (NIT + KS * NST * NCH - 1) / (KS * NST * NCH) * (KS * NST * NCH);
   const int XS = (NITC * 16 + 63) / 64 * 64 + 1;  // whole 64-entry DMAs, +1 spreads rows over banks
   static_assert(NST == 2 || NST == 3, "two or three chunks in flight");
-  static_assert(NST == 3 || NCH >= 1, "");
+  static_assert(NCH % 2 == 0, "whole squares of 16 rows x 8 blocks");
   const int R = T * k;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -152,16 +154,31 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   auto block_row0 = [&](int j) { return ((int)blockIdx.x + j * (int)gridDim.x) * RW * 16; };
   // this lane's weight row in block j (rows past N re-read row N - 1 and meet zero activations)
   auto lane_row = [&](int j) { return block_row0(j) + rw * 16 + (lane & 15); };
-  auto wrow_of = [&](int j) {
-    return reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(lane_row(j), N - 1)) * KB;
-  };
-  // step 1: the chunk's NCH groups; step 0: NCH reads of the same 16 bytes
-  // (a placeholder request, almost free)
-  auto load_chunk = [&](const uint4* wr, int c0, uint4 (&w)[NCH], int step = 1) {
-    // groups past K re-read the row's last block; they meet zero activations
+  // the wave's first weight row in block j
+  auto wrow_of = [&](int j) { return block_row0(j) + rw * 16; };
+  // A chunk is NCH / 2 squares of 16 rows x 8 blocks (2 K groups).  Load i
+  // covers half i % 2 of square i / 2, 8 rows x 128 contiguous bytes (whole
+  // lines; the MFMA's own layout, 16 rows x 64 bytes, streams markedly
+  // slower): lane l takes row 8 (i % 2) + l / 8, block l % 8 of the square.
+  // step 1: the chunk's groups; step 0: the first square again (a placeholder
+  // request, almost free).  Rows past N re-read row N - 1 and blocks past K
+  // the row's last block; they meet zero activations.
+  const uint4* wbase = reinterpret_cast<const uint4*>(blocks) + (size_t)e * N * KB;
+  auto load_chunk = [&](int wr, int c0, uint4 (&w)[NCH], int step = 1) {
 #pragma unroll
-    for (int i = 0; i < NCH; i++) w[i] = load_nt(wr + min((c0 + i * step) * 4 + kq, KB - 1));
+    for (int i = 0; i < NCH; i++) {
+      const int r = min(wr + 8 * (i & 1) + (lane >> 3), N - 1);
+      const int b = min((c0 + (i & ~1) * step) * 4 + (lane & 7), KB - 1);
+      w[i] = load_nt(wbase + (size_t)r * KB + b);
+    }
   };
+  // The MFMA wants lane l on row l % 16 and block 4 g + l / 16 of K group g:
+  // each K group of a square passes through the wave's own 1 KB of LDS, [16
+  // rows][4 pieces of 16 bytes] with piece b of row r at b ^ (r / 4 % 4), so
+  // that the writes (2 rows per 16 lanes) and the reads (16 rows, one piece)
+  // hit distinct banks.  A wave's LDS accesses complete in order.
+  uint8_t* trw = reinterpret_cast<uint8_t*>(xs + MT * XS) + wave * 1024;
+  auto tr_at = [&](int r, int b) { return trw + r * 64 + ((b ^ ((r >> 2) & 3)) << 4); };
 
   // ---- weight scales of block j: rows row0 .. row0 + RW * 16 - 1 (clamped to
   // N - 1), contiguous in memory: the aligned 16-byte blocks from the one
@@ -180,7 +197,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     // the same blocks through the (global) scales pointer, so loads stay global
     s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
   };
-  uint4* sc_lds = xs + MT * XS;
+  uint4* sc_lds = xs + MT * XS + WAVES * 64;
   auto sorted_rows_checked = [&](int i) {
     const int r = sorted_rows[i];
     return (r < 0 || r >= R) ? -1 : r;
@@ -238,7 +255,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     uint4 wa[NCH], wb[NCH], wc[NCH];
     const int g_first = kpart * (NITC / KS);  // this wave's first K group
     {
-      const uint4* wr0 = wrow_of(0);
+      const int wr0 = wrow_of(0);
       load_chunk(wr0, g_first, wa);
       load_chunk(wr0, g_first + NCH, wb);
       if (NST == 3) load_chunk(wr0, g_first + 2 * NCH, wc);
@@ -258,9 +275,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       const int row0 = block_row0(j);
       const int row = lane_row(j);
       const bool row_ok = row < N;
-      const uint4* wrow = wrow_of(j);
+      const int wrow = wrow_of(j);
       const bool more = j + 1 < nb;  // uniform
-      const uint4* wnext = wrow_of(min(j + 1, nb - 1));
+      const int wnext = wrow_of(min(j + 1, nb - 1));
       const int nstep = more ? 1 : 0;   // after the last block: placeholder requests
       const int nfirst = more ? g_first : 0;
       // the row's bias, loaded unconditionally (from a zero without bias: a
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       // LDS (the registers are needed for the weights in flight; the other waves
       // cover the LDS latency).
       constexpr bool kXPrefetch = OCC < 3;
-      auto compute_chunk = [&](int c0, const uint4 (&w)[NCH]) {
+      auto compute_chunk = [&](int c0, const uint4 (&wl)[NCH]) {
         uint32_t sv[NCH];
 #pragma unroll
         for (int i = 0; i < NCH; i++) sv[i] = srow[min((c0 + i) * 4 + kq, KB - 1)];
@@ -310,8 +327,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 #pragma unroll
             for (int d = 0; d < 4; d++) xv[d] = xread((c0 + i) * 16 + d);
           }
+          // group i is blocks 4 (i % 2) .. 4 (i % 2) + 3 of square i / 2: the
+          // lanes that loaded them write them, then every lane reads its own
+          if (((lane >> 2) & 1) == (i & 1)) {
+            *reinterpret_cast<uint4*>(tr_at(lane >> 3, lane & 3)) = wl[i & ~1];
+            *reinterpret_cast<uint4*>(tr_at(8 + (lane >> 3), lane & 3)) = wl[i | 1];
+          }
+          asm volatile("" ::: "memory");
+          const uint4 w = *reinterpret_cast<const uint4*>(tr_at(lane & 15, kq));
           const float sf = e8m0_to_float(sv[i]);
-          const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int d = 0; d < 4; d++) {
             const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 0);
@@ -666,8 +691,11 @@ size_t gemv_sc_entries(int WAVES, int KS, int K) {
   const size_t blocks = ((size_t)(WAVES / KS) * 16 * (K / 32) + 15) / 16 + 2;
   return (blocks + 63) / 64 * 64;
 }
+// LDS of one workgroup, in 16-byte entries: the staged token rows, each
+// wave's 1 KB transpose region, then the weight-scale rows of each of its
+// nbpw row blocks.
 size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K, int nbpw) {
-  return (gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)nbpw * gemv_sc_entries(WAVES, KS, K)) * 16;
+  return (gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * 64 + (size_t)nbpw * gemv_sc_entries(WAVES, KS, K)) * 16;
 }
 
 template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU>
@@ -681,7 +709,7 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
   const int groups = R < E ? R : E;
   constexpr int RW = WAVES / KS;
   const int nblk = (N + RW * 16 - 1) / (RW * 16);
-  const size_t xs = gemv_xs_entries(MT, NCH, NST, KS, K), sc = gemv_sc_entries(WAVES, KS, K);
+  const size_t xs = gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * 64, sc = gemv_sc_entries(WAVES, KS, K);
   const int nbpw_max = (int)((kGemvMaxDynLds / 16 - xs) / sc);  // >= 1: checked by the caller
   constexpr int kPerCu = (OCC * 4) / WAVES > 0 ? (OCC * 4) / WAVES : 1;
   int G = (256 * kPerCu + groups - 1) / groups;
@@ -747,7 +775,7 @@ hipError_t launch_gemv_any(const uint8_t* blocks, const uint8_t* scales, const u
   return launch_gemv_shape<MT, W, NCH, NST, KS, OCC, SWIGLU>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, \
                                                              offsets, sorted_rows, out, act, stream)
   const GemvShape g = gemv_shape(T, K);
-  if (g.mt == 1) MXFP4_GEMV_LAUNCH(1, 2, 4, 3, 2, 3);
+  if (g.mt == 1) MXFP4_GEMV_LAUNCH(1, 2, 4, 3, 2, 2);
   if (g.mt == 4) MXFP4_GEMV_LAUNCH(4, 4, 4, 3, 1, 2);
   if (g.nch == 4) MXFP4_GEMV_LAUNCH(16, 8, 4, 2, 1, 2);
   if (g.nch == 6) MXFP4_GEMV_LAUNCH(16, 8, 6, 2, 1, 2);
