@@ -198,10 +198,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
   };
   uint4* sc_lds = xs + MT * XS + WAVES * 64;
-  auto sorted_rows_checked = [&](int i) {
-    const int r = sorted_rows[i];
-    return (r < 0 || r >= R) ? -1 : r;
-  };
 
   for (int mb = m0; mb < m1; mb += MT) {
     const int mc = min(MT, m1 - mb);
@@ -213,18 +209,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     // repeats one: the same bytes to the same place).  Lanes past the data
     // read a clamped source into padding that is never read.
     bare_barrier<63>();  // the previous pass is done with the staged rows (its reads have returned)
-    // token row m's source: uniform per m, so these are scalar loads
+    // the pass's routed rows: one vector load (lane m, an unconditional read
+    // of a clamped index), then token row m's source as a uniform value (MT
+    // scalar loads behind branches would each wait for the one before)
     int src[MT];
+    {
+      int r = sorted_rows[mb + min(lane, mc - 1)];
+      if (lane >= mc || r < 0 || r >= R) r = -1;
+      const int s = r < 0 ? 0 : (x_per_slot ? r : r / k);  // row 0 stands in: masked when read
 #pragma unroll
-    for (int m = 0; m < MT; m++) {
-      int r = -1;
-      if (m < mc) {
-        r = sorted_rows[mb + m];
-        if (r < 0 || r >= R) r = -1;
-      }
-      src[m] = r < 0 ? 0 : (x_per_slot ? r : r / k);  // row 0 stands in: masked when read
+      for (int m = 0; m < MT; m++) src[m] = __builtin_amdgcn_readlane(s, m);
+      if (threadIdx.x < MT) rows_lds[threadIdx.x] = r;
     }
-    if (threadIdx.x < MT) rows_lds[threadIdx.x] = threadIdx.x < mc ? sorted_rows_checked(mb + threadIdx.x) : -1;
     {
       // scale blocks: 64 per DMA, instructions spread over the waves
       for (int j = 0; j < nb; j++) {
