@@ -23,7 +23,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for the per-tensor streams
-_T_BLOCKS, _T_SCALES, _T_BIAS, _T_X, _T_LOGITS, _T_IDS = range(6)
+_T_BLOCKS, _T_SCALES, _T_BIAS, _T_X, _T_LOGITS, _T_IDS, _T_ROUTER_W, _T_ROUTER_B = range(8)
 
 
 def _rng(seed: int, cfg: int, tensor: int) -> np.random.Generator:
@@ -158,3 +158,29 @@ def make_custom(E, N, K, T, k, *, x_per_slot=False, route="logits", seed=0, tag=
         combine = logits is not None
     return MoEProblem(f"custom_E{E}_N{N}_K{K}_T{T}_k{k}", E, N, K, T, k, blocks, scales, bias, x,
                       x_per_slot, logits, ids, combine)
+
+
+@dataclass
+class RouterProblem:
+    """Router inputs (src/experts.linnet block MixtureOfExperts, sub router: a
+    Linear from the hidden width H to the E experts).
+
+    x     u16 [T, H]  bf16 token rows
+    w     u16 [E, H]  bf16 weights, row e = expert e
+    bias  u16 [E]     bf16
+    """
+    T: int
+    H: int
+    E: int
+    x: np.ndarray
+    w: np.ndarray
+    bias: np.ndarray
+
+
+def make_router(T: int, H: int, E: int, *, seed: int = 0, tag: int = 98) -> RouterProblem:
+    """x ~ N(0, 1); w ~ N(0, 1 / H) per entry, so that the logits spread about
+    like the N(0, 1) logits of the routing workloads; bias ~ N(0, 0.02)."""
+    x = _normal_bf16(seed, tag, _T_X, (T, H))
+    w = f32_to_bf16_bits(_rng(seed, tag, _T_ROUTER_W).normal(0.0, 1.0 / np.sqrt(H), size=(E, H)).astype(np.float32))
+    b = f32_to_bf16_bits(_rng(seed, tag, _T_ROUTER_B).normal(0.0, 0.02, size=(E,)).astype(np.float32))
+    return RouterProblem(T, H, E, x, w, b)

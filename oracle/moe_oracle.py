@@ -25,6 +25,10 @@ without blocking, fusion or reordering:
 * combine: y[t, n] = sum over slots of gate[t, s] * out[t, s, n]
   (src/experts.linnet ``forward_topk``: the f32 sum over k and the down bias
   carried by the router weights);
+* router: logits[t, e] = bias[e] + sum_j x[t, j] * w[e, j], the Linear from
+  the hidden width to the experts (src/experts.linnet block
+  ``MixtureOfExperts``, ``sub router``; its output feeds ``ranks`` and
+  ``route``), exact in float64 for bf16 inputs up to the final rounding;
 * gated activation of the gate/up projection: even output rows are the gate,
   odd rows the multiplier; the gate is clamped from above at LIMIT = 7, the
   multiplier to [-7, 7], and the result is (up + 1) * gate *
@@ -155,6 +159,25 @@ def dense_route(logits_bits: np.ndarray, k: int) -> np.ndarray:
     floored = np.where(expert_ranks(l) < k, l, -1e30)
     z = np.exp(floored - floored.max(axis=1, keepdims=True))
     return z / z.sum(axis=1, keepdims=True)
+
+
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray, bias_bits: np.ndarray | None = None):
+    """Router logits before any rounding (``sub router``, a Linear from H to the
+    experts): z[t, e] = bias[e] + sum_j x[t, j] * w[e, j] in float64, with the
+    magnitude mag[t, e] = |bias[e]| + sum_j |x[t, j] * w[e, j]|.
+
+    x_bits [T, H] and w_bits [E, H] (row e = expert e) and bias_bits [E] are bf16
+    bit patterns.  Pinned by loops over tiny inputs, unit weight rows (the
+    logits are then columns of x plus the bias) and x = 0 (the bias)."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    z = x @ w.T
+    mag = np.abs(x) @ np.abs(w).T
+    if bias_bits is not None:
+        b = bf16_to_f64(bias_bits)
+        z = z + b[None, :]
+        mag = mag + np.abs(b)[None, :]
+    return z, mag
 
 
 def gates_for_ids(logits_bits: np.ndarray, ids: np.ndarray) -> np.ndarray:

@@ -428,6 +428,65 @@ def test_pins_catch_wrong_slope(monkeypatch):
         test_swiglu_gate_term_matches_torch_silu()
 
 
+# ----------------------------------------------------------------- router
+def _bf16(a):
+    return S.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def test_router_matches_loops():
+    """src/experts.linnet, sub router (a Linear from H to the experts): brute force
+    over (token, expert, j) with Python floats."""
+    rng = np.random.default_rng(5)
+    T, H, E = 3, 64, 5
+    x = _bf16(rng.standard_normal((T, H)))
+    w = _bf16(rng.standard_normal((E, H)) * 0.05)
+    b = _bf16(rng.standard_normal(E) * 0.1)
+    z, mag = O.router_logits(x, w, b)
+    assert z.shape == (T, E) and mag.shape == (T, E)
+    xf, wf, bf = O.bf16_to_f64(x), O.bf16_to_f64(w), O.bf16_to_f64(b)
+    for t in range(T):
+        for e in range(E):
+            acc, m = float(bf[e]), abs(float(bf[e]))
+            for j in range(H):
+                p_ = float(xf[t, j]) * float(wf[e, j])
+                acc += p_
+                m += abs(p_)
+            assert abs(z[t, e] - acc) <= 1e-12 * m
+            assert abs(mag[t, e] - m) <= 1e-12 * m
+
+
+def test_router_unit_rows_pick_columns():
+    """Expert e's weight row is the unit vector at column c_e: its logit is
+    x[t, c_e] + bias[e], exactly (a transposed operand or a shifted index fails)."""
+    rng = np.random.default_rng(6)
+    T, H, E = 4, 96, 6
+    cols = [0, 5, 31, 32, 63, 95]
+    w = np.zeros((E, H), np.float32)
+    w[np.arange(E), cols] = 1.0
+    x = _bf16(rng.standard_normal((T, H)))
+    b = _bf16(rng.standard_normal(E))
+    z, _ = O.router_logits(x, _bf16(w), b)
+    np.testing.assert_array_equal(z, O.bf16_to_f64(x)[:, cols] + O.bf16_to_f64(b)[None, :])
+
+
+def test_router_zero_input_is_bias():
+    rng = np.random.default_rng(7)
+    w = _bf16(rng.standard_normal((8, 64)))
+    b = _bf16(rng.standard_normal(8))
+    x = _bf16(np.zeros((2, 64)))
+    z, mag = O.router_logits(x, w, b)
+    np.testing.assert_array_equal(z, np.broadcast_to(O.bf16_to_f64(b), (2, 8)))
+    z0, _ = O.router_logits(x, w, None)
+    np.testing.assert_array_equal(z0, np.zeros((2, 8)))
+
+
+def test_pins_catch_router_without_bias(monkeypatch):
+    real = O.router_logits
+    monkeypatch.setattr(O, "router_logits", lambda x, w, b=None: real(x, w, None))
+    with pytest.raises(AssertionError):
+        test_router_zero_input_is_bias()
+
+
 # ----------------------------------------------------------------- inputs
 def test_bf16_rounding_is_nearest_even():
     v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], np.float32)
