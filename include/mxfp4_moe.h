@@ -112,6 +112,24 @@ int mxfp4_moe_route_group(const uint16_t* logits, const int32_t* ids_in, int T, 
                           int32_t* sorted_rows, int32_t* error_word, void* stream);
 
 /*
+ * Router logits of the MoE block: logits = x . w^T + bias, the Linear from the
+ * hidden width to the experts whose output the routing ranks.
+ * (src/experts.linnet block MixtureOfExperts, sub router: a Linear from H to
+ * the experts, weight [E, H] and bias [E] in bf16.)
+ *
+ *   x       [T, H] bf16, 16-byte aligned.  T >= 0, H a positive multiple of 32.
+ *   w       [E, H] bf16 (row e = expert e's weights), 16-byte aligned.
+ *           1 <= E <= MXFP4_MAX_EXPERTS.
+ *   bias    [E] bf16, or NULL for none.
+ *   logits  [T, E] bf16 out: the bf16 rounding (to nearest even) of
+ *           bias[e] + sum_j x[t, j] * w[e, j], with exact bf16 products summed
+ *           in fp32 in a fixed order (deterministic).
+ * One kernel launch; T = 0 returns MXFP4_OK and enqueues nothing.
+ */
+int mxfp4_moe_router(const uint16_t* x, const uint16_t* w, const uint16_t* bias, int T, int H, int E,
+                     uint16_t* logits, void* stream);
+
+/*
  * Dense router weights: every expert's probability, exactly zero outside each
  * token's top k -- the weights of the dense-routing form, which evaluates every
  * expert on every token (a validation mode of the sparse path: with all E

@@ -34,6 +34,7 @@ ENTRY_POINTS = (
     "mxfp4_moe_decode",
     "mxfp4_dequantize",
     "mxfp4_moe_dense_route",
+    "mxfp4_moe_router",
 )
 
 _lib_handle = None
@@ -79,6 +80,8 @@ def load_library():
     lib.mxfp4_dequantize.restype = i32
     lib.mxfp4_moe_dense_route.argtypes = [vp, i32, i32, i32, vp, vp]
     lib.mxfp4_moe_dense_route.restype = i32
+    lib.mxfp4_moe_router.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.mxfp4_moe_router.restype = i32
     _lib_handle = lib
     return lib
 
@@ -234,3 +237,11 @@ def mxfp4_moe_dense_route(logits, T: int, E: int, k: int, probs, stream=None):
                                    _ptr(probs, "probs", _F32, dev), _stream(stream, dev))
     _check(st)
 
+
+def mxfp4_moe_router(x, w, bias, T: int, H: int, E: int, logits, stream=None):
+    """Router logits (mxfp4_moe_router): logits [T,E] bf16 = x [T,H] . w [E,H]^T + bias [E]."""
+    lib = load_library()
+    dev = logits.device
+    st = lib.mxfp4_moe_router(_ptr(x, "x", _BF16, dev), _ptr(w, "w", _BF16, dev), _ptr(bias, "bias", _BF16, dev),
+                              int(T), int(H), int(E), _ptr(logits, "logits", _BF16, dev), _stream(stream, dev))
+    _check(st)

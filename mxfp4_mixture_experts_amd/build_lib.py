@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmxfp4_moe.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["route_group.hip", "expert_gemv.hip", "expert_gemm.hip", "combine.hip", "dequantize.hip", "capi.cpp"]
+SOURCES = ["route_group.hip", "expert_gemv.hip", "expert_gemm.hip", "combine.hip", "dequantize.hip", "router.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 

@@ -173,6 +173,22 @@ int mxfp4_moe_dense_route(const uint16_t* logits, int T, int E, int k, float* pr
   return MXFP4_OK;
 }
 
+int mxfp4_moe_router(const uint16_t* x, const uint16_t* w, const uint16_t* bias, int T, int H, int E,
+                     uint16_t* logits, void* stream) {
+  g_last_error[0] = '\0';
+  if (T < 0) return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be >= 0", T);
+  if (H < 32 || H % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "H = %d must be a positive multiple of 32", H);
+  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
+  if (T == 0) return MXFP4_OK;
+  if (!x || !w || !logits) return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(w)) return fail(MXFP4_ERR_INVALID_ARG, "x and w must be 16-byte aligned");
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_router(x, w, bias, T, H, E, logits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return MXFP4_OK;
+}
+
 size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x_per_slot, int path) {
   if (E < 1 || E > MXFP4_MAX_EXPERTS || N < 1 || T < 0 || k < 1 || K < 32 || K % 32 != 0) return (size_t)-1;
   if (path < MXFP4_PATH_AUTO || path > MXFP4_PATH_GEMM) return (size_t)-1;

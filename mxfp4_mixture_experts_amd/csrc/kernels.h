@@ -42,6 +42,10 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
 hipError_t launch_dequantize(const uint8_t* blocks, const uint8_t* scales, size_t nblocks, uint16_t* out,
                              hipStream_t stream);
 
+// router.hip: logits [T, E] bf16 = x [T, H] . w [E, H]^T + bias (fp32 sums, rounded once)
+hipError_t launch_router(const uint16_t* x, const uint16_t* w, const uint16_t* bias, int T, int H, int E,
+                         uint16_t* logits, hipStream_t stream);
+
 // combine.hip
 hipError_t launch_combine(const float* proj, const float* gates, int T, int k, int N, float* y,
                           hipStream_t stream);

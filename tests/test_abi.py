@@ -184,3 +184,18 @@ def test_dense_route_rejects_bad_arguments():
     assert lib.mxfp4_moe_dense_route(None, 4, 32, 4, p, None) == 1
     assert lib.mxfp4_moe_dense_route(None, 0, 32, 4, None, None) == 0
 
+
+
+def test_router_rejects_bad_arguments():
+    lib = B.load_library()
+    p = ctypes.c_void_p(16)
+    assert lib.mxfp4_moe_router(p, p, None, -1, 2880, 32, p, None) == 1
+    assert lib.mxfp4_moe_router(p, p, None, 4, 100, 32, p, None) == 1   # H % 32 != 0
+    assert lib.mxfp4_moe_router(p, p, None, 4, 0, 32, p, None) == 1
+    assert lib.mxfp4_moe_router(p, p, None, 4, 2880, 0, p, None) == 1
+    assert lib.mxfp4_moe_router(p, p, None, 4, 2880, 513, p, None) == 1
+    assert lib.mxfp4_moe_router(None, p, None, 4, 2880, 32, p, None) == 1
+    assert lib.mxfp4_moe_router(p, p, None, 4, 2880, 32, None, None) == 1
+    assert lib.mxfp4_moe_router(ctypes.c_void_p(8), p, None, 4, 2880, 32, p, None) == 1  # x misaligned
+    assert lib.mxfp4_last_error() != b""
+    assert lib.mxfp4_moe_router(None, None, None, 0, 2880, 32, None, None) == 0
