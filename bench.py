@@ -236,6 +236,92 @@ def measure_dequant(cfg_index, reps, rotate_bytes):
     return us, nbytes, copies
 
 
+def _graph_us(fn, reps):
+    """us per call of fn(i) over a graph of `reps` back-to-back calls (one untimed replay first)."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del g
+    return us
+
+
+def measure_router(T, reps, rotate_bytes, H=2880, E=32):
+    """mxfp4_moe_router at the gpt-oss-20b widths (H = 2880, E = 32): us per launch
+    and algorithmic bytes (x, w, bias, logits); inputs rotated over copies (at most
+    64, so a one-token router's inputs stay within the last-level cache)."""
+    import torch
+    from mxfp4_mixture_experts_amd import binding as B
+    from mxfp4_mixture_experts_amd import synthetic as S
+    r = S.make_router(T, H, E)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    x, w, b = bf(r.x), bf(r.w), bf(r.bias)
+    nbytes = (T * H + E * H + E + T * E) * 2
+    copies = max(1, min(64, math.ceil(rotate_bytes / ((T + E) * H * 2))))
+    ins = [(x, w)] + [(x.clone(), w.clone()) for _ in range(copies - 1)]
+    logits = torch.empty((T, E), dtype=torch.bfloat16, device="cuda")
+    us = _graph_us(lambda i: B.mxfp4_moe_router(ins[i % copies][0], ins[i % copies][1], b, T, H, E, logits), reps)
+    del ins
+    return us, nbytes, copies
+
+
+def measure_block_decode(reps, rotate_bytes):
+    """The whole MoE block for one gpt-oss-20b token, five launches: router ->
+    route_group -> gate/up through the gated activation -> down projection of the
+    activations -> combine.  Expert weights rotated over copies (>= rotate_bytes of
+    touched weights per rotation).  Returns (us per token, algorithmic bytes, copies)."""
+    import torch
+    from mxfp4_mixture_experts_amd import binding as B
+    from mxfp4_mixture_experts_amd import synthetic as S
+    from mxfp4_mixture_experts_amd.runner import DeviceProblem
+    H, E, k = 2880, 32, 4
+    r = S.make_router(1, H, E)
+    gu = S.make_config(1)
+    gu.x = r.x
+    dn = S.make_custom(E=E, N=H, K=2880, T=1, k=k, x_per_slot=True, route="logits", tag=97, combine=True)
+    d1, d2 = DeviceProblem(gu), DeviceProblem(dn)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    rw, rb = bf(r.w), bf(r.bias)
+    # the down projection reads the gate/up activations and the gate/up routing
+    d2.x = d1.act
+    d2.topk_ids, d2.gates, d2.offsets, d2.sorted_rows = d1.topk_ids, d1.gates, d1.offsets, d1.sorted_rows
+    acc_gu = algorithmic(gu, k, swiglu=True)
+    acc_dn = algorithmic(dn, k)
+    nbytes = (H + E * H + E + E) * 2 + acc_gu["proj"] + acc_gu["route"] + acc_dn["proj"] + acc_dn["combine"]
+    touched = acc_gu["weight_bytes"] + acc_dn["weight_bytes"]
+    copies = max(1, math.ceil(rotate_bytes / touched))
+    wg = [(d1.blocks, d1.scales)] + [(d1.blocks.clone(), d1.scales.clone()) for _ in range(copies - 1)]
+    wd = [(d2.blocks, d2.scales)] + [(d2.blocks.clone(), d2.scales.clone()) for _ in range(copies - 1)]
+
+    def step(i):
+        B.mxfp4_moe_router(d1.x, rw, rb, 1, H, E, d1.logits)
+        d1.route_group()
+        d1.expert_proj_swiglu(blocks=wg[i % copies][0], scales=wg[i % copies][1])
+        d2.expert_proj(blocks=wd[i % copies][0], scales=wd[i % copies][1])
+        d2.combine()
+
+    us = _graph_us(step, reps)
+    del wg, wd
+    return us, nbytes, copies
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(cfg_index, reps=2):
     """The oracle as it stands, on this host, one BLAS thread, on the whole headline workload."""
@@ -374,6 +460,29 @@ def main():
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_launch": nbytes,
+            "weight_copies_rotated": copies,
+        })
+        # the router GEMV (mxfp4_moe_router) for one token and for a prompt
+        for T, reps in ((1, 200), (4096, 40)):
+            us, nbytes, copies = measure_router(T, reps, args.rotate_bytes)
+            sec.append({
+                "workload": f"gpt-oss-20b router: x bf16 [{T},2880] . w bf16 [32,2880]^T + bias -> bf16 logits "
+                            f"[{T},32] (mxfp4_moe_router)",
+                "kernel_us": round(us, 2),
+                "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": nbytes,
+                "input_copies_rotated": copies,
+            })
+        # the whole MoE block for one token, five launches
+        us, nbytes, copies = measure_block_decode(200, args.rotate_bytes)
+        sec.append({
+            "workload": "gpt-oss-20b MoE block, one token: router -> route_group -> gate_up + gated activation "
+                        "(bf16 [1,4,2880]) -> down [32,2880,90,16] -> combine [1,2880]",
+            "us_per_token": round(us, 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_token": nbytes,
             "weight_copies_rotated": copies,
         })
         line["secondary"] = sec
