@@ -100,7 +100,7 @@ class Workload:
         from mxfp4_mixture_experts_amd.runner import DeviceProblem
         self.torch = torch
         self.p = S.make_config(cfg_index)
-        self.fused = fused and fusable(self.p) and not swiglu
+        self.fused = fused and fusable(self.p)
         self.swiglu = swiglu
         self.dp = DeviceProblem(self.p, device="cuda:0", path=path)
         self.dp.route_group()            # the device's own routing decides which experts are touched
@@ -115,6 +115,9 @@ class Workload:
 
     def step(self, i, stream=None):
         b, s = self.weights[i % self.copies]
+        if self.fused and self.swiglu:
+            self.dp.decode_swiglu(stream, blocks=b, scales=s)
+            return
         if self.fused:
             self.dp.decode(stream, blocks=b, scales=s)
         elif self.swiglu:
@@ -129,7 +132,9 @@ class Workload:
     def proj_only(self, i, stream=None):
         """The dominant kernel alone: the projection (the single-launch decode when fused)."""
         b, s = self.weights[i % self.copies]
-        if self.fused:
+        if self.fused and self.swiglu:
+            self.dp.decode_swiglu(stream, blocks=b, scales=s)
+        elif self.fused:
             self.dp.decode(stream, blocks=b, scales=s)
         elif self.swiglu:
             self.dp.expert_proj_swiglu(stream, blocks=b, scales=s)
@@ -283,9 +288,9 @@ def measure_router(T, reps, rotate_bytes, H=2880, E=32):
 
 
 def measure_block_decode(reps, rotate_bytes):
-    """The whole MoE block for one gpt-oss-20b token, five launches: router ->
-    route_group -> gate/up through the gated activation -> down projection of the
-    activations -> combine.  Expert weights rotated over copies (>= rotate_bytes of
+    """The whole MoE block for one gpt-oss-20b token, four launches: router ->
+    routing + gate/up through the gated activation (mxfp4_moe_decode_swiglu) -> down
+    projection of the activations -> combine.  Expert weights rotated over copies (>= rotate_bytes of
     touched weights per rotation).  Returns (us per token, algorithmic bytes, copies)."""
     import torch
     from mxfp4_mixture_experts_amd import binding as B
@@ -312,8 +317,7 @@ def measure_block_decode(reps, rotate_bytes):
 
     def step(i):
         B.mxfp4_moe_router(d1.x, rw, rb, 1, H, E, d1.logits)
-        d1.route_group()
-        d1.expert_proj_swiglu(blocks=wg[i % copies][0], scales=wg[i % copies][1])
+        d1.decode_swiglu(blocks=wg[i % copies][0], scales=wg[i % copies][1])
         d2.expert_proj(blocks=wd[i % copies][0], scales=wd[i % copies][1])
         d2.combine()
 
@@ -432,21 +436,24 @@ def main():
         sec = []
         # the other model-size workloads, then the two gate_up workloads through
         # the fused gated activation (bf16 [T, k, N / 2], the down projection's input)
+        # (the one-token one as a single launch, mxfp4_moe_decode_swiglu)
         for cfg, steps, swiglu in ((2, 100, False), (3, 20, False), (4, 40, False), (1, 200, True), (3, 20, True)):
-            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu)
+            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu, fused=swiglu)
             a = r["acc"]
             t_step = r["ms_per_step"] * 1e-3
             t_proj = r["proj_us"] * 1e-6
             roof_t = max(a["flops"] / (MXFP4_PEAK_TFLOPS * 1e12), a["step"] / (HBM_PEAK_GBS * 1e9))
+            a_proj = a["proj"] + (a["route"] if r["fused"] else 0)   # the single launch routes too
             sec.append({
-                "workload": describe(r["p"], swiglu),
+                "workload": describe(r["p"], swiglu) + (" (routing + projection + activation in one launch)"
+                                                        if r["fused"] else ""),
                 "ms_per_step": round(r["ms_per_step"], 4),
                 "step_GBps": round(a["step"] / t_step / 1e9, 1),
                 "step_TFLOPs": round(a["flops"] / t_step / 1e12, 2),
                 "proj_us": round(r["proj_us"], 2),
-                "proj_GBps": round(a["proj"] / t_proj / 1e9, 1),
+                "proj_GBps": round(a_proj / t_proj / 1e9, 1),
                 "proj_TFLOPs": round(a["flops"] / t_proj / 1e12, 2),
-                "proj_frac_hbm": round(a["proj"] / t_proj / 1e9 / HBM_PEAK_GBS, 4),
+                "proj_frac_hbm": round(a_proj / t_proj / 1e9 / HBM_PEAK_GBS, 4),
                 "proj_frac_mxfp4_peak": round(a["flops"] / t_proj / 1e12 / MXFP4_PEAK_TFLOPS, 4),
                 "step_frac_combined_roofline": round(roof_t / t_step, 4),
                 "weight_copies_rotated": r["copies"],
@@ -474,11 +481,11 @@ def main():
                 "bytes_per_launch": nbytes,
                 "input_copies_rotated": copies,
             })
-        # the whole MoE block for one token, five launches
+        # the whole MoE block for one token, four launches
         us, nbytes, copies = measure_block_decode(200, args.rotate_bytes)
         sec.append({
-            "workload": "gpt-oss-20b MoE block, one token: router -> route_group -> gate_up + gated activation "
-                        "(bf16 [1,4,2880]) -> down [32,2880,90,16] -> combine [1,2880]",
+            "workload": "gpt-oss-20b MoE block, one token: router -> routing + gate_up + gated activation in one "
+                        "launch (bf16 [1,4,2880]) -> down [32,2880,90,16] -> combine [1,2880]",
             "us_per_token": round(us, 2),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -247,6 +247,25 @@ int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks
                      void* stream);
 
 /*
+ * One decode token through the gate/up projection and the gated activation in
+ * a single launch: mxfp4_moe_route_group (logits route) followed by
+ * mxfp4_expert_proj_swiglu for T = 1, with the same results bit for bit.
+ * (README "Dense routing"; src/experts.linnet fn forward_topk and fn activate:
+ * the gate/up product of the token's experts through the gpt-oss activation,
+ * even rows the gate and odd rows the multiplier.)
+ *
+ *   logits, E, k, blocks, scales, bias, K, topk_ids, gates, expert_offsets,
+ *   sorted_rows, error_word: as for mxfp4_moe_decode (one shared input row x
+ *           [1, K] bf16).  N even.
+ *   act     [1, k, N / 2] bf16 out, as mxfp4_expert_proj_swiglu writes it.
+ * One kernel launch, no workspace; the NaN-logit behaviour of mxfp4_moe_decode.
+ */
+int mxfp4_moe_decode_swiglu(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
+                            const uint16_t* bias, int N, int K, const uint16_t* x, int32_t* topk_ids, float* gates,
+                            int32_t* expert_offsets, int32_t* sorted_rows, int32_t* error_word, uint16_t* act,
+                            void* stream);
+
+/*
  * MXFP4 -> bf16 dequantization of a weight tensor, in its own layout.
  * (README "MXFP4": rows of 32-element blocks, 16 code bytes per block with the
  * even element in the low nibble, one E8M0 scale byte per block, a weight is

@@ -35,6 +35,7 @@ ENTRY_POINTS = (
     "mxfp4_dequantize",
     "mxfp4_moe_dense_route",
     "mxfp4_moe_router",
+    "mxfp4_moe_decode_swiglu",
 )
 
 _lib_handle = None
@@ -82,6 +83,8 @@ def load_library():
     lib.mxfp4_moe_dense_route.restype = i32
     lib.mxfp4_moe_router.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     lib.mxfp4_moe_router.restype = i32
+    lib.mxfp4_moe_decode_swiglu.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mxfp4_moe_decode_swiglu.restype = i32
     _lib_handle = lib
     return lib
 
@@ -210,6 +213,22 @@ def mxfp4_moe_decode(logits, E: int, k: int, blocks, scales, bias, N: int, K: in
         int(bool(x_per_slot)), _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
         _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
         _ptr(error_word, "error_word", _I32, dev), _ptr(out, "out", _F32, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_moe_decode_swiglu(logits, E: int, k: int, blocks, scales, bias, N: int, K: int, x, topk_ids, gates,
+                            expert_offsets, sorted_rows, act, error_word=None, stream=None):
+    """One decode token through the gate/up projection and the gated activation in one launch
+    (mxfp4_moe_decode_swiglu): act [1,k,N/2] bf16, with the same outputs as
+    mxfp4_moe_route_group followed by mxfp4_expert_proj_swiglu."""
+    lib = load_library()
+    dev = act.device
+    st = lib.mxfp4_moe_decode_swiglu(
+        _ptr(logits, "logits", _BF16, dev), int(E), int(k), _ptr(blocks, "blocks", _U8, dev),
+        _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(N), int(K), _ptr(x, "x", _BF16, dev),
+        _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(error_word, "error_word", _I32, dev), _ptr(act, "act", _BF16, dev), _stream(stream, dev))
     _check(st)
 
 

@@ -797,15 +797,21 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
                                 nullptr, stream);
 }
 
-// One token: routing, grouping and the projection in one launch.
+// One token: routing, grouping and the projection in one launch (act != NULL:
+// through the gated activation, bf16 [k, N / 2], instead of out).
 hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
                                 const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot,
                                 int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
-                                int32_t* error_word, float* out, hipStream_t stream) {
+                                int32_t* error_word, float* out, uint16_t* act, hipStream_t stream) {
   const dim3 grid((N + kT1Rows - 1) / kT1Rows, k);
   const FusedRoute fr{logits, topk_ids, gates, offsets, sorted_rows, error_word};
-  hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, false>), grid, dim3(kT1Waves * 64), 0, stream,
-                     blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr);
+  if (act) {
+    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, true>), grid, dim3(kT1Waves * 64), 0, stream,
+                       blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, nullptr, act, fr);
+  } else {
+    hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, false>), grid, dim3(kT1Waves * 64), 0, stream,
+                       blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr);
+  }
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
 hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
                                 const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot,
                                 int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
-                                int32_t* error_word, float* out, hipStream_t stream);
+                                int32_t* error_word, float* out, uint16_t* act, hipStream_t stream);
 
 // expert_gemm.hip
 size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);

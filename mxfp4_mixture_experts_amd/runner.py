@@ -80,6 +80,15 @@ class DeviceProblem:
                            self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.out, self.error_word,
                            stream)
 
+    def decode_swiglu(self, stream=None, blocks=None, scales=None):
+        """One token from logits through the gated activation: routing, grouping, the
+        gate/up projection and the activation in one launch."""
+        p = self.p
+        B.mxfp4_moe_decode_swiglu(self.logits, p.E, p.k, self.blocks if blocks is None else blocks,
+                                  self.scales if scales is None else scales, self.bias, p.N, p.K, self.x,
+                                  self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.act,
+                                  self.error_word, stream)
+
     def run_dense(self, stream=None):
         """The dense-routing form (a validation mode): every expert on every token,
         weighed by the dense router weights, through the same kernels.  Returns

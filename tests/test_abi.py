@@ -123,6 +123,23 @@ def test_moe_decode_rejects_bad_arguments(kw):
     assert lib.mxfp4_last_error() != b""
 
 
+def _decode_swiglu(lib, E=32, k=4, N=64, K=2880, ptr=16, logits=16, act=16):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    lg = ctypes.c_void_p(logits) if logits else None
+    a = ctypes.c_void_p(act) if act else None
+    return lib.mxfp4_moe_decode_swiglu(lg, E, k, p, p, None, N, K, p, p, None, p, p, None, a, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(E=0), dict(E=65), dict(k=0), dict(k=5, E=4), dict(N=0), dict(N=63), dict(K=100), dict(K=3104),
+    dict(ptr=0), dict(ptr=8), dict(logits=0), dict(act=0),
+])
+def test_moe_decode_swiglu_rejects_bad_arguments(kw):
+    lib = B.load_library()
+    assert _decode_swiglu(lib, **kw) == 1, kw
+    assert lib.mxfp4_last_error() != b""
+
+
 def test_expert_proj_t0_is_a_noop():
     lib = B.load_library()
     assert _proj(lib, T=0, ptr=0) == 0

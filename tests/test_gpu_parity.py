@@ -245,6 +245,51 @@ def test_fused_decode(case):
             np.testing.assert_array_equal(g[key], g2[key], err_msg=key)
 
 
+DECODE_SWIGLU_CASES = {
+    "gate_up_like": dict(E=32, N=200, K=2880, T=1, k=4, route="logits"),
+    "k3072": dict(E=16, N=100, K=3072, T=1, k=3, route="logits"),
+    "k32_top1_pair": dict(E=7, N=2, K=32, T=1, k=1, route="logits"),
+    "all_64_experts": dict(E=64, N=40, K=544, T=1, k=32, route="logits"),
+    "model_size": None,
+}
+
+
+@pytest.mark.parametrize("case", sorted(DECODE_SWIGLU_CASES))
+def test_fused_decode_swiglu(case):
+    """mxfp4_moe_decode_swiglu against the oracle, and bit for bit against
+    route_group + expert_proj_swiglu."""
+    kw = DECODE_SWIGLU_CASES[case]
+    p = S.make_config(1) if kw is None else S.make_custom(**kw)
+    p.name = case
+    _announce(f"decode swiglu {case}")
+    dp = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp.act.view(torch.int16).fill_(-1)
+    dp.decode_swiglu()
+    g = dp.results()
+    assert g["error_word"] == 0
+    if kw is None:
+        ids, gates = O.route_topk(p.logits, p.k)
+        offsets, rows_sorted = O.group_by_expert(ids, p.E)
+        check_routing(g, dict(ids=ids, gates=gates, offsets=offsets, sorted_rows=rows_sorted))
+        R, NA = p.T * p.k, p.N // 2
+        rng = np.random.default_rng(78)
+        rows, cols = _sample_pairs(rng, R, NA, 800)
+        vg, mg = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, rows, 2 * cols)
+        vu, mu = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, p.x_per_slot, ids, rows, 2 * cols + 1)
+        check_act(g["act"].reshape(R, NA)[rows, cols][:, None], np.stack([vg, vu], -1), np.stack([mg, mu], -1),
+                  f"{case} act")
+    else:
+        ref = O.run_problem(p)
+        check_routing(g, ref)
+        check_act(g["act"], ref["out"], ref["mag"], f"{case} act")
+    dp2 = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp2.route_group()
+    dp2.expert_proj_swiglu()
+    g2 = dp2.results()
+    for key in ("ids", "offsets", "sorted_rows", "gates", "act"):
+        np.testing.assert_array_equal(g[key], g2[key], err_msg=key)
+
+
 def test_fused_decode_model_size():
     """The gpt-oss-20b gate_up decode shape, sampled outputs against the oracle."""
     p = S.make_config(1)
