@@ -288,9 +288,9 @@ def measure_router(T, reps, rotate_bytes, H=2880, E=32):
 
 
 def measure_block_decode(reps, rotate_bytes):
-    """The whole MoE block for one gpt-oss-20b token, four launches: router ->
+    """The whole MoE block for one gpt-oss-20b token, three launches: router ->
     routing + gate/up through the gated activation (mxfp4_moe_decode_swiglu) -> down
-    projection of the activations -> combine.  Expert weights rotated over copies (>= rotate_bytes of
+    projection of the activations with the combine (mxfp4_expert_proj_combine).  Expert weights rotated over copies (>= rotate_bytes of
     touched weights per rotation).  Returns (us per token, algorithmic bytes, copies)."""
     import torch
     from mxfp4_mixture_experts_amd import binding as B
@@ -309,7 +309,9 @@ def measure_block_decode(reps, rotate_bytes):
     d2.topk_ids, d2.gates, d2.offsets, d2.sorted_rows = d1.topk_ids, d1.gates, d1.offsets, d1.sorted_rows
     acc_gu = algorithmic(gu, k, swiglu=True)
     acc_dn = algorithmic(dn, k)
-    nbytes = (H + E * H + E + E) * 2 + acc_gu["proj"] + acc_gu["route"] + acc_dn["proj"] + acc_dn["combine"]
+    # router; routing + gate/up + activation; down with the combine (no per-slot outputs written)
+    nbytes = ((H + E * H + E + E) * 2 + acc_gu["proj"] + acc_gu["route"]
+              + acc_dn["proj"] - k * H * 4 + k * 4 + H * 4)
     touched = acc_gu["weight_bytes"] + acc_dn["weight_bytes"]
     copies = max(1, math.ceil(rotate_bytes / touched))
     wg = [(d1.blocks, d1.scales)] + [(d1.blocks.clone(), d1.scales.clone()) for _ in range(copies - 1)]
@@ -318,8 +320,7 @@ def measure_block_decode(reps, rotate_bytes):
     def step(i):
         B.mxfp4_moe_router(d1.x, rw, rb, 1, H, E, d1.logits)
         d1.decode_swiglu(blocks=wg[i % copies][0], scales=wg[i % copies][1])
-        d2.expert_proj(blocks=wd[i % copies][0], scales=wd[i % copies][1])
-        d2.combine()
+        d2.proj_combine(blocks=wd[i % copies][0], scales=wd[i % copies][1], with_out=False)
 
     us = _graph_us(step, reps)
     del wg, wd
@@ -481,11 +482,11 @@ def main():
                 "bytes_per_launch": nbytes,
                 "input_copies_rotated": copies,
             })
-        # the whole MoE block for one token, four launches
+        # the whole MoE block for one token, three launches
         us, nbytes, copies = measure_block_decode(200, args.rotate_bytes)
         sec.append({
             "workload": "gpt-oss-20b MoE block, one token: router -> routing + gate_up + gated activation in one "
-                        "launch (bf16 [1,4,2880]) -> down [32,2880,90,16] -> combine [1,2880]",
+                        "launch (bf16 [1,4,2880]) -> down [32,2880,90,16] + combine [1,2880] in one launch",
             "us_per_token": round(us, 2),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

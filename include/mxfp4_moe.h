@@ -266,6 +266,31 @@ int mxfp4_moe_decode_swiglu(const uint16_t* logits, int E, int k, const uint8_t*
                             void* stream);
 
 /*
+ * One decode token's projection through all of its k experts and the
+ * gate-weighted combine, in one launch: mxfp4_expert_proj (T = 1, GEMV path)
+ * followed by moe_combine, with the same results bit for bit.
+ * (src/experts.linnet fn forward_topk: each slot's down product and the f32
+ * sum over k; fn down_bias_of: the down bias weighed by the router weights.)
+ *
+ *   blocks, scales, bias, E, N: as for mxfp4_expert_proj;
+ *           32 <= K <= MXFP4_DECODE_MAX_K, K % 32 == 0.
+ *   x       x_per_slot == 0: [1, K] bf16; x_per_slot != 0: [1, k, K] bf16 (the
+ *           down projection's per-slot inputs, e.g. mxfp4_moe_decode_swiglu's
+ *           activations).  16-byte aligned.
+ *   k       1 <= k <= min(E, MXFP4_MAX_TOPK).
+ *   topk_ids [1, k] i32, gates [1, k] f32: the token's routing, as
+ *           mxfp4_moe_route_group or mxfp4_moe_decode writes it.  A slot whose
+ *           id lies outside [0, E) contributes nothing.
+ *   out     [1, k, N] f32 out (each slot's projection, bias included), or NULL.
+ *   y       [1, N] f32 out: y[n] = sum over slots, in slot order, of
+ *           gates[s] * out[s, n] (one fused multiply-add per slot).
+ * One kernel launch, no workspace.
+ */
+int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
+                              int K, const uint16_t* x, int x_per_slot, int k, const int32_t* topk_ids,
+                              const float* gates, float* out, float* y, void* stream);
+
+/*
  * MXFP4 -> bf16 dequantization of a weight tensor, in its own layout.
  * (README "MXFP4": rows of 32-element blocks, 16 code bytes per block with the
  * even element in the low nibble, one E8M0 scale byte per block, a weight is

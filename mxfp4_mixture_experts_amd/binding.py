@@ -36,6 +36,7 @@ ENTRY_POINTS = (
     "mxfp4_moe_dense_route",
     "mxfp4_moe_router",
     "mxfp4_moe_decode_swiglu",
+    "mxfp4_expert_proj_combine",
 )
 
 _lib_handle = None
@@ -85,6 +86,8 @@ def load_library():
     lib.mxfp4_moe_router.restype = i32
     lib.mxfp4_moe_decode_swiglu.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mxfp4_moe_decode_swiglu.restype = i32
+    lib.mxfp4_expert_proj_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.mxfp4_expert_proj_combine.restype = i32
     _lib_handle = lib
     return lib
 
@@ -263,4 +266,18 @@ def mxfp4_moe_router(x, w, bias, T: int, H: int, E: int, logits, stream=None):
     dev = logits.device
     st = lib.mxfp4_moe_router(_ptr(x, "x", _BF16, dev), _ptr(w, "w", _BF16, dev), _ptr(bias, "bias", _BF16, dev),
                               int(T), int(H), int(E), _ptr(logits, "logits", _BF16, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_expert_proj_combine(blocks, scales, bias, E: int, N: int, K: int, x, x_per_slot: bool, k: int, topk_ids,
+                              gates, y, out=None, stream=None):
+    """One token through its k experts and the gate-weighted combine in one launch
+    (mxfp4_expert_proj_combine): y [1,N] f32 (and out [1,k,N] f32 if given), equal to
+    mxfp4_expert_proj followed by moe_combine."""
+    lib = load_library()
+    dev = y.device
+    st = lib.mxfp4_expert_proj_combine(
+        _ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(E),
+        int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(k), _ptr(topk_ids, "topk_ids", _I32, dev),
+        _ptr(gates, "gates", _F32, dev), _ptr(out, "out", _F32, dev), _ptr(y, "y", _F32, dev), _stream(stream, dev))
     _check(st)

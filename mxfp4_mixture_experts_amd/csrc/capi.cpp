@@ -267,6 +267,27 @@ int mxfp4_moe_decode_swiglu(const uint16_t* logits, int E, int k, const uint8_t*
                          sorted_rows, error_word, nullptr, act, stream);
 }
 
+int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
+                              int K, const uint16_t* x, int x_per_slot, int k, const int32_t* topk_ids,
+                              const float* gates, float* out, float* y, void* stream) {
+  g_last_error[0] = '\0';
+  if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
+  if (k < 1 || k > E || k > MXFP4_MAX_TOPK)
+    return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, min(E = %d, %d)]", k, E, MXFP4_MAX_TOPK);
+  if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+  if (K < 32 || K % 32 != 0 || K > MXFP4_DECODE_MAX_K)
+    return fail(MXFP4_ERR_INVALID_ARG, "K = %d must be a positive multiple of 32 up to %d", K, MXFP4_DECODE_MAX_K);
+  if ((long long)E * N > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "E * N overflows int32");
+  if (!blocks || !scales || !x || !topk_ids || !gates || !y) return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_proj_combine_t1(blocks, scales, bias, E, N, K, x, x_per_slot, k, topk_ids, gates, out,
+                                               y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "expert_proj_combine launch");
+  return MXFP4_OK;
+}
+
 int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, long long rows, int K, uint16_t* out,
                      void* stream) {
   g_last_error[0] = '\0';

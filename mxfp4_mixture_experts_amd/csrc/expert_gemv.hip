@@ -662,6 +662,149 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// one token: the projection of every slot and the gate-weighted combine
+// ---------------------------------------------------------------------------
+//
+// y[n] = sum over the token's slots s of gates[s] * (bias[e_s, n] + sum_j
+// W[e_s, n, j] * x_s[j]) (src/experts.linnet fn forward_topk: each slot's down
+// product and the f32 sum over k; fn down_bias_of: the down bias weighed by the
+// router).  A workgroup owns 4 * WPS weight rows and runs kT1Group slots of the
+// token over them at a time, WPS waves per slot, so the combine needs no other
+// workgroup's results.  Each slot's value is the row-streaming kernel's (the
+// same lane split, products, fixed lane sum and bias added last); the values
+// meet in LDS and the first slot's waves sum them in slot order with one fused
+// multiply-add each, as moe_combine does: y equals mxfp4_expert_proj followed
+// by moe_combine bit for bit.
+constexpr int kT1Group = 4;  // slots per round, WPS waves each
+
+template <int WPS>
+__global__ __launch_bounds__(WPS * kT1Group * 64) void expert_gemv_combine_t1_kernel(
+    const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
+    int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int k,
+    const int32_t* __restrict__ topk_ids, const float* __restrict__ gates, float* __restrict__ out,
+    float* __restrict__ y) {
+  using Sh = T1Shape<1, WPS>;
+  constexpr int kRows = Sh::kRows;
+  __shared__ uint4 xs1[kT1Group][kT1MaxKB * 4];   // the slots' input rows: 4 entries of 8 bf16 per block
+  __shared__ uint4 sc1[kT1Group][Sh::kScBlocks];   // each slot's expert's scale rows, from their aligned blocks
+  __shared__ float vals[kT1Group][kRows];          // each slot's projection of the workgroup's rows
+  const int KB = K >> 5;
+  const int K8 = K >> 3;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = wave / WPS;     // this wave's slot in the round
+  const int wq = wave % WPS;    // and its 4 rows among the slot's
+  const int j = lane & 15;      // block lane within a row
+  const int q4 = lane >> 4;     // row within the wave's 4
+  const int wg_row0 = blockIdx.x * kRows;
+  const int rows_wg = min(kRows, N - wg_row0);
+  const int rl = wq * 4 + q4;   // row within the workgroup
+  const int row = wg_row0 + rl;
+  // Never taken (K >= 32): arrays written only by LDS DMA look unwritten to the
+  // optimizer, which would then fold their loads away.
+  if (K < 0) {
+    xs1[0][threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    sc1[0][threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  const uintptr_t sbase = reinterpret_cast<uintptr_t>(scales);
+  float yacc = 0.f;  // the first slot's waves: the combine of their rows
+  for (int s0 = 0; s0 < k; s0 += kT1Group) {
+    const int ng = min(kT1Group, k - s0);
+    const bool active = g < ng;  // uniform
+    const int s = min(s0 + g, k - 1);
+    const int e_raw = topk_ids[s];
+    const bool ok = active && e_raw >= 0 && e_raw < E;  // a slot without a valid expert contributes nothing
+    const int e = ok ? e_raw : 0;
+    // the bias value first (see the row-streaming kernel: unconditional, through an opaque address)
+    uint32_t bias_bits;
+    {
+      const uint16_t* bp = bias ? bias + (size_t)e * N + min(row, N - 1) : &kZeroBf16;
+      asm volatile("" : "+v"(bp));
+      bias_bits = *(const __attribute__((address_space(1))) uint16_t*)(bp);
+    }
+    if (s0 > 0) bare_barrier<63>();  // the previous round is done with the staged rows and values
+    // ---- LDS DMAs of this wave's slot: the expert's scale blocks and the
+    // slot's input row (one shared row without x_per_slot, staged by slot 0's
+    // waves), spread over the slot's waves; older than every weight load
+    const uintptr_t s_first = sbase + ((size_t)e * N + wg_row0) * KB;
+    const uintptr_t s_blk0 = s_first & ~(uintptr_t)15;
+    const uintptr_t s_blk1 = (s_first + (size_t)rows_wg * KB - 1) & ~(uintptr_t)15;
+    const int n_sblk = (int)((s_blk1 - s_blk0) >> 4) + 1;
+    const int sc_base = (int)(s_first - s_blk0);
+    if (active) {
+      const uint4* s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
+      const int n_si = (n_sblk + 63) >> 6;
+      for (int ins = wq; ins < n_si; ins += WPS)
+        dma16(s_blocks + min(ins * 64 + lane, n_sblk - 1), reinterpret_cast<uint8_t*>(&sc1[g][ins * 64]));
+      if (x_per_slot || g == 0) {
+        const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)(x_per_slot ? s : 0) * K);
+        const int n_xi = (K8 + 63) >> 6;
+        for (int ins = wq; ins < n_xi; ins += WPS)
+          dma16(xrow + min(ins * 64 + lane, K8 - 1), reinterpret_cast<uint8_t*>(&xs1[g][ins * 64]));
+      }
+    }
+    asm volatile("" ::: "memory");  // the weight loads stay behind the DMAs
+    // ---- all of this lane's weights of the slot: kT1Ins loads (blocks past K
+    // re-read the row's last block, zeroed below)
+    uint4 w[kT1Ins];
+    const uint4* wrow = reinterpret_cast<const uint4*>(blocks) + ((size_t)e * N + min(row, N - 1)) * KB;
+#pragma unroll
+    for (int i = 0; i < kT1Ins; i++) w[i] = load_nt(wrow + min(16 * i + j, KB - 1));
+    asm volatile("" ::: "memory");
+    bare_barrier<kT1Ins>();  // every wave's DMAs have landed
+    {
+      // every wave multiplies, so that its loads are used where they were
+      // issued (a load used only under a branch is sunk into it, behind the
+      // barrier); a wave without a slot discards its result
+      const uint4* xg = xs1[x_per_slot ? g : 0];
+      const uint8_t* scb = reinterpret_cast<const uint8_t*>(sc1[g]) + sc_base;
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < kT1Ins; i++) {
+        const int b = 16 * i + j;
+        const int bc = min(b, KB - 1);
+        const uint32_t keep = b < KB ? 0xffffffffu : 0u;
+        const uint4 x0 = xg[bc * 4 + 0], x1 = xg[bc * 4 + 1], x2 = xg[bc * 4 + 2], x3 = xg[bc * 4 + 3];
+        const float sf = e8m0_to_float(scb[min(rl, rows_wg - 1) * KB + bc]);
+#define MXFP4_T1C_WORD(WD, XV)                                                                             \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 0),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).x), a, false);                     \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 1),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).y), a, false);                     \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 2),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).z), a, false);                     \
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 3),       \
+                                      __builtin_bit_cast(bf16x2_t, (XV).w), a, false);
+        MXFP4_T1C_WORD(w[i].x, x0)
+        MXFP4_T1C_WORD(w[i].y, x1)
+        MXFP4_T1C_WORD(w[i].z, x2)
+        MXFP4_T1C_WORD(w[i].w, x3)
+#undef MXFP4_T1C_WORD
+      }
+      // the 16 lanes of a row add their sums (fixed order), then the bias
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o, 64);
+      uint32_t bb = bias_bits;
+      asm volatile("" : "+v"(bb));
+      const float v = a + bf16_bits_to_f32(bb);
+      if (j == 0 && active) {
+        vals[g][rl] = v;
+        if (ok && out && row < N) out[(size_t)s * N + row] = v;
+      }
+    }
+    lds_barrier();  // every slot's values are in LDS
+    if (g == 0) {
+      for (int h = 0; h < ng; h++) {  // slot order
+        const int sh = s0 + h;
+        const int eh = topk_ids[sh];
+        if (eh >= 0 && eh < E) yacc = fmaf(gates[sh], vals[h][rl], yacc);
+      }
+    }
+  }
+  if (g == 0 && j == 0 && row < N) y[row] = yacc;
+}
+
 #ifndef MXFP4_T1_QUADS
 #define MXFP4_T1_QUADS 1
 #endif
@@ -795,6 +938,18 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
                                  act, stream);
   return launch_gemv_any<false>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out,
                                 nullptr, stream);
+}
+
+// One token: every slot's projection and the gate-weighted combine in one launch.
+hipError_t launch_proj_combine_t1(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
+                                  int K, const uint16_t* x, int x_per_slot, int k, const int32_t* topk_ids,
+                                  const float* gates, float* out, float* y, hipStream_t stream) {
+  constexpr int kWps = 2;  // 8 rows per workgroup, 8 waves: 360 workgroups at N = 2880
+  constexpr int kRows = T1Shape<1, kWps>::kRows;
+  hipLaunchKernelGGL(expert_gemv_combine_t1_kernel<kWps>, dim3((N + kRows - 1) / kRows),
+                     dim3(kWps * kT1Group * 64), 0, stream, blocks, scales, bias, E, N, K, x, x_per_slot, k, topk_ids,
+                     gates, out, y);
+  return hipGetLastError();
 }
 
 // One token: routing, grouping and the projection in one launch (act != NULL:

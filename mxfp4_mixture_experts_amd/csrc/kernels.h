@@ -30,6 +30,12 @@ hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint
                                 int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
                                 int32_t* error_word, float* out, uint16_t* act, hipStream_t stream);
 
+// one token, k slots (topk_ids [k], gates [k]): out [k, N] (or NULL) and the
+// gate-weighted combine y [N] in one launch
+hipError_t launch_proj_combine_t1(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
+                                  int K, const uint16_t* x, int x_per_slot, int k, const int32_t* topk_ids,
+                                  const float* gates, float* out, float* y, hipStream_t stream);
+
 // expert_gemm.hip
 size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,

@@ -89,6 +89,16 @@ class DeviceProblem:
                                   self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.act,
                                   self.error_word, stream)
 
+    def proj_combine(self, stream=None, blocks=None, scales=None, with_out=True):
+        """One token (T = 1): every slot's projection and the combine in one launch,
+        from the routing already in topk_ids and gates."""
+        p = self.p
+        assert p.T == 1 and self.y is not None
+        B.mxfp4_expert_proj_combine(self.blocks if blocks is None else blocks,
+                                    self.scales if scales is None else scales, self.bias, p.E, p.N, p.K, self.x,
+                                    p.x_per_slot, p.k, self.topk_ids, self.gates, self.y,
+                                    out=self.out if with_out else None, stream=stream)
+
     def run_dense(self, stream=None):
         """The dense-routing form (a validation mode): every expert on every token,
         weighed by the dense router weights, through the same kernels.  Returns

@@ -216,3 +216,18 @@ def test_router_rejects_bad_arguments():
     assert lib.mxfp4_moe_router(ctypes.c_void_p(8), p, None, 4, 2880, 32, p, None) == 1  # x misaligned
     assert lib.mxfp4_last_error() != b""
     assert lib.mxfp4_moe_router(None, None, None, 0, 2880, 32, None, None) == 0
+
+
+def test_proj_combine_rejects_bad_arguments():
+    lib = B.load_library()
+    p = ctypes.c_void_p(16)
+    f = lib.mxfp4_expert_proj_combine
+    assert f(p, p, None, 0, 2880, 2880, p, 1, 4, p, p, None, p, None) == 1
+    assert f(p, p, None, 32, 0, 2880, p, 1, 4, p, p, None, p, None) == 1
+    assert f(p, p, None, 32, 2880, 3104, p, 1, 4, p, p, None, p, None) == 1   # K > MXFP4_DECODE_MAX_K
+    assert f(p, p, None, 32, 2880, 100, p, 1, 4, p, p, None, p, None) == 1
+    assert f(p, p, None, 4, 2880, 2880, p, 1, 5, p, p, None, p, None) == 1    # k > E
+    assert f(p, p, None, 32, 2880, 2880, p, 1, 4, p, None, None, p, None) == 1  # no gates
+    assert f(p, p, None, 32, 2880, 2880, p, 1, 4, p, p, None, None, None) == 1  # no y
+    assert f(p, p, None, 32, 2880, 2880, ctypes.c_void_p(8), 1, 4, p, p, None, p, None) == 1  # x misaligned
+    assert lib.mxfp4_last_error() != b""

@@ -290,6 +290,43 @@ def test_fused_decode_swiglu(case):
         np.testing.assert_array_equal(g[key], g2[key], err_msg=key)
 
 
+PROJ_COMBINE_CASES = {
+    "down_like_per_slot": dict(E=32, N=136, K=2880, T=1, k=4, x_per_slot=True, route="logits"),
+    "shared_x_k3072": dict(E=16, N=100, K=3072, T=1, k=3, route="logits"),
+    "two_groups_k8": dict(E=16, N=70, K=544, T=1, k=8, x_per_slot=True, route="logits"),
+    "all_64_experts_k32": dict(E=64, N=40, K=544, T=1, k=32, x_per_slot=True, route="logits"),
+    "odd_n_k32": dict(E=5, N=33, K=32, T=1, k=2, route="logits"),
+    "down_model_size": dict(E=32, N=2880, K=2880, T=1, k=4, x_per_slot=True, route="logits"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PROJ_COMBINE_CASES))
+def test_proj_combine(case):
+    """mxfp4_expert_proj_combine against the oracle, and bit for bit against
+    expert_proj (GEMV) + moe_combine on the same routing."""
+    p = S.make_custom(**PROJ_COMBINE_CASES[case], combine=True)
+    p.name = case
+    _announce(f"proj+combine {case}")
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp.route_group()
+    dp.out.fill_(float("nan"))
+    dp.proj_combine()
+    g = dp.results()
+    check_routing(g, ref)
+    check_close(g["out"], ref["out"], ref["mag"], f"{case} out")
+    check_close(g["y"], ref["y"], ref["mag_y"], f"{case} y")
+    dp2 = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp2.run()
+    g2 = dp2.results()
+    np.testing.assert_array_equal(g["out"], g2["out"])
+    np.testing.assert_array_equal(g["y"], g2["y"])
+    # without the per-slot outputs: the same y
+    dp.y.fill_(float("nan"))
+    dp.proj_combine(with_out=False)
+    np.testing.assert_array_equal(dp.results()["y"], g2["y"])
+
+
 def test_fused_decode_model_size():
     """The gpt-oss-20b gate_up decode shape, sampled outputs against the oracle."""
     p = S.make_config(1)
