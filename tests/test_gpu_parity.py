@@ -327,6 +327,29 @@ def test_proj_combine(case):
     np.testing.assert_array_equal(dp.results()["y"], g2["y"])
 
 
+def test_proj_combine_skips_invalid_slots():
+    """A slot whose expert id lies outside [0, E) contributes nothing to y and
+    writes no output row; the others are combined in slot order."""
+    p = S.make_custom(E=8, N=72, K=256, T=1, k=4, x_per_slot=True, route="ids+logits", combine=True)
+    _announce("proj+combine with invalid slots")
+    ids = np.array([[3, -1, 6, 8]], dtype=np.int32)      # slots 1 and 3 invalid
+    gates = np.array([[0.5, 0.25, 0.125, 0.0625]], dtype=np.float32)
+    dp = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp.topk_ids.copy_(torch.from_numpy(ids))
+    dp.gates.copy_(torch.from_numpy(gates))
+    dp.out.fill_(float("nan"))
+    dp.proj_combine()
+    g = dp.results()
+    valid = [0, 2]
+    sub = np.asarray(ids)[:, valid]
+    x_valid = np.ascontiguousarray(p.x[:, valid])
+    ref, mag = O.expert_proj(p.blocks, p.scales, p.bias, x_valid, True, sub)
+    check_close(g["out"][:, valid], ref, mag, "valid slots")
+    assert np.all(np.isnan(g["out"][:, [1, 3]])), "an invalid slot's output row was written"
+    y_ref, y_mag = O.combine(ref, gates[:, valid].astype(np.float64), mag)
+    check_close(g["y"], y_ref, y_mag, "y over the valid slots")
+
+
 def test_fused_decode_model_size():
     """The gpt-oss-20b gate_up decode shape, sampled outputs against the oracle."""
     p = S.make_config(1)
