@@ -184,7 +184,8 @@ def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fu
     kreps = kernel_reps or steps
     g_proj = w.capture(w.proj_only, kreps)
     g_proj.replay()
-    ms_proj, _ = w.time_graph(g_proj)
+    # the kernel's own time: the median of five replays of the back-to-back launches
+    ms_proj = sorted(w.time_graph(g_proj)[0] for _ in range(5))[2]
     res = {
         "p": w.p, "acc": w.acc, "copies": w.copies, "steps": steps, "fused": w.fused,
         "ms_per_step": ms_total / steps, "wall_s": wall,

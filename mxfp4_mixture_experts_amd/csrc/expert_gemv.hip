@@ -461,6 +461,29 @@ struct FusedRoute {
   int32_t* error_word;
 };
 
+// One MXFP4 block's 32 products with 32 staged bf16 inputs, added to a: the
+// block's four code words w (8 codes each) become exact bf16 weights through
+// v_cvt_scalef32_pk_bf16_fp4 with the E8M0 factor sf, and v_dot2_f32_bf16
+// multiplies them by the inputs x0 .. x3 (8 each) and sums in fp32, in element
+// order.  keep = 0 zeroes the block (a block past K).
+__device__ __forceinline__ float block_dot(const uint4 w, uint32_t keep, float sf, const uint4 x0, const uint4 x1,
+                                           const uint4 x2, const uint4 x3, float a) {
+  const uint32_t wd[4] = {w.x & keep, w.y & keep, w.z & keep, w.w & keep};
+  const uint4 xv[4] = {x0, x1, x2, x3};
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 0),
+                                        __builtin_bit_cast(bf16x2_t, xv[d].x), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 1),
+                                        __builtin_bit_cast(bf16x2_t, xv[d].y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 2),
+                                        __builtin_bit_cast(bf16x2_t, xv[d].z), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], sf, 3),
+                                        __builtin_bit_cast(bf16x2_t, xv[d].w), a, false);
+  }
+  return a;
+}
+
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -614,22 +637,7 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
       for (int q = 0; q < QUADS; q++) {
         const int rl = (wave * QUADS + q) * 4 + q4;
         const float sf = e8m0_to_float(scb[min(rl, rows_wg - 1) * KB + bc]);
-        float a = acc[q];
-#define MXFP4_T1_WORD(WD, XV)                                                                              \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 0),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).x), a, false);                     \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 1),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).y), a, false);                     \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 2),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).z), a, false);                     \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 3),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).w), a, false);
-        MXFP4_T1_WORD(w[q][i].x, x0)
-        MXFP4_T1_WORD(w[q][i].y, x1)
-        MXFP4_T1_WORD(w[q][i].z, x2)
-        MXFP4_T1_WORD(w[q][i].w, x3)
-#undef MXFP4_T1_WORD
-        acc[q] = a;
+        acc[q] = block_dot(w[q][i], keep, sf, x0, x1, x2, x3, acc[q]);
       }
     }
     // ---- the 16 lanes of a row add their sums (fixed order: deterministic)
@@ -767,20 +775,7 @@ __global__ __launch_bounds__(WPS * kT1Group * 64) void expert_gemv_combine_t1_ke
         const uint32_t keep = b < KB ? 0xffffffffu : 0u;
         const uint4 x0 = xg[bc * 4 + 0], x1 = xg[bc * 4 + 1], x2 = xg[bc * 4 + 2], x3 = xg[bc * 4 + 3];
         const float sf = e8m0_to_float(scb[min(rl, rows_wg - 1) * KB + bc]);
-#define MXFP4_T1C_WORD(WD, XV)                                                                             \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 0),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).x), a, false);                     \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 1),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).y), a, false);                     \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 2),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).z), a, false);                     \
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((WD) & keep, sf, 3),       \
-                                      __builtin_bit_cast(bf16x2_t, (XV).w), a, false);
-        MXFP4_T1C_WORD(w[i].x, x0)
-        MXFP4_T1C_WORD(w[i].y, x1)
-        MXFP4_T1C_WORD(w[i].z, x2)
-        MXFP4_T1C_WORD(w[i].w, x3)
-#undef MXFP4_T1C_WORD
+        a = block_dot(w[i], keep, sf, x0, x1, x2, x3, a);
       }
       // the 16 lanes of a row add their sums (fixed order), then the bias
 #pragma unroll
