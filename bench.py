@@ -179,7 +179,8 @@ def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fu
         w.step(i)
     w.torch.cuda.synchronize()
     g_steps = w.capture(w.step, steps)
-    g_steps.replay()                      # untimed: first replay of the instantiated graph
+    for _ in range(3):                    # untimed: the instantiated graph's first replays (clocks settle)
+        g_steps.replay()
     ms_total, wall = w.time_graph(g_steps)
     kreps = kernel_reps or steps
     g_proj = w.capture(w.proj_only, kreps)
