@@ -52,7 +52,7 @@ typedef enum {
 } mxfp4_status;
 
 /* Bits of the optional device error word written by mxfp4_moe_route_group. */
-#define MXFP4_ROUTE_ERR_ID_RANGE 1  /* a given expert id was outside [0, E) (or no expert could be chosen) */
+#define MXFP4_ROUTE_ERR_ID_RANGE 1  /* a given expert id was outside [0, E), or a token's logits held a NaN */
 #define MXFP4_ROUTE_ERR_ID_DUP 2    /* a token's given expert ids were not distinct */
 
 /* Library limits. */
@@ -84,7 +84,10 @@ const char* mxfp4_last_error(void);
  *               - ids_in == NULL: topk_ids[t, s] = the expert of rank s among
  *                 token t's logits, where an expert's rank counts the experts
  *                 with a larger logit or an equal logit and a lower index
- *                 (logits must be finite; logits is then required).
+ *                 (logits is then required).  A NaN logit compares false
+ *                 both ways, so it ranks 0 and more than k experts qualify:
+ *                 such a token gets -1 in all k slots (its rows are left out
+ *                 of the grouping), no gates, and MXFP4_ROUTE_ERR_ID_RANGE.
  *               - ids_in != NULL: topk_ids = ids_in (slot order kept).  Ids must
  *                 lie in [0, E) and be distinct per token; violations set bits in
  *                 *error_word, an out-of-range id is written as -1 and its row is
@@ -237,9 +240,9 @@ int mxfp4_expert_proj_swiglu(const uint8_t* blocks, const uint8_t* scales, const
  *   sorted_rows [k] i32, error_word [1] i32 (or NULL): out, exactly as
  *           mxfp4_moe_route_group writes them for T = 1.
  *   out     [1, k, N] f32 out, as mxfp4_expert_proj writes it (GEMV path).
- * One kernel launch, no workspace.  A NaN logit can leave fewer than k
- * experts chosen: error_word then holds MXFP4_ROUTE_ERR_ID_RANGE and the
- * slots without an expert are not written.
+ * One kernel launch, no workspace.  A NaN logit: as mxfp4_moe_route_group
+ * (ids -1, zero offsets, no gates, sorted_rows untouched, error_word
+ * MXFP4_ROUTE_ERR_ID_RANGE) and out is not written.
  */
 int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
                      const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot, int32_t* topk_ids,

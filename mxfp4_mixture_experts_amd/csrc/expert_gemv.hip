@@ -517,32 +517,40 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
       const float lj = readlane_f(l, jj);
       rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
     }
+    // Finite logits choose exactly k lanes.  A NaN logit compares false both
+    // ways, so it ranks 0 and more than k lanes qualify: then, as in the
+    // routing kernel, every slot gets id -1, no row is grouped or projected
+    // and no gate is written.
     const bool chosen = lane < E && rank < k;
-    const uint64_t mask = __ballot(chosen);
-    const uint64_t mine = __ballot(chosen && lanes_below(mask) == (int)blockIdx.y);
+    const uint64_t all = __ballot(chosen);
+    const bool ok = __popcll(all) == k;
+    const uint64_t mask = ok ? all : 0ull;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
+      // the routing outputs: ids and gates by slot, offsets, grouped rows
+      if (ok) {
+        const float mx = readlane_f(l, __ffsll((long long)__ballot(chosen && rank == 0)) - 1);
+        const float num = chosen ? expf(l - mx) : 0.f;
+        const float sum = wave_sum(num);
+        if (chosen) {
+          fr.topk_ids[rank] = lane;
+          if (fr.gates) fr.gates[rank] = num / sum;
+          fr.sorted_rows[lanes_below(mask)] = rank;
+        }
+      } else if (lane < k) {
+        fr.topk_ids[lane] = -1;
+      }
+      if (lane < E) fr.offsets[lane] = __popcll(mask & ((1ull << lane) - 1));
+      if (lane == 0) {
+        fr.offsets[E] = __popcll(mask);
+        if (fr.error_word) *fr.error_word = ok ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
+      }
+    }
+    const uint64_t mine = __ballot(chosen && ok && lanes_below(mask) == (int)blockIdx.y);
     if (mine == 0) return;
     e = __builtin_amdgcn_readfirstlane(__ffsll((long long)mine) - 1);
     fused_row = __builtin_amdgcn_readlane(rank, e);
     m0 = 0;
     m1 = 1;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
-      // the routing outputs: ids and gates by slot, offsets, grouped rows
-      const float mx = readlane_f(l, __ffsll((long long)__ballot(chosen && rank == 0)) - 1);
-      const float num = chosen ? expf(l - mx) : 0.f;
-      const float sum = wave_sum(num);
-      if (chosen) {
-        fr.topk_ids[rank] = lane;
-        if (fr.gates) fr.gates[rank] = num / sum;
-        fr.sorted_rows[lanes_below(mask)] = rank;
-      }
-      if (lane < E) fr.offsets[lane] = __popcll(mask & ((1ull << lane) - 1));
-      if (lane == 0) {
-        // finite logits always give k experts; a NaN breaks the order
-        const int chosen_n = __popcll(mask);
-        fr.offsets[E] = chosen_n;
-        if (fr.error_word) *fr.error_word = chosen_n == k ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
-      }
-    }
   } else {
     if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
     e = __builtin_amdgcn_readfirstlane(e);

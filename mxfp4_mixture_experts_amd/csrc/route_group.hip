@@ -114,6 +114,20 @@ __device__ int route_ranked(const float (&l)[EC], int t, int E, int k, int lane,
       }
     }
   }
+  // Finite logits give exactly k experts of ranks 0 .. k - 1.  A NaN logit
+  // compares false both ways, so it ranks 0 beside the largest logit and more
+  // than k experts qualify: such a token gets id -1 in every slot (its rows are
+  // left out of the grouping) and no gates.
+  int seen = 0;
+#pragma unroll
+  for (int i = 0; i < EC; i++) seen += __popcll(__ballot(lane + 64 * i < E && rank[i] < k));
+  if (seen != k) {
+    if (lane < k) {
+      ids[lane] = -1;
+      if (idc) idc[lane] = -1;
+    }
+    return MXFP4_ROUTE_ERR_ID_RANGE;
+  }
   // slot s <- the expert of rank s; the largest kept logit has rank 0
   float mx = -INFINITY;
 #pragma unroll
@@ -144,11 +158,7 @@ __device__ int route_ranked(const float (&l)[EC], int t, int E, int k, int lane,
       if (e < E && rank[i] < k) gates[(size_t)t * k + rank[i]] = num[i] / sum;
     }
   }
-  // finite logits always give k experts; a NaN breaks the order
-  int seen = 0;
-#pragma unroll
-  for (int i = 0; i < EC; i++) seen += __popcll(__ballot(lane + 64 * i < E && rank[i] < k));
-  return seen == k ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
+  return 0;
 }
 
 // Route the NB tokens t0 + stride * b (b < NB; those past T are skipped) with
