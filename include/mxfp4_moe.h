@@ -53,6 +53,9 @@ typedef enum {
 
 /* Bits of the optional device error word written by mxfp4_moe_route_group. */
 #define MXFP4_ROUTE_ERR_ID_RANGE 1  /* a given expert id was outside [0, E), or a token's logits held a NaN */
+/* A token with either error keeps a defined result: gate 0 in every slot it
+ * could not route (all k slots for a NaN logit), so moe_combine gives that
+ * token's y the sum over its valid slots only (0 for a NaN logit). */
 #define MXFP4_ROUTE_ERR_ID_DUP 2    /* a token's given expert ids were not distinct */
 
 /* Library limits. */
@@ -65,7 +68,7 @@ typedef enum {
 /* Projection paths for mxfp4_expert_proj. */
 #define MXFP4_PATH_AUTO 0  /* GEMV while T * k <= 16 * min(E, T * k), grouped GEMM otherwise */
 #define MXFP4_PATH_GEMV 1  /* decode GEMV: 128-bit weight streaming, exact bf16 products, fp32 sums */
-#define MXFP4_PATH_GEMM 2  /* grouped GEMM on scaled-FP4 MFMA, activations as two MX-FP6 terms */
+#define MXFP4_PATH_GEMM 2  /* grouped GEMM on scaled-FP4 MFMA, activations as two to four MX-FP6 terms */
 
 /* Static text for a status code. */
 const char* mxfp4_status_string(int status);
@@ -84,19 +87,19 @@ const char* mxfp4_last_error(void);
  *               - ids_in == NULL: topk_ids[t, s] = the expert of rank s among
  *                 token t's logits, where an expert's rank counts the experts
  *                 with a larger logit or an equal logit and a lower index
- *                 (logits is then required).  A NaN logit compares false
- *                 both ways, so it ranks 0 and more than k experts qualify:
- *                 such a token gets -1 in all k slots (its rows are left out
- *                 of the grouping), no gates, and MXFP4_ROUTE_ERR_ID_RANGE.
+ *                 (logits is then required).  A NaN logit has no rank:
+ *                 such a token gets -1 and gate 0 in all k slots (its rows
+ *                 are left out of the grouping) and MXFP4_ROUTE_ERR_ID_RANGE.
  *               - ids_in != NULL: topk_ids = ids_in (slot order kept).  Ids must
  *                 lie in [0, E) and be distinct per token; violations set bits in
- *                 *error_word, an out-of-range id is written as -1 and its row is
- *                 left out of the grouping.
+ *                 *error_word, an out-of-range id is written as -1, its row is
+ *                 left out of the grouping and its gate is 0.
  *   T >= 0, 1 <= E <= MXFP4_MAX_EXPERTS, 1 <= k <= min(E, MXFP4_MAX_TOPK).
  *   topk_ids    [T, k] i32 out.
  *   gates       [T, k] f32 out, or NULL.  Written only when logits != NULL:
- *               gates[t, s] = exp(l_s - max) / sum_j exp(l_j - max) over the k
- *               logits at topk_ids[t, :] (fp32).
+ *               gates[t, s] = exp(l_s - max) / sum_j exp(l_j - max) over the
+ *               logits at the valid ids of topk_ids[t, :] (all k when the
+ *               routing succeeded), fp32; 0 for a slot whose id is -1.
  *   expert_offsets [E + 1] i32 out: exclusive prefix sum of the number of routed
  *               rows per expert; expert_offsets[E] = number of grouped rows
  *               (T * k when every id is valid).
@@ -105,7 +108,10 @@ const char* mxfp4_last_error(void);
  *               and ascending within an expert.  Entries past offsets[E] are
  *               not written.
  *   error_word  [1] i32 out, or NULL: overwritten with the MXFP4_ROUTE_ERR_* bits
- *               found (0 = none).
+ *               found (0 = none).  With more than 64 rows the routing launch
+ *               zeroes it and the grouping launch ORs in what each workgroup
+ *               finds in its own rows, so the word is final when the call's
+ *               work on the stream is done.
  * T * k <= 64: one kernel launch (a single workgroup); more rows: a routing
  * launch (one token per wave) and a grouping launch (ceil(T * k / 1024)
  * workgroups).  T = 0 writes zero offsets.
@@ -184,10 +190,17 @@ size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x
  *           weights (the E2M1 value times the E8M0 factor) by the bf16 inputs
  *           (bf16 dot products for one token with K <= 3072, the bf16 MFMA
  *           otherwise) and sums in fp32; it needs K <= 4096 when T > 4
- *           (its LDS staging).  GEMM (K <= MXFP4_GEMM_MAX_K) feeds the weights to the MFMA as stored and splits
- *           each bf16 activation block into two MX-FP6 (E2M3) terms; its error
- *           stays within 2e-3 * sum_j |W x| + 1e-5 per output for inputs like
- *           the model's (see the design notes).
+ *           (its LDS staging).  GEMM (K <= MXFP4_GEMM_MAX_K) feeds the weights
+ *           to the MFMA as stored and writes each bf16 activation block of 32
+ *           as a sum of MX-FP6 (E2M3) terms, one MFMA each: two for every block,
+ *           then a third and a fourth while some block's residual exceeds 1/64
+ *           of its mean magnitude without its largest element (outlier
+ *           channels, heavy tails), decided per 32 rows x 64 inputs.  Its
+ *           error is an approximation's, not a rounding's: it has
+ *           stayed within 2e-3 * sum_j |W x| + 1e-5 per output on every input
+ *           tested -- normal, log-normal (sigma <= 3), outlier channels up to
+ *           1e5 x the rest, the gated activation's outputs -- and the GEMV path
+ *           is the one with exact products for any input.
  *   workspace, workspace_bytes: device scratch of at least
  *           mxfp4_expert_proj_workspace_size(E, N, T, k, K, x_per_slot, path) bytes,
  *           16-byte aligned; may be NULL when that size is 0.  Calls that share
@@ -241,7 +254,7 @@ int mxfp4_expert_proj_swiglu(const uint8_t* blocks, const uint8_t* scales, const
  *           mxfp4_moe_route_group writes them for T = 1.
  *   out     [1, k, N] f32 out, as mxfp4_expert_proj writes it (GEMV path).
  * One kernel launch, no workspace.  A NaN logit: as mxfp4_moe_route_group
- * (ids -1, zero offsets, no gates, sorted_rows untouched, error_word
+ * (ids -1, gates 0, zero offsets, sorted_rows untouched, error_word
  * MXFP4_ROUTE_ERR_ID_RANGE) and out is not written.
  */
 int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
@@ -283,7 +296,8 @@ int mxfp4_moe_decode_swiglu(const uint16_t* logits, int E, int k, const uint8_t*
  *   k       1 <= k <= min(E, MXFP4_MAX_TOPK).
  *   topk_ids [1, k] i32, gates [1, k] f32: the token's routing, as
  *           mxfp4_moe_route_group or mxfp4_moe_decode writes it.  A slot whose
- *           id lies outside [0, E) contributes nothing.
+ *           id lies outside [0, E) is not projected and, like a slot with
+ *           gate 0, contributes nothing to y.
  *   out     [1, k, N] f32 out (each slot's projection, bias included), or NULL.
  *   y       [1, N] f32 out: y[n] = sum over slots, in slot order, of
  *           gates[s] * out[s, n] (one fused multiply-add per slot).
@@ -320,7 +334,9 @@ int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, long long row
  *
  *   proj  [T, k, N] f32, gates [T, k] f32, y [T, N] f32 out (overwritten):
  *   y[t, n] = sum_{s = 0}^{k-1} gates[t, s] * proj[t, s, n], accumulated in f32
- *   in slot order with fused multiply-adds.
+ *   in slot order with fused multiply-adds.  A slot with gate 0 adds nothing
+ *   whatever its proj row holds (the routing gives gate 0 to the slots it
+ *   could not route, whose rows the projection never writes).
  *   T >= 0, k >= 1, N >= 1.  T = 0 returns MXFP4_OK and enqueues nothing.
  */
 int moe_combine(const float* proj, const float* gates, int T, int k, int N, float* y, void* stream);

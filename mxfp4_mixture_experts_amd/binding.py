@@ -43,7 +43,10 @@ _lib_handle = None
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4_moe.so")
+    """The in-tree libmxfp4_moe.so, or the build named by MXFP4_MOE_LIB (the
+    host-sanitizer build of the same sources, for the ABI tests)."""
+    return os.environ.get("MXFP4_MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libmxfp4_moe.so")
 
 
 class MXFP4Error(RuntimeError):

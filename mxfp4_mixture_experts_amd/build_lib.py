@@ -65,5 +65,32 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB_PATH
 
 
+SANITIZED_LIB = os.path.join(BUILD_DIR, "libmxfp4_moe_hostsan.so")
+
+
+def build_host_sanitized() -> str:
+    """The same library with its host-side C ABI layer (capi.cpp) compiled by g++
+    under AddressSanitizer and UndefinedBehaviorSanitizer, linked with the kernel
+    objects of build().  For the ABI tests on a host without a GPU: they load it
+    (MXFP4_MOE_LIB) with the sanitizer runtimes preloaded.  Returns its path."""
+    objs = [os.path.join(BUILD_DIR, src + ".o") for src in SOURCES if src.endswith(".hip")]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    obj = os.path.join(BUILD_DIR, "capi.hostsan.o")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+    steps = [
+        ["g++", "-std=c++17", "-O1", "-g", "-fPIC", *san, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+         "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "capi.cpp"), "-o", obj],
+        ["g++", "-shared", *san, "-o", SANITIZED_LIB, obj, *objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+         f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"],
+    ]
+    for cmd in steps:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"sanitized build failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

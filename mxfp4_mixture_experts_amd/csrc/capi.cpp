@@ -4,8 +4,8 @@
 //
 // Every host-checkable precondition is tested before any HIP call, so a
 // rejected call enqueues nothing and the checks work on a host without a GPU
-// (the shape checks mirror the "checked before anything runs" convention of
-// the gpt-oss-20b files page, README "Loading").
+// (the gpt-oss-20b files page, README "Loading", validates names, shapes and
+// dtypes up front in the same way).
 
 #include "mxfp4_moe.h"
 

@@ -5,10 +5,13 @@
 // weights (it is already part of each projection row here).
 //
 // y[t, n] = sum_s gates[t, s] * proj[t, s, n], one fused multiply-add per slot
-// in slot order, so the result does not depend on the launch shape.  The
-// kernel is a pure HBM stream: each thread owns 4 consecutive columns of one
-// token (128-bit loads and stores), the k gates of the token are read once
-// per thread from the cache.
+// in slot order, so the result does not depend on the launch shape.  A slot
+// whose gate is 0 adds nothing, whatever its row holds: the routing gives gate
+// 0 to the slots it could not route, whose projection rows are never written.
+// (For a finite value v, fma(0, v, acc) = acc, so this changes no other sum.)
+// The kernel is a pure HBM stream: each thread owns 4 consecutive columns of
+// one token (128-bit loads and stores), the k gates of the token are read
+// once per thread from the cache.
 
 #include "kernels.h"
 #include "common.h"
@@ -30,7 +33,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < k; s++) {
       const float g = gates[t * k + s];
-      const float4 v = load_nt(p + (size_t)s * N4);
+      float4 v = load_nt(p + (size_t)s * N4);  // unconditional: no branch per load
+      if (g == 0.f) v = make_float4(0.f, 0.f, 0.f, 0.f);
       acc.x = fmaf(g, v.x, acc.x);
       acc.y = fmaf(g, v.y, acc.y);
       acc.z = fmaf(g, v.z, acc.z);
@@ -49,7 +53,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
     const size_t t = i / N;
     const size_t n = i - t * N;
     float acc = 0.f;
-    for (int s = 0; s < k; s++) acc = fmaf(gates[t * k + s], proj[(t * k + s) * N + n], acc);
+    for (int s = 0; s < k; s++) {
+      const float g = gates[t * k + s];
+      const float v = proj[(t * k + s) * N + n];
+      acc = fmaf(g, g == 0.f ? 0.f : v, acc);
+    }
     y[i] = acc;
   }
 }

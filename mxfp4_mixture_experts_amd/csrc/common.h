@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace mxfp4 {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -65,5 +67,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += __shfl_xor(v, 1, 64);
   return v;
 }
+
+// A kernel's dynamic-LDS limit raised once per device: the attribute belongs
+// to the device the call is made on, and launches from several host threads
+// may race to set it.
+class DynLdsLimit {
+ public:
+  DynLdsLimit(const void* func, int bytes) : func_(func), bytes_(bytes) {}
+  hipError_t ensure() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu_);
+    if (done_[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(func_, hipFuncAttributeMaxDynamicSharedMemorySize, bytes_);
+    if (e == hipSuccess) done_[dev] = true;
+    return e;
+  }
+
+ private:
+  static constexpr int kDevices = 64;
+  const void* func_;
+  int bytes_;
+  std::mutex mu_;
+  bool done_[kDevices] = {};
+};
 
 }  // namespace mxfp4

@@ -90,17 +90,17 @@ __host__ __device__ inline int stage_count(int K) {
 }
 
 // ---------------------------------------------------------------------------
-// activation quantization: bf16 block of 32 -> two MX-FP6 (E2M3) terms
+// activation quantization: bf16 block of 32 -> two to four MX-FP6 (E2M3) terms
 // ---------------------------------------------------------------------------
 
-// E8M0 exponent e for a block whose largest magnitude has bf16 bits `amax`:
-// the smallest e with amax * 2^-e <= 7.5.  Blocks below 2^-120 count as zero
-// (returns false).
-__device__ __forceinline__ bool block_exponent(uint32_t amax, int& e) {
-  const int ex = (int)(amax >> 7) - 127;          // amax is a positive bf16: exponent field
-  if (ex < -120) return false;
-  e = ex - 2 + (((amax & 0x7f) > 112) ? 1 : 0);   // 4 * (1 + m/128) > 7.5  <=>  m > 112
-  return true;
+// The E8M0 exponent of a term for a block whose largest magnitude has bf16
+// bits `amax` (nonzero): the smallest e with amax * 2^-e <= 7.5, raised to the
+// format's least exponent -127 for tinier blocks (their codes are then the
+// E2M3 subnormals of 2^-127, or zero).
+__device__ __forceinline__ int block_exponent(uint32_t amax) {
+  const int ex = (int)(amax >> 7) - 127;          // exponent field (a bf16 subnormal reads as -127)
+  const int e = ex - 2 + (((amax & 0x7f) > 112) ? 1 : 0);  // 4 * (1 + m/128) > 7.5  <=>  m > 112
+  return e < -127 ? -127 : e;
 }
 
 __device__ __forceinline__ uint32_t max_abs_bf16(const uint32_t (&w)[16]) {
@@ -110,32 +110,57 @@ __device__ __forceinline__ uint32_t max_abs_bf16(const uint32_t (&w)[16]) {
   return m;
 }
 
-// MX-FP6 hi + lo codes of one bf16 block of 32 (w: 16 words, element 2i in
-// the low half of word i) and their E8M0 scales (127 for a zero block).
-__device__ __forceinline__ void split_block(const uint32_t (&w)[16], v6i& hi, v6i& lo, uint32_t& sh, uint32_t& sl) {
-  hi = v6i{0, 0, 0, 0, 0, 0};
-  lo = v6i{0, 0, 0, 0, 0, 0};
-  sh = 127u;
-  sl = 127u;
-  int e;
-  if (!block_exponent(max_abs_bf16(w), e)) return;
-  sh = (uint32_t)(e + 127);
-  const float scale = __uint_as_float(sh << 23);
-  hi = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32_t, w), scale);
-  const v32f hv = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(hi, scale);
-  uint32_t r[16];
+// One MX-FP6 term of the bf16 block w (16 words, element 2i in the low half of
+// word i): its codes and E8M0 byte (127 for a zero block), and w replaced by
+// the residual w - term.  The convert rounds x / 2^e to the nearest E2M3 value
+// (ties to even); the residual is exact in fp32 and is itself a bf16 (rounding
+// a value of at most 8 significant bits to the E2M3 grid leaves a remainder of
+// at most 8), so it stays in the same form for the next term.  Exponents below
+// -100 run the convert on the block times 2^64 with the scale times 2^64 (the
+// same codes; the scale argument stays a normal fp32), in place.
+__device__ __forceinline__ void scale_block(uint32_t (&w)[16], float f) {
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    // residuals are exact in fp32 and fit bf16 exactly: keep the top halves
-    const float a = bf16_bits_to_f32(w[i] & 0xffffu) - hv[2 * i];
-    const float b = bf16_bits_to_f32(w[i] >> 16) - hv[2 * i + 1];
-    r[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    const float a = bf16_bits_to_f32(w[i] & 0xffffu) * f;
+    const float b = bf16_bits_to_f32(w[i] >> 16) * f;
+    w[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
   }
-  int e2;
-  if (block_exponent(max_abs_bf16(r), e2)) {
-    sl = (uint32_t)(e2 + 127);
-    lo = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32_t, r), __uint_as_float(sl << 23));
+}
+
+__device__ __forceinline__ void fp6_term(uint32_t (&w)[16], v6i& codes, uint32_t& byte) {
+  const uint32_t amax = max_abs_bf16(w);
+  codes = v6i{0, 0, 0, 0, 0, 0};
+  byte = 127u;
+  if (amax == 0) return;
+  const int e = block_exponent(amax);
+  byte = (uint32_t)(e + 127);
+  // The block is multiplied by 1 or 2^64 per lane, under a branch taken by the
+  // whole wave when any lane shifts (a per-lane select of the whole block
+  // would double the registers it holds); none does for ordinary inputs.
+  const bool shift = e < -100;
+  const bool any_shift = wave_ballot(shift) != 0;
+  if (any_shift) scale_block(w, shift ? 0x1p64f : 1.0f);
+  const float scale = __uint_as_float((uint32_t)(e + (shift ? 64 : 0) + 127) << 23);
+  codes = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32_t, w), scale);
+  const v32f dv = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, scale);
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float a = bf16_bits_to_f32(w[i] & 0xffffu) - dv[2 * i];
+    const float b = bf16_bits_to_f32(w[i] >> 16) - dv[2 * i + 1];
+    w[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
   }
+  if (any_shift) scale_block(w, shift ? 0x1p-64f : 1.0f);
+}
+
+// Whether a block whose residual after the terms so far has bf16 bits
+// `rmax` (largest magnitude) takes another term: when that residual exceeds
+// 1/64 of the block's mean magnitude without its largest element,
+// (sum |x| - max |x|) / 31.  Blocks of like magnitudes pass with two terms;
+// a block with an outlier channel, or heavy tails, takes three or four, so
+// that its small elements keep their own precision.
+constexpr float kExtraTermRatio = 31.0f * 64.0f;
+__device__ __forceinline__ bool needs_term(uint32_t rmax, float sum_rest) {
+  return bf16_bits_to_f32(rmax) * kExtraTermRatio > sum_rest;
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -190,19 +215,47 @@ __device__ __forceinline__ bool locate_row_tile(const int32_t* offsets, int E, i
   return false;
 }
 
-// Workgroup = one (row tile t, k-step g); wave = row sub-tile sub; lane (l32, h) = row 32 sub + l32, block 2 g + h.
-// Writes the register image of the MFMA B operand: per (t, sub, g) 3 KB =
+// Wave = row sub-tile sub of row tile t; lane (l32, h) = row 32 sub + l32, block 2 g + h of each k-step g.
+// A wave's 32 rows x 2 blocks are one unit (t, sub, g) of the GEMM: one MFMA
+// B operand per term.  Every block gets two terms (hi, lo); when any block of
+// the unit needs a third (needs_term), all of them get one, and likewise a
+// fourth.  Writes the register image of the MFMA B operand: per unit 3 KB =
 // hi bytes 0..15 [lane][16 B] | hi 16..23 [lane][8 B] | lo 0..15 [lane][16 B]
 // | lo 16..23 [lane][8 B], so that each 24-byte operand is one 16-byte and one
-// 8-byte load into its own six registers; and 64 u32 scales (hi | lo << 8).
-// The k-steps of a sub-tile are consecutive.  Rows past the expert's last routed row, and blocks
-// past K, are zero codes with scale 127.
+// 8-byte load into its own six registers; the third and fourth terms in the
+// same form in the unit's 3 KB extra record (written only when used); 64 u32
+// scale words (hi | lo << 8 | third << 16 | fourth << 24); and the unit's
+// count of extra terms (0, 1 or 2) in one byte.  The k-steps of a sub-tile are
+// consecutive.  Rows past the expert's last routed row, and blocks past K, are
+// zero codes with scale 127.
+__device__ __forceinline__ void put_term(uint8_t* rec, int lane, const v6i& c) {
+  *reinterpret_cast<uint4*>(rec + lane * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+  *reinterpret_cast<uint2*>(rec + 1024 + lane * 8) = make_uint2(c[4], c[5]);
+}
+
+// Workgroup blk = (row tile t, group of kQSteps k-steps): each wave locates
+// its rows once and walks the group's k-steps, the next block's load in
+// flight while the current one is split (loads are unconditional, from a
+// clamped address, and masked afterwards).
+constexpr int kQSteps = 8;
+
+__device__ __forceinline__ void load_block(const uint4* p, uint32_t (&w)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint4 v = p[i];
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+}
+
 __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restrict__ x, int x_per_slot, int k, int R,
                                               int E, int K, int NKP, const int32_t* __restrict__ offsets,
                                               const int32_t* __restrict__ sorted_rows, uint8_t* __restrict__ q,
-                                              uint32_t* __restrict__ s) {
-  const int t = blk / NKP;
-  const int g = blk - t * NKP;
+                                              uint8_t* __restrict__ qx, uint32_t* __restrict__ s,
+                                              uint8_t* __restrict__ qf) {
+  const int NQ = (NKP + kQSteps - 1) / kQSteps;
+  const int t = blk / NQ;
+  const int g0 = (blk - t * NQ) * kQSteps;
+  const int g1 = min(g0 + kQSteps, NKP);
   const int lane = threadIdx.x & 63;
   const int sub = threadIdx.x >> 6;
   int e, b, f, tb;
@@ -214,27 +267,48 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
     r = sorted_rows[p];
     if (r < 0 || r >= R) r = -1;
   }
-  const int kb = 2 * g + h;
-  v6i hi = {0, 0, 0, 0, 0, 0}, lo = {0, 0, 0, 0, 0, 0};
-  uint32_t sh = 127u, sl = 127u;
-  if (r >= 0 && kb < (K >> 5)) {
-    const int src = x_per_slot ? r : r / k;
-    const uint4* srcp = reinterpret_cast<const uint4*>(x + (size_t)src * K + (size_t)kb * 32);
+  const int KB = K >> 5;
+  const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)(r < 0 ? 0 : (x_per_slot ? r : r / k)) * K);
+  auto src = [&](int g) { return row + (size_t)min(2 * g + h, KB - 1) * 4; };  // 4 x 16 bytes per block
+  uint32_t wn[16];
+  load_block(src(g0), wn);
+  for (int g = g0; g < g1; g++) {
     uint32_t w[16];
+    const bool real = r >= 0 && 2 * g + h < KB;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint4 v = srcp[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    for (int i = 0; i < 16; i++) w[i] = real ? wn[i] : 0u;
+    load_block(src(min(g + 1, g1 - 1)), wn);
+    // the block's magnitude without its largest element, in element order
+    float sum = 0.f, mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float a = fabsf(bf16_bits_to_f32(w[i] & 0xffffu)), c = fabsf(bf16_bits_to_f32(w[i] >> 16));
+      sum += a;
+      sum += c;
+      mx = fmaxf(mx, fmaxf(a, c));
     }
-    split_block(w, hi, lo, sh, sl);
+    const float sum_rest = sum - mx;
+    // Terms 0 and 1 always; terms 2 and 3 when the unit needs them (unit-wide
+    // decisions by ballot: the extra MFMAs serve all 32 rows x 2 blocks).  Each
+    // term is stored as soon as it exists; one loop body (not unrolled), so
+    // that few registers are live.
+    const size_t unit = ((size_t)t * kWaves + sub) * NKP + g;
+    uint8_t* rec = q + unit * kAUnit;
+    uint8_t* xrec = qx + unit * kAUnit;
+    uint32_t bytes = 0x7f7f7f7fu;
+    int nterm = 0;
+#pragma unroll 1
+    for (; nterm < 4; nterm++) {
+      if (nterm >= 2 && __ballot(needs_term(max_abs_bf16(w), sum_rest)) == 0) break;
+      v6i c;
+      uint32_t byte;
+      fp6_term(w, c, byte);
+      put_term((nterm < 2 ? rec : xrec) + 1536 * (nterm & 1), lane, c);
+      bytes = (bytes & ~(0xffu << (8 * nterm))) | (byte << (8 * nterm));
+    }
+    s[unit * 64 + lane] = bytes;
+    if (lane == 0) qf[unit] = (uint8_t)(nterm - 2);
   }
-  const size_t unit = ((size_t)t * kWaves + sub) * NKP + g;
-  uint8_t* rec = q + unit * kAUnit;
-  *reinterpret_cast<uint4*>(rec + lane * 16) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  *reinterpret_cast<uint2*>(rec + 1024 + lane * 8) = make_uint2(hi[4], hi[5]);
-  *reinterpret_cast<uint4*>(rec + 1536 + lane * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  *reinterpret_cast<uint2*>(rec + 2560 + lane * 8) = make_uint2(lo[4], lo[5]);
-  s[unit * 64 + lane] = sh | (sl << 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -311,12 +385,13 @@ __global__ __launch_bounds__(kQThreads) void prepare_kernel(const uint8_t* __res
                                                             int R, int K, int NKP,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_rows,
-                                                            uint8_t* __restrict__ q, uint32_t* __restrict__ qs) {
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ qx,
+                                                            uint32_t* __restrict__ qs, uint8_t* __restrict__ qf) {
   extern __shared__ uint32_t panel[];  // (kBN * KB + 4) / 4 + 1 words
   if ((int)blockIdx.x < nrep)
     repack_panel(blockIdx.x, panel, scales, E, N, KB, NT, NS, wsc);
   else
-    quantize_tile(blockIdx.x - nrep, x, x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, q, qs);
+    quantize_tile(blockIdx.x - nrep, x, x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, q, qx, qs, qf);
 }
 
 // ---------------------------------------------------------------------------
@@ -448,9 +523,9 @@ __device__ __forceinline__ void pipeline_fence() {
 template <int NS_T, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void expert_gemm_kernel(
     const uint8_t* __restrict__ blocks, const uint32_t* __restrict__ wsc, const uint16_t* __restrict__ bias, int E,
-    int N, int K, const uint8_t* __restrict__ aq, const uint32_t* __restrict__ as, int T, int k,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
-    uint16_t* __restrict__ act) {
+    int N, int K, const uint8_t* __restrict__ aq, const uint8_t* __restrict__ aqx, const uint32_t* __restrict__ as,
+    const uint8_t* __restrict__ aqf, int T, int k, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_rows, float* __restrict__ out, uint16_t* __restrict__ act) {
   // weight stages, double-buffered: codes [256 rows][8 swizzled blocks] and
   // scale words [64 lanes][8 sub-tiles]
   __shared__ __attribute__((aligned(16))) uint8_t sB0[kBN * 128];
@@ -693,6 +768,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   else
     pipeline(std::false_type{});
 
+  // ---- the third and fourth activation terms of the units that have them
+  // (quantize_tile decides per unit; blocks of like magnitudes have none).  A
+  // flagged k-step g re-reads its weight operands from memory (the stages in
+  // LDS are gone): the 16-byte block 2 g + half of each sub-tile row, and the
+  // repacked scale words of stage g / 4, whose byte g % 4 is the block's.
+  if (valid) {
+    const uint8_t* fl = aqf + unit0;
+    const int f0 = fl[min(lane, NKP - 1)];
+    const int f1 = fl[min(lane + 64, NKP - 1)];
+    uint64_t m0 = wave_ballot(lane < NKP && f0 != 0);
+    uint64_t m1 = wave_ballot(lane + 64 < NKP && f1 != 0);
+    while (m0 | m1) {
+      int g, n;
+      if (m0) {
+        const int i = __builtin_ctzll(m0);
+        m0 &= m0 - 1;
+        g = i;
+        n = __builtin_amdgcn_readlane(f0, i);
+      } else {
+        const int i = __builtin_ctzll(m1);
+        m1 &= m1 - 1;
+        g = 64 + i;
+        n = __builtin_amdgcn_readlane(f1, i);
+      }
+      g = __builtin_amdgcn_readfirstlane(g);
+      n = __builtin_amdgcn_readfirstlane(n);
+      const int blk = min(2 * g + half, KB - 1) * 16;
+      u32x4_t wq[kSubN];
+#pragma unroll
+      for (int c = 0; c < kSubN; c++)
+        wq[c] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(n0 + 32 * c + l32, N - 1) * (KB * 16) + blk, 0, 0);
+      const u32x4_t s0 = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, lane * 32, (g >> 2) * (kSubN * 64 * 4), 0);
+      const u32x4_t s1 = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, lane * 32 + 16, (g >> 2) * (kSubN * 64 * 4), 0);
+      const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc, lane * 4, g * 256, 0);
+      const uint8_t* xr = aqx + (unit0 + g) * kAUnit;
+      const int sh = 8 * (g & 3);
+      const uint32_t wsc8[kSubN] = {s0.x >> sh, s0.y >> sh, s0.z >> sh, s0.w >> sh,
+                                    s1.x >> sh, s1.y >> sh, s1.z >> sh, s1.w >> sh};
+      auto term = [&](const uint8_t* rec) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(rec + lane * 16);
+        const u32x2_t b = *reinterpret_cast<const u32x2_t*>(rec + 1024 + lane * 8);
+        return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, 0, 0};
+      };
+      const v8i t2 = term(xr);
+#pragma unroll
+      for (int c = 0; c < kSubN; c++) {
+        const v8i wa = v8i{(int)wq[c].x, (int)wq[c].y, (int)wq[c].z, (int)wq[c].w, 0, 0, 0, 0};
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, t2, acc[c], kFmtFp4E2M1, kFmtFp6E2M3, 0,
+                                                                 wsc8[c], 2, sw);
+      }
+      if (n > 1) {
+        const v8i t3 = term(xr + 1536);
+#pragma unroll
+        for (int c = 0; c < kSubN; c++) {
+          const v8i wa = v8i{(int)wq[c].x, (int)wq[c].y, (int)wq[c].z, (int)wq[c].w, 0, 0, 0, 0};
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, t3, acc[c], kFmtFp4E2M1, kFmtFp6E2M3, 0,
+                                                                   wsc8[c], 3, sw);
+        }
+      }
+    }
+  }
+
   // ---- epilogue: scatter to the routed rows (bias included).  Each lane
   // holds one routed row and, per accumulator, 4 runs of 4 consecutive
   // columns.  The wide paths pass the wave's results through its own 8 KB of
@@ -806,7 +943,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 struct GemmLayout {
-  size_t codes, scales, wscales, total;
+  size_t codes, extra, scales, flags, wscales, total;
 };
 
 // most row tiles any routing can give: ceil(R / kBM) plus one partial tile per
@@ -822,10 +959,13 @@ GemmLayout gemm_layout(int E, int N, int T, int k, int K) {
   const size_t nkp = ns * kStepsPerStage;
   const size_t nt = (size_t)((N + kBN - 1) / kBN);
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t units = tiles * kWaves * nkp;
   GemmLayout l;
   l.codes = 0;
-  l.scales = al(tiles * kWaves * nkp * kAUnit);
-  l.wscales = l.scales + al(tiles * kWaves * nkp * 256);
+  l.extra = al(units * kAUnit);
+  l.scales = l.extra + al(units * kAUnit);
+  l.flags = l.scales + al(units * 256);
+  l.wscales = l.flags + al(units);
   l.total = l.wscales + al((size_t)E * nt * ns * kSubN * 256);
   return l;
 }
@@ -850,7 +990,9 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   const GemmLayout l = gemm_layout(E, N, T, k, K);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* aq = ws + l.codes;
+  uint8_t* aqx = ws + l.extra;
   uint32_t* as = reinterpret_cast<uint32_t*>(ws + l.scales);
+  uint8_t* aqf = ws + l.flags;
   uint32_t* bsc = reinterpret_cast<uint32_t*>(ws + l.wscales);
   const int R = T * k;
   const size_t tiles = row_tiles_max(E, T, k);
@@ -858,20 +1000,17 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   // workgroups share a CU)
   const size_t panel_bytes = ((size_t)(kBN * (K / 32) + 4) / 4 + 1) * 4;
   hipError_t err;
+  static DynLdsLimit prepare_lds(reinterpret_cast<const void*>(&prepare_kernel),
+                                 (int)(((kBN * kRepackMaxKB + 4) / 4 + 1) * 4));
   if (panel_bytes > 65536) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      err = hipFuncSetAttribute(reinterpret_cast<const void*>(&prepare_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(((kBN * kRepackMaxKB + 4) / 4 + 1) * 4));
-      if (err != hipSuccess) return err;
-      attr_set = true;
-    }
+    err = prepare_lds.ensure();
+    if (err != hipSuccess) return err;
   }
   const long long nrep = (long long)E * NT;
-  const long long nq = (long long)tiles * NKP;
+  const long long nq = (long long)tiles * ((NKP + kQSteps - 1) / kQSteps);
   hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(nrep + nq)), dim3(kQThreads), panel_bytes, stream, scales, E, N,
-                     K / 32, NT, NS, bsc, (int)nrep, x, x_per_slot, k, R, K, NKP, offsets, sorted_rows, aq, as);
+                     K / 32, NT, NS, bsc, (int)nrep, x, x_per_slot, k, R, K, NKP, offsets, sorted_rows, aq, aqx, as,
+                     aqf);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long tiles_max = (long long)tiles * NT;
@@ -879,8 +1018,8 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   // the gpt-oss-20b widths (K = 2880) have 12 stages
   auto kern = act ? (NS == 12 ? expert_gemm_kernel<12, true> : expert_gemm_kernel<0, true>)
                   : (NS == 12 ? expert_gemm_kernel<12, false> : expert_gemm_kernel<0, false>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, blocks, bsc, bias, E, N, K, aq, as, T, k,
-                     offsets, sorted_rows, out, act);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, blocks, bsc, bias, E, N, K, aq, aqx, as,
+                     aqf, T, k, offsets, sorted_rows, out, act);
   return hipGetLastError();
 }
 

@@ -517,14 +517,13 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
       const float lj = readlane_f(l, jj);
       rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
     }
-    // Finite logits choose exactly k lanes.  A NaN logit compares false both
-    // ways, so it ranks 0 and more than k lanes qualify: then, as in the
-    // routing kernel, every slot gets id -1, no row is grouped or projected
-    // and no gate is written.
-    const bool chosen = lane < E && rank < k;
-    const uint64_t all = __ballot(chosen);
-    const bool ok = __popcll(all) == k;
-    const uint64_t mask = ok ? all : 0ull;
+    // Logits without NaN rank the lanes 0 .. E - 1, each rank once.  A NaN
+    // compares false both ways and breaks that: then, as in the routing
+    // kernel, every slot gets id -1 and gate 0, and no row is grouped or
+    // projected.
+    const bool ok = __ballot(lane < E && l != l) == 0;
+    const bool chosen = ok && lane < E && rank < k;
+    const uint64_t mask = __ballot(chosen);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
       // the routing outputs: ids and gates by slot, offsets, grouped rows
       if (ok) {
@@ -538,6 +537,7 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
         }
       } else if (lane < k) {
         fr.topk_ids[lane] = -1;
+        if (fr.gates) fr.gates[lane] = 0.f;
       }
       if (lane < E) fr.offsets[lane] = __popcll(mask & ((1ull << lane) - 1));
       if (lane == 0) {
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
         if (fr.error_word) *fr.error_word = ok ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
       }
     }
-    const uint64_t mine = __ballot(chosen && ok && lanes_below(mask) == (int)blockIdx.y);
+    const uint64_t mine = __ballot(chosen && lanes_below(mask) == (int)blockIdx.y);
     if (mine == 0) return;
     e = __builtin_amdgcn_readfirstlane(__ffsll((long long)mine) - 1);
     fused_row = __builtin_amdgcn_readlane(rank, e);
@@ -801,7 +801,7 @@ __global__ __launch_bounds__(WPS * kT1Group * 64) void expert_gemv_combine_t1_ke
       for (int h = 0; h < ng; h++) {  // slot order
         const int sh = s0 + h;
         const int eh = topk_ids[sh];
-        if (eh >= 0 && eh < E) yacc = fmaf(gates[sh], vals[h][rl], yacc);
+        if (eh >= 0 && eh < E && gates[sh] != 0.f) yacc = fmaf(gates[sh], vals[h][rl], yacc);
       }
     }
   }
@@ -859,12 +859,12 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
   G = G > nblk ? nblk : G;
   const int nbpw = (nblk + G - 1) / G;
   const size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K, nbpw);
-  static bool attr_set = false;  // raise the dynamic LDS limit (to what any K may need) once
-  if (!attr_set && lds > 65536) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxDynLds);
+  // above 64 KB the dynamic LDS limit is raised (to what any K may need)
+  static DynLdsLimit gemv_lds(
+      reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>), kGemvMaxDynLds);
+  if (lds > 65536) {
+    const hipError_t err = gemv_lds.ensure();
     if (err != hipSuccess) return err;
-    attr_set = true;
   }
   const dim3 grid(G, groups);
   hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>), grid, dim3(WAVES * 64), lds, stream, blocks,

@@ -61,8 +61,9 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 
 // Token t with given expert ids: lane s < k holds the id e of slot s and, for
 // the gates, the logit at e (lg).  Checks range and repeats, writes the ids
-// (a repeat flagged in bit 30 for the grouping) and the softmax over the k
-// logits.  Returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
+// (a repeat flagged in bit 30 for the grouping; an id out of range as -1) and
+// the softmax over the logits of the slots in range (gate 0 for the others).
+// Returns MXFP4_ROUTE_ERR_* bits (same on all lanes).
 __device__ int route_given(int e, float lg, int t, int E, int k, int lane, int32_t* __restrict__ topk_ids,
                            float* __restrict__ gates, bool with_gates, int32_t* ids_copy) {
   int32_t* ids = topk_ids + (size_t)t * k;
@@ -80,12 +81,13 @@ __device__ int route_given(int e, float lg, int t, int E, int k, int lane, int32
     ids[lane] = idv;
     if (idc) idc[lane] = idv;
   }
-  if (with_gates && bad == 0) {
-    const float l = lane < k ? lg : -INFINITY;
+  if (with_gates) {
+    // softmax over the logits of the slots with an id in range; 0 for the others
+    const float l = in_range ? lg : -INFINITY;
     const float mx = wave_max(l);
-    const float num = lane < k ? expf(l - mx) : 0.f;
+    const float num = in_range ? expf(l - mx) : 0.f;
     const float sum = wave_sum(num);
-    if (lane < k) gates[(size_t)t * k + lane] = num / sum;
+    if (lane < k) gates[(size_t)t * k + lane] = in_range ? num / sum : 0.f;
   }
   return (bad ? MXFP4_ROUTE_ERR_ID_RANGE : 0) | (dups ? MXFP4_ROUTE_ERR_ID_DUP : 0);
 }
@@ -114,17 +116,18 @@ __device__ int route_ranked(const float (&l)[EC], int t, int E, int k, int lane,
       }
     }
   }
-  // Finite logits give exactly k experts of ranks 0 .. k - 1.  A NaN logit
-  // compares false both ways, so it ranks 0 beside the largest logit and more
-  // than k experts qualify: such a token gets id -1 in every slot (its rows are
-  // left out of the grouping) and no gates.
-  int seen = 0;
+  // Logits without NaN rank the experts 0 .. E - 1, each rank once.  A NaN
+  // compares false both ways, so it would rank 0 beside the largest logit and
+  // break that: a token with a NaN logit gets id -1 and gate 0 in every slot
+  // (its rows are left out of the grouping).
+  bool has_nan = false;
 #pragma unroll
-  for (int i = 0; i < EC; i++) seen += __popcll(__ballot(lane + 64 * i < E && rank[i] < k));
-  if (seen != k) {
+  for (int i = 0; i < EC; i++) has_nan |= __ballot(lane + 64 * i < E && l[i] != l[i]) != 0;
+  if (has_nan) {
     if (lane < k) {
       ids[lane] = -1;
       if (idc) idc[lane] = -1;
+      if (gates) gates[(size_t)t * k + lane] = 0.f;
     }
     return MXFP4_ROUTE_ERR_ID_RANGE;
   }
@@ -222,8 +225,10 @@ constexpr int kRouteBatch = 4;
 // tiles of lower waves give each expert's base for this wave's rows; a lane's
 // place is then that base plus the lanes below it with the same id (one
 // ballot per id bit).  Rows are placed in ascending order within an expert,
-// so the result is the stable counting sort.  Workgroup 0 writes the offsets
-// and the error word; a chunk's owner clears the repeat flags of its rows.
+// so the result is the stable counting sort.  Workgroup 0 writes the offsets.
+// A chunk's owner alone inspects its rows for errors (a -1 or an id >= E, a
+// repeat flag), before it clears their repeat flags, and ORs what it found
+// into the error word, which the routing launch zeroed.
 constexpr int kChunk = kGroupThreads;
 
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restrict__ topk_ids, int R, int E,
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
   int* cnt_pre = cnt_all + kGroupWaves * E;    // [waves][E]: rows per expert in tiles before the chunk
   int* cnt_own = cnt_pre + kGroupWaves * E;    // [waves][E]: rows per expert in the wave's chunk tile
   int* base = cnt_own + kGroupWaves * E;       // [E]
-  __shared__ int err_sh;
+  __shared__ int err_sh;  // error bits found in this workgroup's chunk
   __shared__ int total_sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
   const int own_tile = (int)blockIdx.x * kGroupWaves + wave;  // this wave's chunk tile
   int errbits = 0;
 
-  // one row per lane of tile t: its id with the repeat flag cleared (-1 past R or out of range)
+  // the lanes of a tile whose rows share this lane's expert e (-1: no expert)
   auto peers_of = [&](int e) {
     const bool valid = e >= 0;
     uint64_t peers = __ballot(valid);
@@ -276,12 +281,15 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
       if (t >= tiles) break;  // wave-uniform
       const int r = t * 64 + lane;
       int e = ev[i];
-      if (r < R) {
+      const bool dup = e >= 0 && (e & kDupFlag);
+      if (dup) e &= ~kDupFlag;
+      if (e >= E) e = -1;  // never written by the routing: counted as out of range
+      if (t == own_tile && r < R) {
+        // the chunk's owner: its rows' errors, then the repeat flags cleared
         if (e < 0) errbits |= MXFP4_ROUTE_ERR_ID_RANGE;
-        if (e >= 0 && (e & kDupFlag)) {
+        if (dup) {
           errbits |= MXFP4_ROUTE_ERR_ID_DUP;
-          e &= ~kDupFlag;
-          if (t == own_tile) topk_ids[r] = e;  // the chunk's owner clears the flag
+          topk_ids[r] = e;
         }
       }
       const uint64_t peers = peers_of(e);
@@ -322,9 +330,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
     if (lane == 0) total_sh = carry;
   }
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0) {
-    offsets[E] = total_sh;
-    if (error_word) *error_word = err_sh;
+  if (tid == 0) {
+    if (blockIdx.x == 0) offsets[E] = total_sh;
+    if (error_word && err_sh) atomicOr(error_word, err_sh);
   }
   // per wave: the base of its chunk tile's rows of expert e (the chunk's lower waves first)
   for (int e = tid; e < E; e += kGroupThreads) {
@@ -342,6 +350,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
     const int r = own_tile * 64 + lane;
     int e = r < R ? topk_ids[r] : -1;  // flag cleared above by this wave (program order)
     if (e >= 0) e &= ~kDupFlag;
+    if (e >= E) e = -1;
     const uint64_t peers = peers_of(e);
     if (e >= 0) sorted_rows[cnt_own[wave * E + e] + lanes_below(peers)] = r;
   }
@@ -377,6 +386,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_tiny_kernel(
     topk_ids[lane] = id;
     err |= MXFP4_ROUTE_ERR_ID_DUP;
   }
+  if (id >= E) id = -1;  // never written by the routing: counted as out of range
   if (lane < R && id < 0) err |= MXFP4_ROUTE_ERR_ID_RANGE;
   err = (__ballot(err & MXFP4_ROUTE_ERR_ID_RANGE) ? MXFP4_ROUTE_ERR_ID_RANGE : 0) |
         (__ballot(err & MXFP4_ROUTE_ERR_ID_DUP) ? MXFP4_ROUTE_ERR_ID_DUP : 0);
@@ -398,14 +408,17 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_tiny_kernel(
   if (lane == 0 && error_word) *error_word = err;
 }
 
-// R > 64, first launch: routing, NB tokens per wave, many workgroups.
+// R > 64, first launch: routing, NB tokens per wave, many workgroups; the
+// first thread zeroes the error word the grouping launch ORs its findings into
+// (the routing's own errors reach the grouping through the ids it writes).
 template <int EC, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const uint16_t* __restrict__ logits,
                                                              const int32_t* __restrict__ ids_in, int T, int E,
                                                              int k, int32_t* __restrict__ topk_ids,
-                                                             float* __restrict__ gates) {
+                                                             float* __restrict__ gates, int32_t* __restrict__ error_word) {
   const int lane = threadIdx.x & 63;
   const int w = (blockIdx.x * kRouteThreads + threadIdx.x) >> 6;
+  if (error_word && blockIdx.x == 0 && threadIdx.x == 0) *error_word = 0;
   route_tokens<EC, NB>(logits, ids_in, w * NB, 1, T, E, k, lane, topk_ids, gates, nullptr);
 }
 
@@ -424,19 +437,19 @@ hipError_t launch_ec(const uint16_t* logits, const int32_t* ids_in, int T, int E
   const dim3 rgrid((T + per_block - 1) / per_block);
   if (one)
     hipLaunchKernelGGL((route_kernel<EC, 1>), rgrid, dim3(kRouteThreads), 0, stream, logits, ids_in, T, E, k, topk_ids,
-                       gates);
+                       gates, error_word);
   else
     hipLaunchKernelGGL((route_kernel<EC, kTokensPerRouteWave>), rgrid, dim3(kRouteThreads), 0, stream, logits,
-                       ids_in, T, E, k, topk_ids, gates);
+                       ids_in, T, E, k, topk_ids, gates, error_word);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t glds = ((size_t)3 * kGroupWaves * E + E) * sizeof(int);
-  static bool attr_set = false;  // up to 3 * 16 * 512 + 512 ints: raise the dynamic LDS limit once
-  if (!attr_set && glds > 65536) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&group_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)((3 * kGroupWaves + 1) * kMaxRouteE * sizeof(int)));
+  // up to 3 * 16 * 512 + 512 ints: above 64 KB the dynamic LDS limit is raised
+  static DynLdsLimit group_lds(reinterpret_cast<const void*>(&group_kernel),
+                               (int)((3 * kGroupWaves + 1) * kMaxRouteE * sizeof(int)));
+  if (glds > 65536) {
+    err = group_lds.ensure();
     if (err != hipSuccess) return err;
-    attr_set = true;
   }
   const long long R = (long long)T * k;
   hipLaunchKernelGGL(group_kernel, dim3((unsigned)((R + kChunk - 1) / kChunk)), dim3(kGroupThreads), glds, stream,

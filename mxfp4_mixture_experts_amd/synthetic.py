@@ -160,6 +160,28 @@ def make_custom(E, N, K, T, k, *, x_per_slot=False, route="logits", seed=0, tag=
                       x_per_slot, logits, ids, combine)
 
 
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns as float32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def scale_channels(x_bits: np.ndarray, channels, factor: float) -> np.ndarray:
+    """Activations with outlier channels: the given input channels (last axis) of
+    every row multiplied by `factor`, rounded back to bf16.  Hidden states of
+    trained transformers carry a few such channels, often 100-1000x the rest."""
+    f = bf16_bits_to_f32(x_bits).copy()
+    f[..., list(channels)] *= np.float32(factor)
+    return f32_to_bf16_bits(f)
+
+
+def lognormal_bf16(shape, sigma: float, *, seed: int = 0, tag: int = 97) -> np.ndarray:
+    """Heavy-tailed activations: random sign times exp(sigma * N(0, 1)), as bf16."""
+    rng = _rng(seed, tag, _T_X)
+    mag = np.exp(sigma * rng.standard_normal(size=shape))
+    sign = np.where(rng.integers(0, 2, size=shape) == 0, -1.0, 1.0)
+    return f32_to_bf16_bits((sign * mag).astype(np.float32))
+
+
 @dataclass
 class RouterProblem:
     """Router inputs (src/experts.linnet block MixtureOfExperts, sub router: a

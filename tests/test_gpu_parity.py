@@ -103,16 +103,36 @@ def test_gemm_limits(case):
 
 
 def test_paths_agree_closely():
-    """GEMV (exact products) and GEMM (two-term MX-FP6 activations) on the same input."""
+    """GEMV (exact products) and GEMM (MX-FP6 activation terms) on the same input:
+    each against the oracle, and against each other."""
     p = S.make_custom(E=8, N=256, K=2880, T=24, k=4, route="logits")
     _announce("paths agree")
+    ref = O.run_problem(p)
     outs = []
     for path in (1, 2):
         dp = DeviceProblem(p, path=path)
         dp.run()
         outs.append(dp.results()["out"].astype(np.float64))
-    ref = O.run_problem(p)
+        check_close(outs[-1], ref["out"], ref["mag"], f"path {PATHS[path]} vs oracle")
     check_close(outs[1], outs[0], ref["mag"], "gemm vs gemv")
+
+
+def _scaled_bf16(bits, log2_factor):
+    """bf16 values times 2 ** log2_factor (exact: a power of two in range)."""
+    f = (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    return S.f32_to_bf16_bits((f * 2.0 ** log2_factor).astype(np.float32))
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("lo,hi,shift,T", [(0, 6, 120, 37), (246, 252, -120, 37), (0, 6, 120, 1),
+                                            (246, 252, -120, 1)])
+def test_extreme_scale_bytes(lo, hi, shift, T, path):
+    """Weight scale bytes at both ends of the range (factors 2^-127 .. 2^125),
+    inputs scaled by 2^shift so that the products are ordinary fp32 values."""
+    p = S.make_custom(E=8, N=200, K=320, T=T, k=3, route="logits", scale_lo=lo, scale_hi=hi, tag=800 + lo)
+    p.x = _scaled_bf16(p.x, shift)
+    p.name = f"scales {lo}..{hi} x*2^{shift} T={T}"
+    full_parity(p, path)
 
 
 # ----------------------------------------------------------------- routing paths
@@ -164,6 +184,22 @@ def test_given_ids_errors_are_flagged():
     vals, mags = O.expert_proj_sampled(p.blocks, p.scales, p.bias, p.x, False, np.where(g["ids"] < 0, 0, g["ids"]),
                                        np.repeat(valid_rows, 64), np.tile(np.arange(64), len(valid_rows)))
     check_close(g["out"].reshape(8, 64)[valid_rows].reshape(-1), vals, mags, "valid rows")
+    # gates: the softmax over the logits of the slots in range, 0 for the others;
+    # y sums the valid slots only (the unwritten rows hold 12345 and add nothing)
+    valid = g["ids"] >= 0
+    lg = O.bf16_to_f64(p.logits)
+    want_g = np.zeros((4, 2))
+    for t in range(4):
+        ids_t = g["ids"][t][valid[t]]
+        want_g[t, valid[t]] = O.softmax_at(lg[t:t + 1], ids_t[None, :])[0]
+    assert np.abs(g["gates"] - want_g).max() <= GATE_TOL
+    assert np.all(g["gates"][~valid] == 0.0)
+    out_v = np.zeros((4, 2, 64))
+    mag_v = np.zeros((4, 2, 64))
+    out_v.reshape(8, 64)[valid_rows] = vals.reshape(-1, 64)
+    mag_v.reshape(8, 64)[valid_rows] = mags.reshape(-1, 64)
+    y_ref, y_mag = O.combine(out_v, g["gates"], mag_v)
+    check_close(g["y"], y_ref, y_mag, "y over the valid slots")
 
 
 def test_given_ids_errors_flagged_multiworkgroup():
@@ -177,6 +213,7 @@ def test_given_ids_errors_flagged_multiworkgroup():
     ids[599] = [7, 7]      # repeat in the second chunk
     p.ids_in = ids
     dp = DeviceProblem(p, path=1)
+    dp.error_word.fill_(-1)
     dp.run()
     g = dp.results()
     assert g["error_word"] == (B.MXFP4_ROUTE_ERR_ID_RANGE | B.MXFP4_ROUTE_ERR_ID_DUP)
@@ -190,6 +227,28 @@ def test_given_ids_errors_flagged_multiworkgroup():
     order = valid[np.argsort(flat[valid], kind="stable")]
     np.testing.assert_array_equal(g["sorted_rows"][:valid.size], order)
     np.testing.assert_array_equal(g["offsets"][:-1], np.searchsorted(np.sort(flat[valid]), np.arange(E)))
+
+
+@pytest.mark.parametrize("T,E,k,where", [(600, 8, 2, 599), (3000, 16, 4, 2999), (3000, 16, 4, 1300)])
+def test_error_found_only_in_a_later_chunk(T, E, k, where):
+    """A repeat (then an out-of-range id) only in a chunk other than the first:
+    its owner reports it, whatever the other workgroups have read or cleared."""
+    _announce(f"error only in a later chunk T={T} row={where}")
+    for bad, bit in (([3, 3] + list(range(4, 4 + k - 2)), B.MXFP4_ROUTE_ERR_ID_DUP),
+                     ([E + 2] + list(range(1, k)), B.MXFP4_ROUTE_ERR_ID_RANGE)):
+        p = S.make_custom(E=E, N=16, K=32, T=T, k=k, route="ids+logits", tag=700 + T)
+        ids = p.ids_in.copy()
+        ids[where] = np.array(bad[:k], np.int32)
+        p.ids_in = ids
+        dp = DeviceProblem(p, path=1)
+        dp.error_word.fill_(-1)
+        dp.route_group()
+        g = dp.results()
+        assert where * k >= 1024, "the bad row must lie past the first chunk"
+        assert g["error_word"] == bit
+        want = ids.copy()
+        want[(want < 0) | (want >= E)] = -1
+        np.testing.assert_array_equal(g["ids"], want)
 
 
 def test_deterministic_and_stream():
@@ -378,6 +437,13 @@ def _sample_pairs(rng, R, N, n):
 
 @pytest.mark.parametrize("cfg,path", [(1, 0), (1, 2), (2, 0), (2, 1), (3, 0), (4, 0)])
 def test_model_size_config(cfg, path):
+    """Every output of the model-size workloads against the oracle."""
+    p = S.make_config(cfg)
+    full_parity(p, path)
+
+
+@pytest.mark.parametrize("cfg,path", [(3, 1), (4, 1)])
+def test_model_size_config_sampled(cfg, path):
     p = S.make_config(cfg)
     _announce(f"{p.name} path={PATHS[path]} (sampled)")
     if p.ids_in is not None:
