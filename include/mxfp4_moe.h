@@ -213,6 +213,28 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
                       int path, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mxfp4_expert_proj for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments, paths, limits and results (bit for bit) as
+ * mxfp4_expert_proj, without the workspace: the grouped-GEMM path's scratch
+ * (the quantized activation terms, their scales and the repacked weight
+ * scales) is a static device array of MXFP4_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; its device
+ * address is looked up once per device.  Nothing is allocated or freed, and
+ * nothing needs to start at zero: every call writes all of the scratch it
+ * reads.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (on different streams, or from several threads) race:
+ * order them on one stream.  A problem whose grouped GEMM would need more
+ * than MXFP4_NOALLOC_SCRATCH_BYTES (mxfp4_expert_proj_workspace_size) returns
+ * MXFP4_ERR_WORKSPACE and enqueues nothing; the GEMV path needs no scratch.
+ */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mxfp4_expert_proj_noalloc(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
+                              int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                              const int32_t* expert_offsets, const int32_t* sorted_rows, float* out,
+                              int path, void* stream);
+
+/*
  * The routed gate/up projection followed by the gpt-oss gated activation,
  * written as bf16 -- the down projection's per-slot input.
  * (src/experts.linnet: the gate and up weights share one tensor, interleaved

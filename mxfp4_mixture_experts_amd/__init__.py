@@ -12,7 +12,8 @@ raises.
 
 __all__ = ["mxfp4_moe_route_group", "mxfp4_expert_proj", "mxfp4_expert_proj_workspace_size", "moe_combine",
            "mxfp4_expert_proj_swiglu", "mxfp4_expert_proj_combine", "mxfp4_moe_decode", "mxfp4_moe_decode_swiglu",
-           "mxfp4_moe_router", "mxfp4_moe_dense_route", "mxfp4_dequantize", "library_path"]
+           "mxfp4_moe_router", "mxfp4_moe_dense_route", "mxfp4_dequantize", "mxfp4_expert_proj_noalloc",
+           "library_path"]
 
 
 def __getattr__(name):

@@ -21,6 +21,7 @@ MXFP4_PATH_AUTO, MXFP4_PATH_GEMV, MXFP4_PATH_GEMM = 0, 1, 2
 MXFP4_ROUTE_ERR_ID_RANGE, MXFP4_ROUTE_ERR_ID_DUP = 1, 2
 MXFP4_MAX_EXPERTS, MXFP4_MAX_TOPK = 512, 32
 MXFP4_DECODE_MAX_EXPERTS, MXFP4_DECODE_MAX_K, MXFP4_GEMM_MAX_K = 64, 3072, 8192
+MXFP4_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 #: the C entry points this binding uses (all declared in include/mxfp4_moe.h)
 ENTRY_POINTS = (
@@ -37,6 +38,7 @@ ENTRY_POINTS = (
     "mxfp4_moe_router",
     "mxfp4_moe_decode_swiglu",
     "mxfp4_expert_proj_combine",
+    "mxfp4_expert_proj_noalloc",
 )
 
 _lib_handle = None
@@ -74,6 +76,8 @@ def load_library():
     lib.mxfp4_expert_proj_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.mxfp4_expert_proj_workspace_size.restype = sz
     lib.mxfp4_expert_proj.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.mxfp4_expert_proj_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, vp]
+    lib.mxfp4_expert_proj_noalloc.restype = i32
     lib.mxfp4_expert_proj.restype = i32
     lib.mxfp4_expert_proj_swiglu.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.mxfp4_expert_proj_swiglu.restype = i32
@@ -175,6 +179,20 @@ def mxfp4_expert_proj(blocks, scales, bias, E: int, N: int, K: int, x, x_per_slo
         int(E), int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(T), int(k),
         _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
         _ptr(out, "out", _F32, dev), int(path), ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_expert_proj_noalloc(blocks, scales, bias, E: int, N: int, K: int, x, x_per_slot: bool, T: int, k: int,
+                              expert_offsets, sorted_rows, out, path: int = MXFP4_PATH_AUTO, stream=None):
+    """mxfp4_expert_proj with the library's static scratch instead of a workspace
+    (mxfp4_expert_proj_noalloc); out [T,k,N] f32 is written in place."""
+    lib = load_library()
+    dev = out.device
+    st = lib.mxfp4_expert_proj_noalloc(
+        _ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev),
+        int(E), int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(T), int(k),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(out, "out", _F32, dev), int(path), _stream(stream, dev))
     _check(st)
 
 

@@ -76,10 +76,14 @@ bool gemv_fits(int T, int K) { return mxfp4::gemv_lds_bytes(T, K) <= 160 * 1024 
 
 // The routed projection; exactly one of out (f32 [T, k, N]) and act (bf16
 // [T, k, N / 2], the gated activation) is written.
+static_assert(mxfp4::kGemmStaticScratchBytes == MXFP4_NOALLOC_SCRATCH_BYTES, "one size for the static scratch");
+
+// noalloc: the grouped GEMM's scratch is the library's static device array
+// (workspace and workspace_bytes are ignored).
 int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                      const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
                      const int32_t* sorted_rows, float* out, uint16_t* act, int path, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, bool noalloc = false) {
   g_last_error[0] = '\0';
   if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
   if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
@@ -104,13 +108,23 @@ int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_
     return fail(MXFP4_ERR_INVALID_ARG, "N * K / 2 = %zu bytes per expert exceeds 4 GiB", (size_t)N * (K / 32) * 16);
   if (p == MXFP4_PATH_GEMM) {
     const size_t need = mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
-    if (!workspace || workspace_bytes < need)
-      return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
-                  need);
-    if (!aligned16(workspace)) return fail(MXFP4_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (noalloc) {
+      if (need > MXFP4_NOALLOC_SCRATCH_BYTES)
+        return fail(MXFP4_ERR_WORKSPACE, "the grouped GEMM needs %zu bytes of scratch, the static scratch holds %zu",
+                    need, (size_t)MXFP4_NOALLOC_SCRATCH_BYTES);
+    } else {
+      if (!workspace || workspace_bytes < need)
+        return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+      if (!aligned16(workspace)) return fail(MXFP4_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    }
   }
   int st = check_device();
   if (st != MXFP4_OK) return st;
+  if (noalloc && p == MXFP4_PATH_GEMM) {
+    const hipError_t se = mxfp4::gemm_static_scratch(&workspace);
+    if (se != hipSuccess) return hip_fail(se, "static scratch address");
+  }
   hipError_t e;
   if (p == MXFP4_PATH_GEMV)
     e = mxfp4::launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
@@ -204,6 +218,17 @@ int mxfp4_expert_proj(const uint8_t* blocks, const uint8_t* scales, const uint16
   if (T > 0 && !out) return fail(MXFP4_ERR_INVALID_ARG, "out is NULL");
   return expert_proj_impl(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows, out,
                           nullptr, path, workspace, workspace_bytes, stream);
+}
+
+int mxfp4_expert_proj_noalloc(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
+                              const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
+                              const int32_t* sorted_rows, float* out, int path, void* stream) {
+  if (T > 0 && !out) {
+    g_last_error[0] = '\0';
+    return fail(MXFP4_ERR_INVALID_ARG, "out is NULL");
+  }
+  return expert_proj_impl(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows, out,
+                          nullptr, path, nullptr, 0, stream, true);
 }
 
 int mxfp4_expert_proj_swiglu(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,

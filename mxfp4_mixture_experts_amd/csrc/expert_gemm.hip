@@ -972,6 +972,35 @@ GemmLayout gemm_layout(int E, int N, int T, int k, int K) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// the grouped GEMM's scratch for callers that cannot allocate
+// (mxfp4_expert_proj_noalloc): a static device array, one per GPU for the
+// life of the process.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kGemmStaticScratchBytes];
+
+hipError_t gemm_static_scratch(void** ptr) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
+}
+
 size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot) {
   (void)x_per_slot;
   return gemm_layout(E, N, T, k, K).total;

@@ -38,6 +38,10 @@ hipError_t launch_proj_combine_t1(const uint8_t* blocks, const uint8_t* scales, 
 
 // expert_gemm.hip
 size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);
+// the static scratch of the current device (its device address; resolved once
+// per device) and its size, = MXFP4_NOALLOC_SCRATCH_BYTES
+constexpr size_t kGemmStaticScratchBytes = (size_t)128 << 20;
+hipError_t gemm_static_scratch(void** ptr);
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
                               int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
                               const int32_t* offsets, const int32_t* sorted_rows, float* out, uint16_t* act,

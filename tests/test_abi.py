@@ -239,3 +239,21 @@ def test_proj_combine_rejects_bad_arguments():
     assert f(p, p, None, 32, 2880, 2880, p, 1, 4, p, p, None, None, None) == 1  # no y
     assert f(p, p, None, 32, 2880, 2880, ctypes.c_void_p(8), 1, 4, p, p, None, p, None) == 1  # x misaligned
     assert lib.mxfp4_last_error() != b""
+
+
+def test_noalloc_refuses_more_than_its_scratch():
+    """mxfp4_expert_proj_noalloc rejects, before any HIP call, a problem whose grouped
+    GEMM needs more than the static scratch (the gate_up prefill of 4096 tokens
+    needs about 215 MB); the same problem on the GEMV path needs none."""
+    lib = B.load_library()
+    p = ctypes.c_void_p
+    need = lib.mxfp4_expert_proj_workspace_size(32, 5760, 4096, 4, 2880, 0, 2)
+    assert need > B.MXFP4_NOALLOC_SCRATCH_BYTES
+    args = lambda T, path: (p(16), p(16), None, 32, 5760, 2880, p(16), 0, T, 4, p(16), p(16), p(16), path, None)
+    assert lib.mxfp4_expert_proj_noalloc(*args(4096, 2)) == 2
+    assert b"static scratch" in lib.mxfp4_last_error()
+    small = lib.mxfp4_expert_proj_workspace_size(32, 5760, 512, 4, 2880, 0, 2)
+    assert small <= B.MXFP4_NOALLOC_SCRATCH_BYTES
+    assert lib.mxfp4_expert_proj_noalloc(*args(0, 2)) == 0           # T = 0: nothing to do
+    assert lib.mxfp4_expert_proj_noalloc(p(16), p(16), None, 32, 5760, 2880, p(16), 0, 4, 4, p(16), p(16), None,
+                                         2, None) == 1               # out is NULL
