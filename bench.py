@@ -34,6 +34,11 @@ MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4 MFMA, published
 METRIC = "MXFP4 expert-proj HBM GB/s (decode) & TFLOP/s (prefill), % of MI355X roofline"
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_gemv_gate_up_decode_t1.traffic.txt")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_gemm_gate_up_prefill_t4096.traffic.txt")
+# the FP6 x FP4 scaled MFMA's sustained rate measured on this part (independent
+# v_mfma_scale_f32_32x32x64_f8f6f4 on every CU), halved: each product takes two
+# terms, so this is the grouped GEMM's ceiling in algorithmic flops
+TWO_TERM_CEILING_TFLOPS = 7700.0 / 2
 KERNEL_SOURCES = {
     "expert_gemv": ["mxfp4_mixture_experts_amd/csrc/expert_gemv.hip", "mxfp4_mixture_experts_amd/csrc/common.h"],
     "expert_gemm": ["mxfp4_mixture_experts_amd/csrc/expert_gemm.hip", "mxfp4_mixture_experts_amd/csrc/common.h"],
@@ -48,13 +53,13 @@ def kernel_source_hash(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
+def read_traffic(kernel: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 key, v = line.split(":", 1)
@@ -330,23 +335,48 @@ def measure_block_decode(reps, rotate_bytes):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(cfg_index, reps=2):
-    """The oracle as it stands, on this host, one BLAS thread, on the whole headline workload."""
-    from threadpoolctl import threadpool_limits
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg_index, min_seconds=10.0, max_reps=200):
+    """The oracle as it stands, on this host's cores (BLAS threads = the CPUs this
+    process may run on), on the whole headline step, repeated until at least
+    min_seconds of work; then the same once on one thread for comparison."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle.moe_oracle as O
     from mxfp4_mixture_experts_amd import synthetic as S
     p = S.make_config(cfg_index)
     ids = p.ids_in if p.ids_in is not None else O.route_topk(p.logits, p.k)[0]
     acc = algorithmic(p, np.unique(ids).size)
-    best = float("inf")
-    with threadpool_limits(limits=1):
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            O.run_problem(p)
-            best = min(best, time.perf_counter() - t0)
-    return {"value": round(acc["step"] / best / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole {p.name} step (route, group, projection{', combine' if p.combine else ''}) "
-                      f"in float64 numpy, best of {reps}, {best:.2f} s per step"}
+    cores = len(os.sched_getaffinity(0))
+
+    def run(limit, seconds):
+        with threadpool_limits(limits=limit):
+            used = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+            O.run_problem(p)                      # warm caches and thread pools
+            reps, t0 = 0, time.perf_counter()
+            while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < seconds):
+                O.run_problem(p)
+                reps += 1
+            return (time.perf_counter() - t0) / reps, reps, used
+
+    t_all, reps, used = run(cores, min_seconds)
+    t_one, reps1, _ = run(1, min(min_seconds, 5.0))
+    return {"value": round(acc["step"] / t_all / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "cpu_model": _cpu_model(), "cpus_available": cores,
+            "value_one_thread": round(acc["step"] / t_one / 1e9, 4),
+            "sample": f"the whole {p.name} step (route, group, projection{', combine' if p.combine else ''}) in "
+                      f"float64 numpy: {reps} steps of {t_all * 1e3:.1f} ms each with BLAS on {used} threads "
+                      f"(the LUT dequantization of the chosen experts is numpy on one thread); on one thread "
+                      f"{t_one * 1e3:.1f} ms per step ({reps1} steps)"}
 
 
 def main():
@@ -443,6 +473,24 @@ def main():
         for cfg, steps, swiglu in ((2, 100, False), (3, 20, False), (4, 40, False), (1, 200, True), (3, 20, True)):
             r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu, fused=swiglu)
             a = r["acc"]
+            if cfg == 3 and not swiglu:
+                # the prefill half of the metric: the grouped GEMM at the gate_up prefill
+                tf = a["flops"] / (r["proj_us"] * 1e-6) / 1e12
+                line["roofline_prefill"] = {
+                    "bound": "mfma",
+                    "kernel": "expert_proj grouped-GEMM path: prepare_kernel + expert_gemm_kernel",
+                    "workload": describe(r["p"]),
+                    "achieved": round(tf, 1),
+                    "peak": MXFP4_PEAK_TFLOPS,
+                    "unit": "TFLOP/s",
+                    "frac": round(tf / MXFP4_PEAK_TFLOPS, 4),
+                    "frac_of_two_term_ceiling": round(tf / TWO_TERM_CEILING_TFLOPS, 4),
+                    "kernel_us": round(r["proj_us"], 2),
+                    "algorithmic_flops_per_launch": a["flops"],
+                    "algorithmic_bytes_per_launch": a["proj"],
+                    "GBps": round(a["proj"] / (r["proj_us"] * 1e-6) / 1e9, 1),
+                    "traffic": read_traffic("expert_gemm", PREFILL_TRAFFIC_FILE),
+                }
             t_step = r["ms_per_step"] * 1e-3
             t_proj = r["proj_us"] * 1e-6
             roof_t = max(a["flops"] / (MXFP4_PEAK_TFLOPS * 1e12), a["step"] / (HBM_PEAK_GBS * 1e9))
