@@ -26,8 +26,11 @@
 //    routed order), written in the register image of the MFMA B operand, so
 //    that a wave fetches one k-step of its 32 rows with four contiguous loads
 //    straight into registers, two k-steps ahead.
-//  * Tile = 128 routed rows x 256 weight rows, 4 waves; wave w owns routed
-//    rows 32w .. 32w + 31 and all 256 weight rows (8 accumulators of 32 x 32).
+//  * Tile = 128 routed rows x 192 weight rows, 4 waves; wave w owns routed
+//    rows 32w .. 32w + 31 and all 192 weight rows (6 accumulators of 32 x 32).
+//    192 divides both gpt-oss widths (2880, 5760), so no weight panel is
+//    padded, and the registers the accumulators leave free hold a second
+//    stage of weights in flight: weight loads have two stages to arrive.
 //    The weight tile is the only operand shared by the waves, and it is the
 //    light one (16 bytes per row and block against 48 for the two activation
 //    terms), so it alone goes through LDS.  Two workgroups share a CU.
@@ -67,9 +70,11 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;    // GEMM workgroup
 constexpr int kQThreads = 256;           // pre-pass workgroups (one wave per row sub-tile)
 constexpr int kBM = 128;                 // routed rows per tile: one 32-row sub-tile per wave
-constexpr int kBN = 256;                 // weight rows per tile: 8 sub-tiles of 32
+constexpr int kBN = 192;                 // weight rows per tile: 6 sub-tiles of 32 (192 divides 2880 and 5760)
 constexpr int kSubN = kBN / 32;
-static_assert(kThreads == kBN && kThreads >= kBM, "the prologue has one thread per tile column");
+constexpr int kSubW = 8;                 // repacked weight-scale words per lane and stage (kSubN used)
+static_assert(kThreads >= kBN && kThreads >= kBM, "the prologue has one thread per tile column and row");
+static_assert(kSubN <= kSubW, "scale words");
 constexpr int kStepsPerStage = 4;        // MFMA k-steps (two MX blocks each) per weight stage
 constexpr int kStageBlocks = 2 * kStepsPerStage;
 constexpr int kStagePad = 2;             // stage counts are padded to a multiple of 2 (the ring)
@@ -219,18 +224,24 @@ __device__ __forceinline__ bool locate_row_tile(const int32_t* offsets, int E, i
 // A wave's 32 rows x 2 blocks are one unit (t, sub, g) of the GEMM: one MFMA
 // B operand per term.  Every block gets two terms (hi, lo); when any block of
 // the unit needs a third (needs_term), all of them get one, and likewise a
-// fourth.  Writes the register image of the MFMA B operand: per unit 3 KB =
-// hi bytes 0..15 [lane][16 B] | hi 16..23 [lane][8 B] | lo 0..15 [lane][16 B]
-// | lo 16..23 [lane][8 B], so that each 24-byte operand is one 16-byte and one
-// 8-byte load into its own six registers; the third and fourth terms in the
-// same form in the unit's 3 KB extra record (written only when used); 64 u32
-// scale words (hi | lo << 8 | third << 16 | fourth << 24); and the unit's
-// count of extra terms (0, 1 or 2) in one byte.  The k-steps of a sub-tile are
-// consecutive.  Rows past the expert's last routed row, and blocks past K, are
-// zero codes with scale 127.
-__device__ __forceinline__ void put_term(uint8_t* rec, int lane, const v6i& c) {
-  *reinterpret_cast<uint4*>(rec + lane * 16) = make_uint4(c[0], c[1], c[2], c[3]);
-  *reinterpret_cast<uint2*>(rec + 1024 + lane * 8) = make_uint2(c[4], c[5]);
+// fourth.  Writes the register image of the MFMA B operand: per unit 3 KB, the
+// 48 bytes of a lane's hi and lo operands (6 words each, in that order) as
+// three chunks of [lane][16 B], so that a wave fetches a k-step with three
+// full-width loads into twelve consecutive registers; the third and fourth
+// terms in the same form in the unit's 3 KB extra record (written only when
+// used); per (row tile, sub-tile, stage of 4 k-steps) [lane][4] u32 scale
+// words, word j for k-step 4 stage + j (hi | lo << 8 | third << 16 | fourth <<
+// 24), one load per stage; and the unit's count of extra terms (0, 1 or 2) in
+// one byte.  The k-steps of a sub-tile are consecutive.  Rows past the
+// expert's last routed row, and blocks past K, are zero codes with scale 127.
+__device__ __forceinline__ void put_term(uint8_t* rec, int lane, const v6i& c, int second) {
+  if (!second) {
+    *reinterpret_cast<uint4*>(rec + lane * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+    *reinterpret_cast<uint2*>(rec + 1024 + lane * 16) = make_uint2(c[4], c[5]);
+  } else {
+    *reinterpret_cast<uint2*>(rec + 1024 + lane * 16 + 8) = make_uint2(c[0], c[1]);
+    *reinterpret_cast<uint4*>(rec + 2048 + lane * 16) = make_uint4(c[2], c[3], c[4], c[5]);
+  }
 }
 
 // Workgroup blk = (row tile t, group of kQSteps k-steps): each wave locates
@@ -303,10 +314,10 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
       v6i c;
       uint32_t byte;
       fp6_term(w, c, byte);
-      put_term((nterm < 2 ? rec : xrec) + 1536 * (nterm & 1), lane, c);
+      put_term(nterm < 2 ? rec : xrec, lane, c, nterm & 1);
       bytes = (bytes & ~(0xffu << (8 * nterm))) | (byte << (8 * nterm));
     }
-    s[unit * 64 + lane] = bytes;
+    s[(unit - g) * 64 + (g >> 2) * 256 + lane * 4 + (g & 3)] = bytes;
     if (lane == 0) qf[unit] = (uint8_t)(nterm - 2);
   }
 }
@@ -359,7 +370,8 @@ __device__ __forceinline__ void repack_panel(int blk, uint32_t* panel, const uin
   __syncthreads();
   const uint8_t* prow = reinterpret_cast<const uint8_t*>(panel) + lead + min(t, rows - 1) * KB;
   const int c = t >> 5, l32 = t & 31;
-  uint32_t* dst = out + ((size_t)e * NT + nt) * NS * (kSubN * 64) + l32 * kSubN + c;
+  if (t >= kBN) return;  // the threads past the panel's rows only helped stage it
+  uint32_t* dst = out + ((size_t)e * NT + nt) * NS * (kSubW * 64) + l32 * kSubW + c;
   for (int s = 0; s < NS; s++) {
     uint32_t b[kStageBlocks];
 #pragma unroll
@@ -370,8 +382,8 @@ __device__ __forceinline__ void repack_panel(int blk, uint32_t* panel, const uin
       w0 |= b[2 * j] << (8 * j);
       w1 |= b[2 * j + 1] << (8 * j);
     }
-    dst[(size_t)s * (kSubN * 64)] = w0;                // lane l32 (h = 0)
-    dst[(size_t)s * (kSubN * 64) + 32 * kSubN] = w1;   // lane l32 + 32 (h = 1)
+    dst[(size_t)s * (kSubW * 64)] = w0;                // lane l32 (h = 0)
+    dst[(size_t)s * (kSubW * 64) + 32 * kSubW] = w1;   // lane l32 + 32 (h = 1)
   }
 }
 
@@ -528,10 +540,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int32_t* __restrict__ sorted_rows, float* __restrict__ out, uint16_t* __restrict__ act) {
   // weight stages, double-buffered: codes [256 rows][8 swizzled blocks] and
   // scale words [64 lanes][8 sub-tiles]
-  __shared__ __attribute__((aligned(16))) uint8_t sB0[kBN * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sB1[kBN * 128];
-  __shared__ __attribute__((aligned(16))) uint32_t sS0[kSubN * 64];
-  __shared__ __attribute__((aligned(16))) uint32_t sS1[kSubN * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBN * 128];
+  __shared__ __attribute__((aligned(16))) uint32_t sS0[kSubW * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t sS1[kSubW * 64];
+  uint8_t* const sB0 = sB[0];
+  uint8_t* const sB1 = sB[1];
   __shared__ __attribute__((aligned(16))) int rows_lds[kBM];  // routed row of each tile row, -1 if none
   __shared__ __attribute__((aligned(16))) float bias_lds[kBN];  // bias of each tile column (0 without bias)
 
@@ -560,7 +573,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     rows_lds[tid] = r;
   }
   // the tile's bias values, read here so that the epilogue waits on no global load
-  bias_lds[tid] = bias ? bf16_bits_to_f32(bias[(size_t)tc.e * N + min(tc.nt * kBN + tid, N - 1)]) : 0.f;
+  if (tid < kBN)
+    bias_lds[tid] = bias ? bf16_bits_to_f32(bias[(size_t)tc.e * N + min(tc.nt * kBN + tid, N - 1)]) : 0.f;
   const bool valid = wave * 32 < tc.m_count;
 
   // activations: this wave's row sub-tile, k-steps consecutive.  Buffer
@@ -572,7 +586,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(as + unit0 * 64), (short)0, NKP * 256, kBufferFlags);
 
-  // weight stage pieces: piece i = wave + 4q (q < 8) covers tile rows 8i ..
+  // weight stage pieces: piece i = wave + 4q (q < kSubN) covers tile rows 8i ..
   // 8i + 7 (1 KB); lane L takes row 8i + L / 8 and LDS slot L % 8, which holds
   // block (L % 8) ^ swizzle(row) of the stage (rows past N re-read row N - 1,
   // blocks past K re-read block K - 1)
@@ -586,26 +600,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // weight-scale words: the 2 KB of a stage as two 1 KB halves; waves of equal
   // parity move the same half (the same bytes to the same place)
   const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(wsc + ((size_t)e * NT + tc.nt) * NS * kSubN * 64), (short)0, NS * kSubN * 256,
+      const_cast<uint32_t*>(wsc + ((size_t)e * NT + tc.nt) * NS * kSubW * 64), (short)0, NS * kSubW * 256,
       kBufferFlags);
   const int bs_off = (wave & 1) * 1024 + lane * 16;
 
-  // A stage's weights move in two halves (pieces q = 4h .. 4h + 3), the
-  // second with the scale words, through 4 (5) registers of 16 bytes.
-  u32x4_t rb[5];
-  auto load_b = [&](int s, int h) {
+  // A stage's weights move global -> registers -> LDS, 6 pieces and the
+  // stage's scale words per wave.  Two register sets: set s % 2 is loaded with
+  // stage s + 2 at the start of stage s (it held stage s, which is in LDS by
+  // then) and written to LDS at the end of stage s + 1, so the loads have two
+  // stages to arrive (HBM latency under load is about two k-steps' work).
+  u32x4_t rbs[2][kSubN + 1];
+  auto load_w = [&](int s, auto xc) {
+    constexpr int X = decltype(xc)::value;
     const int blk = min(kStageBlocks * s + b_blk, KB - 1) * 16;
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-      rb[q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(b_r0 + 32 * (4 * h + q), N - 1) * (KB * 16) + blk, 0,
-                                                    0);
-    if (h) rb[4] = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, bs_off, s * (kSubN * 64 * 4), 0);
+    for (int q = 0; q < kSubN; q++)
+      rbs[X][q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(b_r0 + 32 * q, N - 1) * (KB * 16) + blk, 0, 0);
+    rbs[X][kSubN] = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, bs_off, s * (kSubW * 64 * 4), 0);
   };
-  auto store_b = [&](uint8_t* sb, uint32_t* ss, int h) {
+  auto store_w = [&](uint8_t* sb, uint32_t* ss, auto xc) {
+    constexpr int X = decltype(xc)::value;
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-      *reinterpret_cast<u32x4_t*>(sb + (wave + 4 * (4 * h + q)) * 1024 + lane * 16) = rb[q];
-    if (h) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(ss) + (wave & 1) * 1024 + lane * 16) = rb[4];
+    for (int q = 0; q < kSubN; q++) *reinterpret_cast<u32x4_t*>(sb + (wave + 4 * q) * 1024 + lane * 16) = rbs[X][q];
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(ss) + (wave & 1) * 1024 + lane * 16) = rbs[X][kSubN];
   };
 
   // this lane's offsets into a stage for the k-step j: row l32 of each 32-row
@@ -623,19 +640,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   v16f acc[kSubN];
 
   // activation ring: k-step g lives in slot g % 2 from its load (two k-steps
-  // ahead) until it is multiplied
-  v6i rh[kAhead], rl[kAhead];  // the hi and lo operands
-  uint32_t rs[kAhead];
+  // ahead) until it is multiplied: three full-width loads of the unit's hi and
+  // lo operands.  The scale words of a stage's four k-steps are one load,
+  // made during the stage before.
+  v12i ra[kAhead];
+  u32x4_t asw[2];
   auto load_a = [&](int g, auto jc) {
     constexpr int J = decltype(jc)::value % kAhead;
     const int so = g * kAUnit;
-    const u32x4_t h0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16, so, 0);
-    const u32x2_t h1 = __builtin_amdgcn_raw_buffer_load_b64(a_rsrc, lane * 8 + 1024, so, 0);
-    const u32x4_t l0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16 + 1536, so, 0);
-    const u32x2_t l1 = __builtin_amdgcn_raw_buffer_load_b64(a_rsrc, lane * 8 + 2560, so, 0);
-    rh[J] = v6i{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y};
-    rl[J] = v6i{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y};
-    rs[J] = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc, lane * 4, g * 256, 0);
+    const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16, so, 0);
+    const u32x4_t c1 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16 + 1024, so, 0);
+    const u32x4_t c2 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16 + 2048, so, 0);
+    ra[J] = v12i{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y,
+                 (int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
+  };
+  auto load_as = [&](int s, auto xc) {
+    asw[decltype(xc)::value] = __builtin_amdgcn_raw_buffer_load_b128(as_rsrc, lane * 16, s * 1024, 0);
   };
 
   using J0 = std::integral_constant<int, 0>;
@@ -653,17 +673,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // One k-step J of a stage: for each weight sub-tile c the hi and lo MFMAs,
   // then (NEXT) the read of sub-tile c for k-step J + 1 into the registers
   // they just freed, so the LDS latency hides under the remaining MFMAs.
-  auto kstep = [&](const uint8_t* sb, const uint32_t (&bsc)[kSubN], auto jc, bool next) {
+  auto kstep = [&](const uint8_t* sb, const uint32_t (&bsc)[kSubN], uint32_t sw, auto jc, bool next) {
     constexpr int J = decltype(jc)::value;
     constexpr int A = J % kAhead;
-    const v8i ahi = __builtin_shufflevector(rh[A], rh[A], 0, 1, 2, 3, 4, 5, -1, -1);
-    const v8i alo = __builtin_shufflevector(rl[A], rl[A], 0, 1, 2, 3, 4, 5, -1, -1);
+    const v8i ahi = __builtin_shufflevector(ra[A], ra[A], 0, 1, 2, 3, 4, 5, -1, -1);
+    const v8i alo = __builtin_shufflevector(ra[A], ra[A], 6, 7, 8, 9, 10, 11, -1, -1);
 #pragma unroll
     for (int c = 0; c < kSubN; c++) {
       acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[c], ahi, acc[c], kFmtFp4E2M1, kFmtFp6E2M3, J,
-                                                               bsc[c], 0, rs[A]);
+                                                               bsc[c], 0, sw);
       acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[c], alo, acc[c], kFmtFp4E2M1, kFmtFp6E2M3, J,
-                                                               bsc[c], 1, rs[A]);
+                                                               bsc[c], 1, sw);
       if (next) read_b(sb, c, (J + 1) & 3);
       // the read stays here, 7 sub-tiles ahead of its MFMAs
       pipeline_fence();
@@ -675,73 +695,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // meets the barriers).  Slot s % 2 holds stage s (NS is even).
   auto pipeline = [&](auto vc) {
     constexpr bool V = decltype(vc)::value;
-    // One stage s from slot (sb, ss): multiply its four k-steps, each followed
-    // by the activation loads of the k-step two ahead (none past the last);
-    // meanwhile move the next stage's weights into the other slot (nb, ns),
-    // half loaded at the start and written after the second k-step, half
-    // loaded then and written at the end; then meet the other waves.  The other
-    // slot was last read in stage s - 1, which every wave finished before the
-    // barrier that ended it.  The compiler fences keep each load where it is
-    // written: otherwise it sinks next to its use and exposes its latency.
-    auto stage = [&](int s, const uint8_t* sb, const uint32_t* ss, uint8_t* nb, uint32_t* ns, bool last) {
-      if (!last) load_b(s + 1, 0);
-      auto mid = [&]() {
-        if (!last) {
-          store_b(nb, ns, 0);
-          load_b(s + 1, 1);
-        }
-      };
-      if (!V) mid();
+    // One stage s from slot (sb, ss), register set X = s % 2: load stage s + 2
+    // into set X; multiply the four k-steps, each followed by the activation
+    // loads of the k-step two later (none past the last); then write set
+    // 1 - X (stage s + 1, loaded during stage s - 1) into the other slot (nb,
+    // ns) and meet the other waves.  The other slot was last read in stage
+    // s - 1, which every wave finished before the barrier that ended it.  The
+    // compiler fences keep each load where it is written: otherwise it sinks
+    // next to its use and exposes its latency.
+    // Mode M: 0 a stage with two after it, 1 the next-to-last, 2 the last.
+    auto stage = [&](int s, const uint8_t* sb, const uint32_t* ss, uint8_t* nb, uint32_t* ns, auto xc, auto mc) {
+      constexpr int X = decltype(xc)::value;
+      constexpr int M = decltype(mc)::value;
+      constexpr bool last = M == 2;
+      if (M == 0) load_w(s + 2, xc);
+      pipeline_fence();
       if (V) {
         uint32_t bsc[kSubN];
-        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(ss + lane * kSubN);
-        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(ss + lane * kSubN + 4);
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(ss + lane * kSubW);
+        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(ss + lane * kSubW + 4);
+        static_assert(kSubN == 6, "the scale words of 6 sub-tiles");
         bsc[0] = v0.x; bsc[1] = v0.y; bsc[2] = v0.z; bsc[3] = v0.w;
-        bsc[4] = v1.x; bsc[5] = v1.y; bsc[6] = v1.z; bsc[7] = v1.w;
+        bsc[4] = v1.x; bsc[5] = v1.y;
 #pragma unroll
         for (int c = 0; c < kSubN; c++) read_b(sb, c, 0);
         const int g = s * kStepsPerStage;
         pipeline_fence();  // the reads are issued before the first MFMA
+        const u32x4_t sw = asw[X];
         if (!last) {
-          kstep(sb, bsc, J0{}, true);
+          // each k-step is followed by the activation loads of the k-step
+          // two later, into the ring slot it just freed; the next stage's
+          // scale words go with the first of its k-steps
+          kstep(sb, bsc, sw.x, J0{}, true);
           load_a(g + 2, J2{});
           pipeline_fence();
-          kstep(sb, bsc, J1{}, true);
+          kstep(sb, bsc, sw.y, J1{}, true);
           load_a(g + 3, J3{});
-          mid();
           pipeline_fence();
-          kstep(sb, bsc, J2{}, true);
+          kstep(sb, bsc, sw.z, J2{}, true);
+          load_as(s + 1, std::integral_constant<int, 1 - X>{});
           load_a(g + 4, J0{});
           pipeline_fence();
-          kstep(sb, bsc, J3{}, false);
+          kstep(sb, bsc, sw.w, J3{}, false);
           load_a(g + 5, J1{});
           pipeline_fence();
         } else {
           // the last stage: k-steps past the last real block are skipped
-          kstep(sb, bsc, J0{}, true);
+          kstep(sb, bsc, sw.x, J0{}, true);
           load_a(g + 2, J2{});
           pipeline_fence();
-          if (g + 1 < nks) kstep(sb, bsc, J1{}, true);
+          if (g + 1 < nks) kstep(sb, bsc, sw.y, J1{}, true);
           load_a(g + 3, J3{});
           pipeline_fence();
-          if (g + 2 < nks) kstep(sb, bsc, J2{}, true);
-          if (g + 3 < nks) kstep(sb, bsc, J3{}, false);
+          if (g + 2 < nks) kstep(sb, bsc, sw.z, J2{}, true);
+          if (g + 3 < nks) kstep(sb, bsc, sw.w, J3{}, false);
         }
       }
       if (!last) {
-        store_b(nb, ns, 1);
+        store_w(nb, ns, std::integral_constant<int, 1 - X>{});
         lds_barrier();
       }
     };
 
-    load_b(0, 0);
+    load_w(0, J0{});
+    load_w(1, J1{});
     if (V) {
+      load_as(0, J0{});
       load_a(0, J0{});
       load_a(1, J1{});
     }
-    store_b(sB0, sS0, 0);
-    load_b(0, 1);
-    store_b(sB0, sS0, 1);
+    store_w(sB0, sS0, J0{});
     lds_barrier();
     if (V) {
       // the sums start at the bias of their columns (bias_lds is complete)
@@ -754,14 +777,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           for (int i = 0; i < 4; i++) acc[c][4 * q + i] = b[i];
         }
     }
+    using M0 = std::integral_constant<int, 0>;
+    using M1 = std::integral_constant<int, 1>;
+    using M2 = std::integral_constant<int, 2>;
     int s = 0;
 #pragma unroll
     for (; s + 2 < NS; s += 2) {
-      stage(s, sB0, sS0, sB1, sS1, false);
-      stage(s + 1, sB1, sS1, sB0, sS0, false);
+      stage(s, sB0, sS0, sB1, sS1, J0{}, M0{});
+      stage(s + 1, sB1, sS1, sB0, sS0, J1{}, M0{});
     }
-    stage(s, sB0, sS0, sB1, sS1, false);  // s = NS - 2
-    stage(s + 1, sB1, sS1, nullptr, nullptr, true);
+    stage(s, sB0, sS0, sB1, sS1, J0{}, M1{});  // s = NS - 2
+    stage(s + 1, sB1, sS1, nullptr, nullptr, J1{}, M2{});
   };
   if (valid)
     pipeline(std::true_type{});
@@ -799,19 +825,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int c = 0; c < kSubN; c++)
         wq[c] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(n0 + 32 * c + l32, N - 1) * (KB * 16) + blk, 0, 0);
-      const u32x4_t s0 = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, lane * 32, (g >> 2) * (kSubN * 64 * 4), 0);
-      const u32x4_t s1 = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, lane * 32 + 16, (g >> 2) * (kSubN * 64 * 4), 0);
-      const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc, lane * 4, g * 256, 0);
+      const u32x4_t s0 = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, lane * 32, (g >> 2) * (kSubW * 64 * 4), 0);
+      const u32x2_t s1 = __builtin_amdgcn_raw_buffer_load_b64(bs_rsrc, lane * 32 + 16, (g >> 2) * (kSubW * 64 * 4), 0);
+      const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc, lane * 16 + (g & 3) * 4, (g >> 2) * 1024, 0);
       const uint8_t* xr = aqx + (unit0 + g) * kAUnit;
       const int sh = 8 * (g & 3);
-      const uint32_t wsc8[kSubN] = {s0.x >> sh, s0.y >> sh, s0.z >> sh, s0.w >> sh,
-                                    s1.x >> sh, s1.y >> sh, s1.z >> sh, s1.w >> sh};
-      auto term = [&](const uint8_t* rec) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(rec + lane * 16);
-        const u32x2_t b = *reinterpret_cast<const u32x2_t*>(rec + 1024 + lane * 8);
-        return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, 0, 0};
-      };
-      const v8i t2 = term(xr);
+      const uint32_t wsc8[kSubN] = {s0.x >> sh, s0.y >> sh, s0.z >> sh, s0.w >> sh, s1.x >> sh, s1.y >> sh};
+      // the extra record in the layout of the main one: the third term's six
+      // words, then the fourth's
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(xr + lane * 16);
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(xr + 1024 + lane * 16);
+      const v8i t2 = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, 0, 0};
 #pragma unroll
       for (int c = 0; c < kSubN; c++) {
         const v8i wa = v8i{(int)wq[c].x, (int)wq[c].y, (int)wq[c].z, (int)wq[c].w, 0, 0, 0, 0};
@@ -819,7 +843,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                                                                  wsc8[c], 2, sw);
       }
       if (n > 1) {
-        const v8i t3 = term(xr + 1536);
+        const u32x4_t x2 = *reinterpret_cast<const u32x4_t*>(xr + 2048 + lane * 16);
+        const v8i t3 = v8i{(int)x1.z, (int)x1.w, (int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, 0, 0};
 #pragma unroll
         for (int c = 0; c < kSubN; c++) {
           const v8i wa = v8i{(int)wq[c].x, (int)wq[c].y, (int)wq[c].z, (int)wq[c].w, 0, 0, 0, 0};
@@ -833,12 +858,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- epilogue: scatter to the routed rows (bias included).  Each lane
   // holds one routed row and, per accumulator, 4 runs of 4 consecutive
   // columns.  The wide paths pass the wave's results through its own 8 KB of
-  // weight slot 0 (no wave reads that slot after the barrier that ends the
-  // next-to-last stage), so that each store instruction writes 4 rows x 256
-  // contiguous bytes: whole 128-byte lines, as HBM wants them (stores of 32
-  // bytes per row slow down every workgroup still streaming its operands).
+  // the weight slots (free once every wave has passed the barrier below), so
+  // that each store instruction writes 4 rows x 256 contiguous bytes: whole
+  // 128-byte lines, as HBM wants them (stores of 32 bytes per row slow down
+  // every workgroup still streaming its operands).
+  // every wave is past the main loop: both weight slots are free for staging
+  lds_barrier();
   if (!valid) return;
-  uint8_t* st = sB0 + wave * 8192;  // [32 rows][16 pieces of 16 bytes], XOR-swizzled
+  uint8_t* st = sB[0] + wave * 8192;  // [32 rows][16 pieces of 16 bytes], XOR-swizzled (slots 0 and 1)
+  static_assert(kWaves * 8192 <= 2 * kBN * 128, "the staging fits the weight slots");
   auto st_at = [&](int row, int piece) { return st + row * 256 + ((piece ^ (row & 15)) << 4); };
   // the rows a lane stores: row 4 i + lane / 16 of the wave's 32, piece lane % 16
   auto out_rows = [&](int (&rr)[8]) {
@@ -875,12 +903,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       out_rows(rr);
       asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
       const int col = a0 + 8 * piece;  // NA % 8 == 0: a piece is wholly inside or outside
+      // a row of the panel's activations is 2 kSubN pieces; the lanes of the
+      // other pieces have nothing to store
+      const bool piece_ok = piece < 2 * kSubN;
       u32x4_t v[8];  // all reads first: one wait, not one per store
 #pragma unroll
       for (int i = 0; i < 8; i++) v[i] = *reinterpret_cast<const u32x4_t*>(st_at(4 * i + (lane >> 4), piece));
 #pragma unroll
       for (int i = 0; i < 8; i++)
-        if (rr[i] >= 0 && col < NA)
+        if (piece_ok && rr[i] >= 0 && col < NA)
           __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4_t*>(act + (size_t)rr[i] * NA + col));
       return;
     }
@@ -901,13 +932,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // streamed out: the outputs must not push the weights and activation tiles
   // other workgroups still read out of the caches
   if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-    // four rounds of 64 columns (accumulators 2 rnd, 2 rnd + 1): element run
+    // kSubN / 2 rounds of 64 columns (accumulators 2 rnd, 2 rnd + 1): element run
     // (c, q) of a lane is piece 8 (c - 2 rnd) + 2 q + half of its row; the
     // columns are a multiple of 4, so col < N covers a whole piece
     int rr[8];
     out_rows(rr);
 #pragma unroll
-    for (int rnd = 0; rnd < 4; rnd++) {
+    for (int rnd = 0; rnd < kSubN / 2; rnd++) {
 #pragma unroll
       for (int cc = 0; cc < 2; cc++)
 #pragma unroll
@@ -966,7 +997,7 @@ GemmLayout gemm_layout(int E, int N, int T, int k, int K) {
   l.scales = l.extra + al(units * kAUnit);
   l.flags = l.scales + al(units * 256);
   l.wscales = l.flags + al(units);
-  l.total = l.wscales + al((size_t)E * nt * ns * kSubN * 256);
+  l.total = l.wscales + al((size_t)E * nt * ns * kSubW * 256);
   return l;
 }
 

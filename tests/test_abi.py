@@ -158,7 +158,7 @@ def test_workspace_size():
     # unit): 3 KB of codes for the two terms every block has, 3 KB for the third
     # and fourth terms of the units that take them, 256 bytes of scale words and
     # one byte with the unit's count of extra terms; the weight scales are
-    # repacked to 2 KB per expert, 256-row panel (5760 rows = 23 panels) and
+    # repacked to 2 KB per expert, 192-row panel (5760 rows = 30 panels) and
     # stage.  Each region starts on a 256-byte boundary.
     al = lambda v: (v + 255) // 256 * 256
 
@@ -167,12 +167,12 @@ def test_workspace_size():
         return al(units * 3072) * 2 + al(units * 256) + al(units) + al(E * panels * stages * 2048)
 
     tiles = 16384 // 128 + 32
-    assert ws(32, 5760, 4096, 4, 2880, 0, 2) == want(tiles, 48, 32, 23, 12)
-    assert ws(32, 2880, 2048, 4, 2880, 1, 0) == want(64 + 32, 48, 32, 12, 12)
+    assert ws(32, 5760, 4096, 4, 2880, 0, 2) == want(tiles, 48, 32, 30, 12)
+    assert ws(32, 2880, 2048, 4, 2880, 1, 0) == want(64 + 32, 48, 32, 15, 12)
     # K = 64: one stage, padded to 2 (8 k-steps); 1024 rows over 8 experts: 8 + 8 tiles
-    assert ws(8, 256, 512, 2, 64, 1, 2) == want(16, 8, 8, 1, 2)
+    assert ws(8, 256, 512, 2, 64, 1, 2) == want(16, 8, 8, 2, 2)
     # fewer rows than experts: at most one partial tile per row
-    assert ws(32, 256, 3, 2, 64, 0, 2) == want(1 + 6, 8, 32, 1, 2)
+    assert ws(32, 256, 3, 2, 64, 0, 2) == want(1 + 6, 8, 32, 2, 2)
     assert ws(32, 5760, 4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(0, 5760, 4, 4, 128, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(32, 0, 4, 4, 128, 0, 2) == ctypes.c_size_t(-1).value
