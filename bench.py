@@ -99,7 +99,8 @@ def fusable(p):
 
 
 class Workload:
-    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0, fused: bool = False, swiglu: bool = False):
+    def __init__(self, cfg_index: int, rotate_bytes: int, path: int = 0, fused: bool = False, swiglu: bool = False,
+                 combine_fused: bool = False):
         import torch
         from mxfp4_mixture_experts_amd import synthetic as S
         from mxfp4_mixture_experts_amd.runner import DeviceProblem
@@ -107,6 +108,8 @@ class Workload:
         self.p = S.make_config(cfg_index)
         self.fused = fused and fusable(self.p)
         self.swiglu = swiglu
+        # many tokens: the projection with the combine fused in (mxfp4_expert_proj_combine_routed)
+        self.combine_fused = combine_fused and self.p.combine and self.p.logits is not None and not swiglu
         self.dp = DeviceProblem(self.p, device="cuda:0", path=path)
         self.dp.route_group()            # the device's own routing decides which experts are touched
         counts = torch.diff(self.dp.offsets.to(torch.int64)).cpu().numpy()
@@ -120,6 +123,10 @@ class Workload:
 
     def step(self, i, stream=None):
         b, s = self.weights[i % self.copies]
+        if self.combine_fused:
+            self.dp.route_group(stream)
+            self.dp.proj_combine_routed(stream, blocks=b, scales=s)
+            return
         if self.fused and self.swiglu:
             self.dp.decode_swiglu(stream, blocks=b, scales=s)
             return
@@ -137,7 +144,9 @@ class Workload:
     def proj_only(self, i, stream=None):
         """The dominant kernel alone: the projection (the single-launch decode when fused)."""
         b, s = self.weights[i % self.copies]
-        if self.fused and self.swiglu:
+        if self.combine_fused:
+            self.dp.proj_combine_routed(stream, blocks=b, scales=s)
+        elif self.fused and self.swiglu:
             self.dp.decode_swiglu(stream, blocks=b, scales=s)
         elif self.fused:
             self.dp.decode(stream, blocks=b, scales=s)
@@ -176,10 +185,11 @@ class Workload:
         return e0.elapsed_time(e1), t1 - t0
 
 
-def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fused=False, swiglu=False):
+def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fused=False, swiglu=False,
+            combine_fused=False):
     """Time `steps` whole-path steps and, separately, back-to-back launches of the
     projection alone (for the kernel's roofline)."""
-    w = Workload(cfg_index, rotate_bytes, path, fused, swiglu)
+    w = Workload(cfg_index, rotate_bytes, path, fused, swiglu, combine_fused)
     for i in range(warmup):
         w.step(i)
     w.torch.cuda.synchronize()
@@ -470,8 +480,11 @@ def main():
         # the other model-size workloads, then the two gate_up workloads through
         # the fused gated activation (bf16 [T, k, N / 2], the down projection's input)
         # (the one-token one as a single launch, mxfp4_moe_decode_swiglu)
-        for cfg, steps, swiglu in ((2, 100, False), (3, 20, False), (4, 40, False), (1, 200, True), (3, 20, True)):
-            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu, fused=swiglu)
+        # (and the down prefill once more with the combine fused into the grouped GEMM)
+        for cfg, steps, swiglu, cf in ((2, 100, False, False), (3, 20, False, False), (4, 40, False, False),
+                                       (1, 200, True, False), (3, 20, True, False), (4, 40, False, True)):
+            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu, fused=swiglu,
+                        combine_fused=cf)
             a = r["acc"]
             if cfg == 3 and not swiglu:
                 # the prefill half of the metric: the grouped GEMM at the gate_up prefill
@@ -494,10 +507,13 @@ def main():
             t_step = r["ms_per_step"] * 1e-3
             t_proj = r["proj_us"] * 1e-6
             roof_t = max(a["flops"] / (MXFP4_PEAK_TFLOPS * 1e12), a["step"] / (HBM_PEAK_GBS * 1e9))
-            a_proj = a["proj"] + (a["route"] if r["fused"] else 0)   # the single launch routes too
+            # the single launch routes too; the fused combine reads and writes the combine's bytes
+            a_proj = a["proj"] + (a["route"] if r["fused"] else 0) + (a["combine"] if cf else 0)
             sec.append({
                 "workload": describe(r["p"], swiglu) + (" (routing + projection + activation in one launch)"
-                                                        if r["fused"] else ""),
+                                                        if r["fused"] else "")
+                            + (" (the combine fused into the grouped GEMM: route_group + "
+                               "mxfp4_expert_proj_combine_routed; proj_us covers both)" if cf else ""),
                 "ms_per_step": round(r["ms_per_step"], 4),
                 "step_GBps": round(a["step"] / t_step / 1e9, 1),
                 "step_TFLOPs": round(a["flops"] / t_step / 1e12, 2),

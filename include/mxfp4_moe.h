@@ -330,6 +330,42 @@ int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, cons
                               const float* gates, float* out, float* y, void* stream);
 
 /*
+ * The routed projection of many tokens and the gate-weighted combine:
+ * mxfp4_expert_proj followed by moe_combine, with the same out and y bit for
+ * bit whenever every unrouted slot has gate 0 (as mxfp4_moe_route_group
+ * writes them).  On the grouped-GEMM path the combine runs inside the GEMM:
+ * per (token, 192-column weight panel) an arrival counter in the workspace,
+ * set by the GEMM's pre-pass, counts the token's routed rows as their tiles
+ * finish, and the tile that brings the last of them sums the token's k rows
+ * over its panel in slot order.  On the GEMV path the combine is a second
+ * launch.
+ * (src/experts.linnet fn forward_routed: the routed rows' down products
+ * summed per token with the router weights; fn down_bias_of: the bias
+ * weighed by them, already inside out here.)
+ *
+ *   blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets,
+ *   sorted_rows, path, workspace, workspace_bytes: as for mxfp4_expert_proj
+ *           (the same workspace size).
+ *   topk_ids [T, k] i32, gates [T, k] f32: the routing that expert_offsets and
+ *           sorted_rows group, from the same mxfp4_moe_route_group call.  A slot
+ *           is routed when its id lies in [0, E); the grouping must hold
+ *           exactly the routed slots (otherwise y is unspecified, though every
+ *           access stays inside the arrays).
+ *   out     [T, k, N] f32 out, as mxfp4_expert_proj writes it.
+ *   y       [T, N] f32 out: y[t, n] = sum over slots s, in slot order, of
+ *           gates[t, s] * out[t, s, n], one fused multiply-add per slot; an
+ *           unrouted slot or one with gate 0 adds a zero product.  A token with
+ *           no routed slot gets y = 0.
+ * Deterministic: the sum order does not depend on the order in which tiles
+ * finish.  T = 0 returns MXFP4_OK and enqueues nothing.
+ */
+int mxfp4_expert_proj_combine_routed(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E,
+                                     int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                                     const int32_t* topk_ids, const float* gates, const int32_t* expert_offsets,
+                                     const int32_t* sorted_rows, float* out, float* y, int path, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * MXFP4 -> bf16 dequantization of a weight tensor, in its own layout.
  * (README "MXFP4": rows of 32-element blocks, 16 code bytes per block with the
  * even element in the low nibble, one E8M0 scale byte per block, a weight is

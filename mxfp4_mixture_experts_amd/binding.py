@@ -39,6 +39,7 @@ ENTRY_POINTS = (
     "mxfp4_moe_decode_swiglu",
     "mxfp4_expert_proj_combine",
     "mxfp4_expert_proj_noalloc",
+    "mxfp4_expert_proj_combine_routed",
 )
 
 _lib_handle = None
@@ -95,6 +96,9 @@ def load_library():
     lib.mxfp4_moe_decode_swiglu.restype = i32
     lib.mxfp4_expert_proj_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.mxfp4_expert_proj_combine.restype = i32
+    lib.mxfp4_expert_proj_combine_routed.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp,
+                                                     vp, vp, i32, vp, sz, vp]
+    lib.mxfp4_expert_proj_combine_routed.restype = i32
     _lib_handle = lib
     return lib
 
@@ -301,4 +305,27 @@ def mxfp4_expert_proj_combine(blocks, scales, bias, E: int, N: int, K: int, x, x
         _ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(E),
         int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(k), _ptr(topk_ids, "topk_ids", _I32, dev),
         _ptr(gates, "gates", _F32, dev), _ptr(out, "out", _F32, dev), _ptr(y, "y", _F32, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_expert_proj_combine_routed(blocks, scales, bias, E: int, N: int, K: int, x, x_per_slot: bool, T: int,
+                                     k: int, topk_ids, gates, expert_offsets, sorted_rows, out, y,
+                                     path: int = MXFP4_PATH_AUTO, workspace=None, stream=None):
+    """The routed projection of T tokens and the gate-weighted combine
+    (mxfp4_expert_proj_combine_routed): out [T,k,N] f32 and y [T,N] f32, equal to
+    mxfp4_expert_proj followed by moe_combine; the combine is fused into the
+    grouped GEMM.  workspace: as for mxfp4_expert_proj."""
+    lib = load_library()
+    dev = y.device
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, "workspace", _U8, dev)
+        ws_bytes = workspace.numel()
+    st = lib.mxfp4_expert_proj_combine_routed(
+        _ptr(blocks, "blocks", _U8, dev), _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev),
+        int(E), int(N), int(K), _ptr(x, "x", _BF16, dev), int(bool(x_per_slot)), int(T), int(k),
+        _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(out, "out", _F32, dev), _ptr(y, "y", _F32, dev), int(path), ws_ptr, ctypes.c_size_t(ws_bytes),
+        _stream(stream, dev))
     _check(st)

@@ -79,11 +79,14 @@ bool gemv_fits(int T, int K) { return mxfp4::gemv_lds_bytes(T, K) <= 160 * 1024 
 static_assert(mxfp4::kGemmStaticScratchBytes == MXFP4_NOALLOC_SCRATCH_BYTES, "one size for the static scratch");
 
 // noalloc: the grouped GEMM's scratch is the library's static device array
-// (workspace and workspace_bytes are ignored).
+// (workspace and workspace_bytes are ignored).  y != NULL: out, then y [T, N]
+// = the gate-weighted combine of each token's routed slots (ids, gates [T, k]),
+// fused into the grouped GEMM, after the projection on the GEMV path.
 int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                      const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
                      const int32_t* sorted_rows, float* out, uint16_t* act, int path, void* workspace,
-                     size_t workspace_bytes, void* stream, bool noalloc = false) {
+                     size_t workspace_bytes, void* stream, bool noalloc = false, const int32_t* ids = nullptr,
+                     const float* gates = nullptr, float* y = nullptr) {
   g_last_error[0] = '\0';
   if (E < 1 || E > MXFP4_MAX_EXPERTS) return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_MAX_EXPERTS);
   if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
@@ -98,6 +101,9 @@ int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_
   if (T == 0) return MXFP4_OK;
   if (!blocks || !scales || !x || !expert_offsets || !sorted_rows || (!out && !act))
     return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (y && (!out || !ids || !gates)) return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (y && (size_t)T * k * N * 4 > 0xFFFFFFFFull)
+    return fail(MXFP4_ERR_INVALID_ARG, "out [T, k, N] f32 must stay under 4 GiB for the fused combine");
   if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
   const int p = resolve_path(path, T, k, E);
   if (p == MXFP4_PATH_GEMV && !gemv_fits(T, K))
@@ -126,12 +132,15 @@ int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_
     if (se != hipSuccess) return hip_fail(se, "static scratch address");
   }
   hipError_t e;
-  if (p == MXFP4_PATH_GEMV)
+  if (p == MXFP4_PATH_GEMV) {
     e = mxfp4::launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
                                   out, act, static_cast<hipStream_t>(stream));
-  else
+    if (e == hipSuccess && y)
+      e = mxfp4::launch_combine(out, gates, T, k, N, y, static_cast<hipStream_t>(stream), ids, E);
+  } else {
     e = mxfp4::launch_expert_gemm(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
-                                  out, act, workspace, static_cast<hipStream_t>(stream));
+                                  out, act, workspace, static_cast<hipStream_t>(stream), ids, gates, y);
+  }
   if (e != hipSuccess) return hip_fail(e, "expert_proj launch");
   return MXFP4_OK;
 }
@@ -311,6 +320,19 @@ int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, cons
                                                y, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "expert_proj_combine launch");
   return MXFP4_OK;
+}
+
+int mxfp4_expert_proj_combine_routed(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E,
+                                     int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                                     const int32_t* topk_ids, const float* gates, const int32_t* expert_offsets,
+                                     const int32_t* sorted_rows, float* out, float* y, int path, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (T > 0 && (!topk_ids || !gates || !out || !y)) {
+    g_last_error[0] = '\0';
+    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  }
+  return expert_proj_impl(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows, out,
+                          nullptr, path, workspace, workspace_bytes, stream, false, topk_ids, gates, y);
 }
 
 int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, long long rows, int K, uint16_t* out,

@@ -9,6 +9,8 @@
 // whose gate is 0 adds nothing, whatever its row holds: the routing gives gate
 // 0 to the slots it could not route, whose projection rows are never written.
 // (For a finite value v, fma(0, v, acc) = acc, so this changes no other sum.)
+// Called with the routing's ids, a slot whose id lies outside [0, E) (never
+// projected) adds a zero product too, whatever its gate.
 // The kernel is a pure HBM stream: each thread owns 4 consecutive columns of
 // one token (128-bit loads and stores), the k gates of the token are read
 // once per thread from the cache.
@@ -21,9 +23,16 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 
+// the weight of slot row r: its gate, or 0 where ids marks the slot unrouted
+__device__ __forceinline__ float slot_gate(const float* __restrict__ gates, const int32_t* __restrict__ ids, int E,
+                                           size_t r) {
+  const float g = gates[r];
+  return (ids && (unsigned)ids[r] >= (unsigned)E) ? 0.f : g;
+}
+
 __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(
     const float* __restrict__ proj, const float* __restrict__ gates, int T, int k, int N4,
-    float* __restrict__ y) {
+    float* __restrict__ y, const int32_t* __restrict__ ids, int E) {
   const size_t total = (size_t)T * N4;
   const size_t stride = (size_t)gridDim.x * kCombineThreads;
   for (size_t i = (size_t)blockIdx.x * kCombineThreads + threadIdx.x; i < total; i += stride) {
@@ -34,7 +43,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(
     for (int s = 0; s < k; s++) {
       const float g = gates[t * k + s];
       float4 v = load_nt(p + (size_t)s * N4);  // unconditional: no branch per load
-      if (g == 0.f) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (slot_gate(gates, ids, E, t * k + s) == 0.f) v = make_float4(0.f, 0.f, 0.f, 0.f);
       acc.x = fmaf(g, v.x, acc.x);
       acc.y = fmaf(g, v.y, acc.y);
       acc.z = fmaf(g, v.z, acc.z);
@@ -46,7 +55,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(
 
 __global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
     const float* __restrict__ proj, const float* __restrict__ gates, int T, int k, int N,
-    float* __restrict__ y) {
+    float* __restrict__ y, const int32_t* __restrict__ ids, int E) {
   const size_t total = (size_t)T * N;
   const size_t stride = (size_t)gridDim.x * kCombineThreads;
   for (size_t i = (size_t)blockIdx.x * kCombineThreads + threadIdx.x; i < total; i += stride) {
@@ -56,7 +65,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
     for (int s = 0; s < k; s++) {
       const float g = gates[t * k + s];
       const float v = proj[(t * k + s) * N + n];
-      acc = fmaf(g, g == 0.f ? 0.f : v, acc);
+      acc = fmaf(g, slot_gate(gates, ids, E, t * k + s) == 0.f ? 0.f : v, acc);
     }
     y[i] = acc;
   }
@@ -65,17 +74,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
 }  // namespace
 
 hipError_t launch_combine(const float* proj, const float* gates, int T, int k, int N, float* y,
-                          hipStream_t stream) {
+                          hipStream_t stream, const int32_t* ids, int E) {
   const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(proj) | reinterpret_cast<uintptr_t>(y)) % 16 == 0);
   const size_t items = (size_t)T * (vec ? N / 4 : N);
   size_t blocks = (items + kCombineThreads - 1) / kCombineThreads;
   if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
   if (vec)
     hipLaunchKernelGGL(combine_vec4_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
-                       gates, T, k, N / 4, y);
+                       gates, T, k, N / 4, y, ids, E);
   else
     hipLaunchKernelGGL(combine_scalar_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
-                       gates, T, k, N, y);
+                       gates, T, k, N, y, ids, E);
   return hipGetLastError();
 }
 

@@ -387,10 +387,29 @@ __device__ __forceinline__ void repack_panel(int blk, uint32_t* panel, const uin
   }
 }
 
-// The two passes before the GEMM in one launch (they are independent, so
-// their workgroups run side by side): workgroups [0, nrep) repack the weight
-// scales of one (expert, panel) each, the rest quantize one (row tile,
-// k-step) each.  Dynamic LDS: a panel's scale rows.
+// ---------------------------------------------------------------------------
+// arrival counters of the fused combine: thread = one token t.  Its counter
+// of every weight panel starts at k minus its routed slots (ids in [0, E)),
+// so that the last routed row to arrive finds k - 1.  A token with no routed
+// slot gets no arrival: its y row is written here, as the combine of k zero
+// products, 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void init_arrivals(int blk, const int32_t* __restrict__ ids, int T, int k, int E, int NT,
+                                              int N, int32_t* __restrict__ cnt, float* __restrict__ y) {
+  const int t = blk * kQThreads + threadIdx.x;
+  if (t >= T) return;
+  int routed = 0;
+  for (int s = 0; s < k; s++) routed += (unsigned)ids[(size_t)t * k + s] < (unsigned)E ? 1 : 0;
+  for (int nt = 0; nt < NT; nt++) cnt[(size_t)t * NT + nt] = k - routed;
+  if (routed == 0)
+    for (int n = 0; n < N; n++) y[(size_t)t * N + n] = 0.f;
+}
+
+// The passes before the GEMM in one launch (they are independent, so their
+// workgroups run side by side): workgroups [0, nrep) repack the weight scales
+// of one (expert, panel) each, the next nq quantize one (row tile, k-step
+// range) each, and any after those set the fused combine's arrival counters.
+// Dynamic LDS: a panel's scale rows.
 __global__ __launch_bounds__(kQThreads) void prepare_kernel(const uint8_t* __restrict__ scales, int E, int N, int KB,
                                                             int NT, int NS, uint32_t* __restrict__ wsc, int nrep,
                                                             const uint16_t* __restrict__ x, int x_per_slot, int k,
@@ -398,12 +417,16 @@ __global__ __launch_bounds__(kQThreads) void prepare_kernel(const uint8_t* __res
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_rows,
                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ qx,
-                                                            uint32_t* __restrict__ qs, uint8_t* __restrict__ qf) {
+                                                            uint32_t* __restrict__ qs, uint8_t* __restrict__ qf, int nq,
+                                                            const int32_t* __restrict__ ids, int32_t* __restrict__ cnt,
+                                                            float* __restrict__ y) {
   extern __shared__ uint32_t panel[];  // (kBN * KB + 4) / 4 + 1 words
   if ((int)blockIdx.x < nrep)
     repack_panel(blockIdx.x, panel, scales, E, N, KB, NT, NS, wsc);
-  else
+  else if ((int)blockIdx.x < nrep + nq)
     quantize_tile(blockIdx.x - nrep, x, x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, q, qx, qs, qf);
+  else
+    init_arrivals(blockIdx.x - nrep - nq, ids, R / k, k, E, NT, N, cnt, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -532,12 +555,179 @@ __device__ __forceinline__ void pipeline_fence() {
 // vector-memory counter as out of order and waits for every load before each
 // use.  NS_T > 0: the stage count, known at compile time (straight-line
 // pipeline); NS_T = 0: any K, with a loop.
-template <int NS_T, bool SWIGLU>
+// Cache policy of the fused combine's row stores and loads: sc1, the bit the
+// compiler sets on device-scope (agent) relaxed atomic loads and stores.  An
+// sc1 store is written through to the level all XCDs share, and is complete
+// (vmcnt) once it is there; an sc1 load reads that level, never a stale line
+// of its own XCD's L2.  With both, a tile's rows are visible to any other
+// tile once its stores are complete, without writing back or invalidating
+// whole L2s (a device-scope fence does both, and at one per tile it slowed
+// the GEMM more than threefold).
+constexpr int kCohPolicy = 16;
+// byte offset of element i of out (out stays under 4 GiB: checked on the host)
+__device__ __forceinline__ int coh_off(int i) { return (int)((uint32_t)i * 4u); }
+
+// A wave's 32 routed rows x kBN columns (bias included) to out, with sc1
+// stores through the buffer resource orsrc (out, byte offsets).  st: the
+// wave's 8 KB of free LDS; wrows: the wave's 32 routed rows (-1: none).  Lane
+// (l32, half) holds row l32 and, in elements 4 q + i of accumulator c, columns
+// n0 + 32 c + 8 q + 4 half + i.
+__device__ __forceinline__ void store_out_rows(const v16f (&acc)[kSubN], uint8_t* st, const int* wrows, int lane,
+                                               int n0, int N, bool vec, __amdgpu_buffer_rsrc_t orsrc) {
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  if (vec) {
+    // [32 rows][16 pieces of 16 bytes], XOR-swizzled; the rows a lane stores:
+    // row 4 i + lane / 16, piece lane % 16.  kSubN / 2 rounds of 64 columns
+    // (accumulators 2 rnd, 2 rnd + 1): element run (c, q) of a lane is piece
+    // 8 (c - 2 rnd) + 2 q + half of its row; the columns are a multiple of 4,
+    // so col < N covers a whole piece.  Each store instruction writes 4 rows x
+    // 256 contiguous bytes: whole 128-byte lines.
+    auto st_at = [&](int row, int piece) { return st + row * 256 + ((piece ^ (row & 15)) << 4); };
+    const int piece = lane & 15;
+    int rr[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) rr[i] = wrows[4 * i + (lane >> 4)];
+#pragma unroll
+    for (int rnd = 0; rnd < kSubN / 2; rnd++) {
+#pragma unroll
+      for (int cc = 0; cc < 2; cc++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int c = 2 * rnd + cc;
+          *reinterpret_cast<f32x4_t*>(st_at(l32, 8 * cc + 2 * q + half)) =
+              f32x4_t{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]};
+        }
+      asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
+      const int col = n0 + 64 * rnd + 4 * piece;
+      u32x4_t v[8];  // all reads first: one wait, not one per store
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = *reinterpret_cast<const u32x4_t*>(st_at(4 * i + (lane >> 4), piece));
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (rr[i] >= 0 && col < N)
+          __builtin_amdgcn_raw_buffer_store_b128(v[i], orsrc, coh_off(rr[i] * N + col), 0, kCohPolicy);
+    }
+    return;
+  }
+  // any other width or alignment: 4-byte stores from the registers
+  const int r = wrows[l32];
+  if (r < 0) return;
+  const int o = r * N + n0 + 4 * half;
+#pragma unroll
+  for (int c = 0; c < kSubN; c++)
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (n0 + 32 * c + 8 * q + 4 * half + i < N)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[c][4 * q + i]), orsrc,
+                                                coh_off(o + 32 * c + 8 * q + i), 0, kCohPolicy);
+}
+
+// The gate-weighted combine fused into the projection (gpt-oss-20b files
+// page, src/experts.linnet fn forward_routed: the routed rows' outputs summed
+// per token with the router weights):
+//   y[t, n] = sum over slots s in slot order of gates[t, s] * out[t, s, n],
+// one fused multiply-add each; a slot that is not routed (id outside [0, E))
+// or has gate 0 adds a zero product.  A token's k slot rows lie in up to k row
+// tiles (one per chosen expert), run by different workgroups, possibly on
+// different XCDs.  Per (token, weight panel) an arrival counter, set by the
+// pre-pass to k minus the token's routed slots, takes one increment per routed
+// row a tile has written (device-scope atomics); the increment that finds
+// k - 1 belongs to the tile with the last of the token's rows, and that tile
+// sums the token's rows over its panel's columns.  The rows were stored with
+// sc1 and every wave waits for its stores to complete before the increments;
+// the summing tile reads them with sc1 loads after its increment returned.
+// The sum order is fixed whatever the arrival order, so y is deterministic and
+// equal bit for bit to the separate combine's.
+__device__ __forceinline__ void combine_arrived(const int* rows_lds, int nt, int NT, int n0, int N, int E, int k,
+                                                const int32_t* __restrict__ ids, const float* __restrict__ gates,
+                                                bool vec, __amdgpu_buffer_rsrc_t orsrc, int32_t* __restrict__ cnt,
+                                                float* __restrict__ y) {
+  __shared__ int last_n;
+  __shared__ int last_t[kBM];
+  const int tid = threadIdx.x;
+  if (tid == 0) last_n = 0;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's row stores are complete
+  __syncthreads();
+  if (tid < kBM) {
+    const int r = rows_lds[tid];
+    if (r >= 0) {
+      const int t = r / k;
+      if (atomicAdd(&cnt[(size_t)t * NT + nt], 1) == k - 1) last_t[atomicAdd(&last_n, 1)] = t;
+    }
+  }
+  __syncthreads();
+  const int nl = last_n;
+  if (nl == 0) return;
+  // a slot's row counts when the slot is routed and its gate is not 0;
+  // otherwise it adds a zero product, whatever the row holds
+  auto counts = [&](int id, float g) { return (unsigned)id < (unsigned)E && g != 0.f; };
+  const int ncol = min(kBN, N - n0);
+  constexpr int kSlots = 4;  // slot rows in flight per item
+  if (vec) {
+    // item = (token, 4 columns), with up to kSlots slot rows in flight
+    const int n4 = ncol >> 2;
+    for (int it = tid; it < nl * n4; it += kThreads) {
+      const int i = it / n4;
+      const int t = last_t[i];
+      const int col = n0 + 4 * (it - i * n4);
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < k; s0 += kSlots) {
+        // every load of the pass first (slots past k re-read slot k - 1)
+        u32x4_t v[kSlots];
+        float g[kSlots];
+        int id[kSlots];
+#pragma unroll
+        for (int j = 0; j < kSlots; j++) {
+          const int r = t * k + min(s0 + j, k - 1);
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, coh_off(r * N + col), 0, kCohPolicy);
+          g[j] = gates[r];
+          id[j] = ids[r];
+        }
+#pragma unroll
+        for (int j = 0; j < kSlots; j++) {
+          if (s0 + j < k) {
+            const f32x4_t x = counts(id[j], g[j]) ? __builtin_bit_cast(f32x4_t, v[j]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            a = f32x4_t{fmaf(g[j], x[0], a[0]), fmaf(g[j], x[1], a[1]), fmaf(g[j], x[2], a[2]), fmaf(g[j], x[3], a[3])};
+          }
+        }
+      }
+      *reinterpret_cast<f32x4_t*>(y + (size_t)t * N + col) = a;
+    }
+    return;
+  }
+  for (int it = tid; it < nl * ncol; it += kThreads) {
+    const int i = it / ncol;
+    const int col = n0 + (it - i * ncol);
+    const int t = last_t[i];
+    float a = 0.f;
+    for (int s = 0; s < k; s++) {
+      const int r = t * k + s;
+      const float g = gates[r];
+      const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, coh_off(r * N + col), 0, kCohPolicy));
+      a = fmaf(g, counts(ids[r], g) ? v : 0.f, a);
+    }
+    y[(size_t)t * N + col] = a;
+  }
+}
+
+// Epilogues: out (f32 rows), the gated activation (bf16 rows), or out followed
+// by the gate-weighted combine of every token whose last slot this tile holds.
+enum Epilogue { kEpiOut = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
+
+template <int NS_T, int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void expert_gemm_kernel(
     const uint8_t* __restrict__ blocks, const uint32_t* __restrict__ wsc, const uint16_t* __restrict__ bias, int E,
     int N, int K, const uint8_t* __restrict__ aq, const uint8_t* __restrict__ aqx, const uint32_t* __restrict__ as,
     const uint8_t* __restrict__ aqf, int T, int k, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_rows, float* __restrict__ out, uint16_t* __restrict__ act) {
+    const int32_t* __restrict__ sorted_rows, float* __restrict__ out, uint16_t* __restrict__ act,
+    const int32_t* __restrict__ ids, const float* __restrict__ gates, int32_t* __restrict__ cnt,
+    float* __restrict__ y) {
+  constexpr bool SWIGLU = EPI == kEpiSwiglu;
+  constexpr bool COMBINE = EPI == kEpiCombine;
   // weight stages, double-buffered: codes [256 rows][8 swizzled blocks] and
   // scale words [64 lanes][8 sub-tiles]
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBN * 128];
@@ -864,6 +1054,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // every workgroup still streaming its operands).
   // every wave is past the main loop: both weight slots are free for staging
   lds_barrier();
+  if constexpr (COMBINE) {
+    // every wave takes part in the arrival (its barriers), with rows or not
+    // (two call sites: one guarded store keeps a few values of the main loop
+    // live across the epilogue, past the registers)
+    // out [T, k, N] as one buffer resource (under 4 GiB, checked on the host)
+    const __amdgpu_buffer_rsrc_t orsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out, (short)0, coh_off(T * k * N), kBufferFlags);
+    const bool vec = (N & 3) == 0 && ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+    if (!valid) {
+      combine_arrived(rows_lds, tc.nt, NT, n0, N, E, k, ids, gates, vec, orsrc, cnt, y);
+      return;
+    }
+    store_out_rows(acc, sB[0] + wave * 8192, rows_lds + wave * 32, lane, n0, N, vec, orsrc);
+    combine_arrived(rows_lds, tc.nt, NT, n0, N, E, k, ids, gates, vec, orsrc, cnt, y);
+    return;
+  }
   if (!valid) return;
   uint8_t* st = sB[0] + wave * 8192;  // [32 rows][16 pieces of 16 bytes], XOR-swizzled (slots 0 and 1)
   static_assert(kWaves * 8192 <= 2 * kBN * 128, "the staging fits the weight slots");
@@ -974,7 +1180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 struct GemmLayout {
-  size_t codes, extra, scales, flags, wscales, total;
+  size_t codes, extra, scales, flags, wscales, counters, total;
 };
 
 // most row tiles any routing can give: ceil(R / kBM) plus one partial tile per
@@ -997,7 +1203,8 @@ GemmLayout gemm_layout(int E, int N, int T, int k, int K) {
   l.scales = l.extra + al(units * kAUnit);
   l.flags = l.scales + al(units * 256);
   l.wscales = l.flags + al(units);
-  l.total = l.wscales + al((size_t)E * nt * ns * kSubW * 256);
+  l.counters = l.wscales + al((size_t)E * nt * ns * kSubW * 256);
+  l.total = l.counters + al((size_t)T * nt * 4);  // the fused combine's arrival counters
   return l;
 }
 
@@ -1040,7 +1247,7 @@ size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot) {
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
                               int K, const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                               const int32_t* sorted_rows, float* out, uint16_t* act, void* workspace,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* ids, const float* gates, float* y) {
   // the GEMM addresses a weight row within its expert with 32-bit offsets;
   // the scale repack stages a panel's scale rows in LDS
   if ((size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull || K / 32 > kRepackMaxKB) return hipErrorInvalidValue;
@@ -1054,6 +1261,8 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   uint32_t* as = reinterpret_cast<uint32_t*>(ws + l.scales);
   uint8_t* aqf = ws + l.flags;
   uint32_t* bsc = reinterpret_cast<uint32_t*>(ws + l.wscales);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + l.counters);
+  const bool combine = y != nullptr;  // out is written too
   const int R = T * k;
   const size_t tiles = row_tiles_max(E, T, k);
   // dynamic LDS: a panel's scale rows (23 KB at K = 2880, so several
@@ -1068,18 +1277,20 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   }
   const long long nrep = (long long)E * NT;
   const long long nq = (long long)tiles * ((NKP + kQSteps - 1) / kQSteps);
-  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(nrep + nq)), dim3(kQThreads), panel_bytes, stream, scales, E, N,
-                     K / 32, NT, NS, bsc, (int)nrep, x, x_per_slot, k, R, K, NKP, offsets, sorted_rows, aq, aqx, as,
-                     aqf);
+  const long long ninit = combine ? (T + kQThreads - 1) / kQThreads : 0;
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(nrep + nq + ninit)), dim3(kQThreads), panel_bytes, stream, scales,
+                     E, N, K / 32, NT, NS, bsc, (int)nrep, x, x_per_slot, k, R, K, NKP, offsets, sorted_rows, aq, aqx,
+                     as, aqf, (int)nq, ids, cnt, y);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long tiles_max = (long long)tiles * NT;
   const long long grid = (tiles_max + kXcds - 1) / kXcds * kXcds;
   // the gpt-oss-20b widths (K = 2880) have 12 stages
-  auto kern = act ? (NS == 12 ? expert_gemm_kernel<12, true> : expert_gemm_kernel<0, true>)
-                  : (NS == 12 ? expert_gemm_kernel<12, false> : expert_gemm_kernel<0, false>);
+  auto kern = act       ? (NS == 12 ? expert_gemm_kernel<12, kEpiSwiglu> : expert_gemm_kernel<0, kEpiSwiglu>)
+              : combine ? (NS == 12 ? expert_gemm_kernel<12, kEpiCombine> : expert_gemm_kernel<0, kEpiCombine>)
+                        : (NS == 12 ? expert_gemm_kernel<12, kEpiOut> : expert_gemm_kernel<0, kEpiOut>);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, blocks, bsc, bias, E, N, K, aq, aqx, as,
-                     aqf, T, k, offsets, sorted_rows, out, act);
+                     aqf, T, k, offsets, sorted_rows, out, act, ids, gates, cnt, y);
   return hipGetLastError();
 }
 

@@ -42,10 +42,13 @@ size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);
 // per device) and its size, = MXFP4_NOALLOC_SCRATCH_BYTES
 constexpr size_t kGemmStaticScratchBytes = (size_t)128 << 20;
 hipError_t gemm_static_scratch(void** ptr);
+// y != NULL: out [T, k, N] and then, fused, y [T, N] = the gate-weighted
+// combine of each token's routed slots (ids [T, k], gates [T, k])
 hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
                               int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
                               const int32_t* offsets, const int32_t* sorted_rows, float* out, uint16_t* act,
-                              void* workspace, hipStream_t stream);
+                              void* workspace, hipStream_t stream, const int32_t* ids = nullptr,
+                              const float* gates = nullptr, float* y = nullptr);
 
 // dequantize.hip: nblocks MXFP4 blocks (16 code bytes + 1 scale byte each) ->
 // 32 bf16 weights each
@@ -56,8 +59,9 @@ hipError_t launch_dequantize(const uint8_t* blocks, const uint8_t* scales, size_
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, const uint16_t* bias, int T, int H, int E,
                          uint16_t* logits, hipStream_t stream);
 
-// combine.hip
+// combine.hip; ids != NULL: a slot whose id lies outside [0, E) adds nothing
+// either (as a slot with gate 0)
 hipError_t launch_combine(const float* proj, const float* gates, int T, int k, int N, float* y,
-                          hipStream_t stream);
+                          hipStream_t stream, const int32_t* ids = nullptr, int E = 0);
 
 }  // namespace mxfp4

@@ -99,6 +99,22 @@ class DeviceProblem:
                                     p.x_per_slot, p.k, self.topk_ids, self.gates, self.y,
                                     out=self.out if with_out else None, stream=stream)
 
+    def proj_combine_routed(self, stream=None, blocks=None, scales=None):
+        """Any T: the projection and the gate-weighted combine (fused into the
+        grouped GEMM), from the routing already in topk_ids, gates, offsets and
+        sorted_rows."""
+        p = self.p
+        assert self.y is not None
+        B.mxfp4_expert_proj_combine_routed(self.blocks if blocks is None else blocks,
+                                           self.scales if scales is None else scales, self.bias, p.E, p.N, p.K,
+                                           self.x, p.x_per_slot, p.T, p.k, self.topk_ids, self.gates, self.offsets,
+                                           self.sorted_rows, self.out, self.y, self.path, self.workspace, stream)
+
+    def run_fused(self, stream=None):
+        """route_group, then the projection with the combine fused in."""
+        self.route_group(stream)
+        self.proj_combine_routed(stream)
+
     def run_dense(self, stream=None):
         """The dense-routing form (a validation mode): every expert on every token,
         weighed by the dense router weights, through the same kernels.  Returns

@@ -159,20 +159,22 @@ def test_workspace_size():
     # and fourth terms of the units that take them, 256 bytes of scale words and
     # one byte with the unit's count of extra terms; the weight scales are
     # repacked to 2 KB per expert, 192-row panel (5760 rows = 30 panels) and
-    # stage.  Each region starts on a 256-byte boundary.
+    # stage; the fused combine's arrival counters take 4 bytes per token and
+    # panel.  Each region starts on a 256-byte boundary.
     al = lambda v: (v + 255) // 256 * 256
 
-    def want(tiles, nkp, E, panels, stages):
+    def want(tiles, nkp, E, panels, stages, T):
         units = tiles * 4 * nkp
-        return al(units * 3072) * 2 + al(units * 256) + al(units) + al(E * panels * stages * 2048)
+        return (al(units * 3072) * 2 + al(units * 256) + al(units) + al(E * panels * stages * 2048)
+                + al(T * panels * 4))
 
     tiles = 16384 // 128 + 32
-    assert ws(32, 5760, 4096, 4, 2880, 0, 2) == want(tiles, 48, 32, 30, 12)
-    assert ws(32, 2880, 2048, 4, 2880, 1, 0) == want(64 + 32, 48, 32, 15, 12)
+    assert ws(32, 5760, 4096, 4, 2880, 0, 2) == want(tiles, 48, 32, 30, 12, 4096)
+    assert ws(32, 2880, 2048, 4, 2880, 1, 0) == want(64 + 32, 48, 32, 15, 12, 2048)
     # K = 64: one stage, padded to 2 (8 k-steps); 1024 rows over 8 experts: 8 + 8 tiles
-    assert ws(8, 256, 512, 2, 64, 1, 2) == want(16, 8, 8, 2, 2)
+    assert ws(8, 256, 512, 2, 64, 1, 2) == want(16, 8, 8, 2, 2, 512)
     # fewer rows than experts: at most one partial tile per row
-    assert ws(32, 256, 3, 2, 64, 0, 2) == want(1 + 6, 8, 32, 2, 2)
+    assert ws(32, 256, 3, 2, 64, 0, 2) == want(1 + 6, 8, 32, 2, 2, 3)
     assert ws(32, 5760, 4, 4, 100, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(0, 5760, 4, 4, 128, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(32, 0, 4, 4, 128, 0, 2) == ctypes.c_size_t(-1).value
@@ -239,6 +241,30 @@ def test_proj_combine_rejects_bad_arguments():
     assert f(p, p, None, 32, 2880, 2880, p, 1, 4, p, p, None, None, None) == 1  # no y
     assert f(p, p, None, 32, 2880, 2880, ctypes.c_void_p(8), 1, 4, p, p, None, p, None) == 1  # x misaligned
     assert lib.mxfp4_last_error() != b""
+
+
+def test_proj_combine_routed_rejects_bad_arguments():
+    """mxfp4_expert_proj_combine_routed checks its arguments before any HIP call:
+    the projection's checks, and the routing ids, gates, out and y it needs."""
+    lib = B.load_library()
+    p = ctypes.c_void_p(16)
+    f = lib.mxfp4_expert_proj_combine_routed
+
+    def call(E=32, N=2880, K=2880, x=p, T=64, k=4, ids=p, gates=p, out=p, y=p, path=1, ws=None, nbytes=0):
+        return f(p, p, None, E, N, K, x, 1, T, k, ids, gates, p, p, out, y, path, ws, nbytes, None)
+
+    assert call(E=0) == 1
+    assert call(K=100) == 1
+    assert call(k=33) == 1
+    assert call(T=-1) == 1
+    assert call(ids=None) == 1
+    assert call(gates=None) == 1
+    assert call(out=None) == 1
+    assert call(y=None) == 1
+    assert call(x=ctypes.c_void_p(8)) == 1
+    assert call(path=2) == 2                                  # the grouped GEMM needs its workspace
+    assert b"workspace" in lib.mxfp4_last_error()
+    assert call(T=0, ids=None, gates=None, out=None, y=None) == 0   # nothing to do
 
 
 def test_noalloc_refuses_more_than_its_scratch():
