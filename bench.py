@@ -203,7 +203,7 @@ def measure(cfg_index, steps, warmup, rotate_bytes, path=0, kernel_reps=None, fu
     # the kernel's own time: the median of five replays of the back-to-back launches
     ms_proj = sorted(w.time_graph(g_proj)[0] for _ in range(5))[2]
     res = {
-        "p": w.p, "acc": w.acc, "copies": w.copies, "steps": steps, "fused": w.fused,
+        "p": w.p, "acc": w.acc, "copies": w.copies, "steps": steps, "fused": w.fused, "combine_fused": w.combine_fused,
         "ms_per_step": ms_total / steps, "wall_s": wall,
         "proj_us": 1e3 * ms_proj / kreps,
     }
@@ -398,6 +398,9 @@ def main():
     ap.add_argument("--rotate-bytes", type=int, default=ROTATE_BYTES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other model-size workloads")
+    ap.add_argument("--combine-fused", action="store_true",
+                    help="many-token workloads with a combine: the projection with the combine fused in "
+                         "(mxfp4_expert_proj_combine_routed) instead of expert_proj + moe_combine")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="run N plain 256 MiB device copies first (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -424,12 +427,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = measure(args.config, args.steps, args.warmup, args.rotate_bytes, fused=True)
+    head = measure(args.config, args.steps, args.warmup, args.rotate_bytes, fused=True,
+                   combine_fused=args.combine_fused)
     p, acc = head["p"], head["acc"]
     kernel = "expert_gemv" if p.T * p.k <= 8 else "expert_gemm"
     gbs = acc["step"] / (head["ms_per_step"] * 1e-3) / 1e9
-    # the fused launch moves the routing bytes too
-    kernel_bytes = acc["proj"] + (acc["route"] if head["fused"] else 0)
+    # the fused launch moves the routing bytes too, the fused combine the combine's
+    kernel_bytes = acc["proj"] + (acc["route"] if head["fused"] else 0) + (acc["combine"] if head["combine_fused"] else 0)
     proj_gbs = kernel_bytes / (head["proj_us"] * 1e-6) / 1e9
     line = {
         "metric": METRIC,
@@ -448,8 +452,9 @@ def main():
             "workload": describe(p),
             "seed": 0,
             "path": ("moe_decode (route + group + GEMV in one launch)" if head["fused"] else
-                     "route_group + expert_proj(auto: " + ("GEMV" if kernel == "expert_gemv" else "GEMM") + ")")
-                    + (" + combine" if p.combine else ""),
+                     "route_group + " + ("expert_proj_combine_routed" if head["combine_fused"] else "expert_proj")
+                     + "(auto: " + ("GEMV" if kernel == "expert_gemv" else "GEMM") + ")")
+                    + (" + combine" if p.combine and not head["combine_fused"] else ""),
             "algorithmic_bytes_per_step": acc["step"],
             "experts_touched": acc["experts_touched"],
             "weight_copies_rotated": head["copies"],

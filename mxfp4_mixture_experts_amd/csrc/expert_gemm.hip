@@ -642,6 +642,81 @@ __device__ __forceinline__ void store_out_rows(const v16f (&acc)[kSubN], uint8_t
 // the summing tile reads them with sc1 loads after its increment returned.
 // The sum order is fixed whatever the arrival order, so y is deterministic and
 // equal bit for bit to the separate combine's.
+// The sums of the tokens last_t[0 .. nl) over the panel's columns n0 ..
+// n0 + ncol (see combine_arrived).  Not inlined: its loads (kItems items x
+// kSlots rows per thread in flight, enough bytes to cover the latency of the
+// level all XCDs share) then do not weigh on the GEMM's register allocation.
+constexpr int kSumItems = 4;  // items per thread in flight
+constexpr int kSumSlots = 4;  // slot rows per item in flight
+__device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int ncol, int N, int E, int k,
+                                        const int32_t* __restrict__ ids, const float* __restrict__ gates, bool vec,
+                                        __amdgpu_buffer_rsrc_t orsrc, float* __restrict__ y) {
+  const int tid = threadIdx.x;
+  // a slot's row counts when the slot is routed and its gate is not 0;
+  // otherwise it adds a zero product, whatever the row holds
+  auto counts = [&](int id, float g) { return (unsigned)id < (unsigned)E && g != 0.f; };
+  if (vec) {
+    // item = (token, 4 columns)
+    const int n4 = ncol >> 2;
+    const int items = nl * n4;
+    for (int it0 = tid; it0 < items; it0 += kSumItems * kThreads) {
+      int tt[kSumItems], cc[kSumItems];
+      f32x4_t a[kSumItems];
+#pragma unroll
+      for (int u = 0; u < kSumItems; u++) {
+        const int it = min(it0 + u * kThreads, items - 1);  // past the end: a repeat, not stored
+        const int i = it / n4;
+        tt[u] = last_t[i];
+        cc[u] = n0 + 4 * (it - i * n4);
+        a[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int s0 = 0; s0 < k; s0 += kSumSlots) {
+        // every load of the pass first (slots past k re-read slot k - 1)
+        u32x4_t v[kSumItems][kSumSlots];
+        float g[kSumItems][kSumSlots];
+        int id[kSumItems][kSumSlots];
+#pragma unroll
+        for (int u = 0; u < kSumItems; u++)
+#pragma unroll
+          for (int j = 0; j < kSumSlots; j++) {
+            const int r = tt[u] * k + min(s0 + j, k - 1);
+            v[u][j] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, coh_off(r * N + cc[u]), 0, kCohPolicy);
+            g[u][j] = gates[r];
+            id[u][j] = ids[r];
+          }
+#pragma unroll
+        for (int u = 0; u < kSumItems; u++)
+#pragma unroll
+          for (int j = 0; j < kSumSlots; j++) {
+            if (s0 + j < k) {
+              const f32x4_t x = counts(id[u][j], g[u][j]) ? __builtin_bit_cast(f32x4_t, v[u][j])
+                                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+              a[u] = f32x4_t{fmaf(g[u][j], x[0], a[u][0]), fmaf(g[u][j], x[1], a[u][1]),
+                             fmaf(g[u][j], x[2], a[u][2]), fmaf(g[u][j], x[3], a[u][3])};
+            }
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < kSumItems; u++)
+        if (it0 + u * kThreads < items) *reinterpret_cast<f32x4_t*>(y + (size_t)tt[u] * N + cc[u]) = a[u];
+    }
+    return;
+  }
+  for (int it = tid; it < nl * ncol; it += kThreads) {
+    const int i = it / ncol;
+    const int col = n0 + (it - i * ncol);
+    const int t = last_t[i];
+    float a = 0.f;
+    for (int s = 0; s < k; s++) {
+      const int r = t * k + s;
+      const float g = gates[r];
+      const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, coh_off(r * N + col), 0, kCohPolicy));
+      a = fmaf(g, counts(ids[r], g) ? v : 0.f, a);
+    }
+    y[(size_t)t * N + col] = a;
+  }
+}
+
 __device__ __forceinline__ void combine_arrived(const int* rows_lds, int nt, int NT, int n0, int N, int E, int k,
                                                 const int32_t* __restrict__ ids, const float* __restrict__ gates,
                                                 bool vec, __amdgpu_buffer_rsrc_t orsrc, int32_t* __restrict__ cnt,
@@ -662,56 +737,7 @@ __device__ __forceinline__ void combine_arrived(const int* rows_lds, int nt, int
   __syncthreads();
   const int nl = last_n;
   if (nl == 0) return;
-  // a slot's row counts when the slot is routed and its gate is not 0;
-  // otherwise it adds a zero product, whatever the row holds
-  auto counts = [&](int id, float g) { return (unsigned)id < (unsigned)E && g != 0.f; };
-  const int ncol = min(kBN, N - n0);
-  constexpr int kSlots = 4;  // slot rows in flight per item
-  if (vec) {
-    // item = (token, 4 columns), with up to kSlots slot rows in flight
-    const int n4 = ncol >> 2;
-    for (int it = tid; it < nl * n4; it += kThreads) {
-      const int i = it / n4;
-      const int t = last_t[i];
-      const int col = n0 + 4 * (it - i * n4);
-      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < k; s0 += kSlots) {
-        // every load of the pass first (slots past k re-read slot k - 1)
-        u32x4_t v[kSlots];
-        float g[kSlots];
-        int id[kSlots];
-#pragma unroll
-        for (int j = 0; j < kSlots; j++) {
-          const int r = t * k + min(s0 + j, k - 1);
-          v[j] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, coh_off(r * N + col), 0, kCohPolicy);
-          g[j] = gates[r];
-          id[j] = ids[r];
-        }
-#pragma unroll
-        for (int j = 0; j < kSlots; j++) {
-          if (s0 + j < k) {
-            const f32x4_t x = counts(id[j], g[j]) ? __builtin_bit_cast(f32x4_t, v[j]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            a = f32x4_t{fmaf(g[j], x[0], a[0]), fmaf(g[j], x[1], a[1]), fmaf(g[j], x[2], a[2]), fmaf(g[j], x[3], a[3])};
-          }
-        }
-      }
-      *reinterpret_cast<f32x4_t*>(y + (size_t)t * N + col) = a;
-    }
-    return;
-  }
-  for (int it = tid; it < nl * ncol; it += kThreads) {
-    const int i = it / ncol;
-    const int col = n0 + (it - i * ncol);
-    const int t = last_t[i];
-    float a = 0.f;
-    for (int s = 0; s < k; s++) {
-      const int r = t * k + s;
-      const float g = gates[r];
-      const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, coh_off(r * N + col), 0, kCohPolicy));
-      a = fmaf(g, counts(ids[r], g) ? v : 0.f, a);
-    }
-    y[(size_t)t * N + col] = a;
-  }
+  sum_tokens(last_t, nl, n0, min(kBN, N - n0), N, E, k, ids, gates, vec, orsrc, y);
 }
 
 // Epilogues: out (f32 rows), the gated activation (bf16 rows), or out followed
