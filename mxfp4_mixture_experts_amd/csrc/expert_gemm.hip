@@ -108,53 +108,67 @@ __device__ __forceinline__ int block_exponent(uint32_t amax) {
   return e < -127 ? -127 : e;
 }
 
-__device__ __forceinline__ uint32_t max_abs_bf16(const uint32_t (&w)[16]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
-  return m;
-}
+// A block of 32 held as fp32: ev[i] = element 2 i, od[i] = element 2 i + 1,
+// the order in which v_cvt_scalef32_2xpk16_fp6_f32 takes them (the same codes
+// as v_cvt_scalef32_pk32_fp6_bf16 on the bf16 words, element 2 i in the low
+// half of word i).  Every value is a bf16 value: the inputs, and each residual
+// (rounding a value of at most 8 significant bits to the E2M3 grid leaves a
+// remainder of at most 8), so fp32 holds them exactly.
+struct Block32 {
+  v16f ev, od;
+};
 
-// One MX-FP6 term of the bf16 block w (16 words, element 2i in the low half of
-// word i): its codes and E8M0 byte (127 for a zero block), and w replaced by
-// the residual w - term.  The convert rounds x / 2^e to the nearest E2M3 value
-// (ties to even); the residual is exact in fp32 and is itself a bf16 (rounding
-// a value of at most 8 significant bits to the E2M3 grid leaves a remainder of
-// at most 8), so it stays in the same form for the next term.  Exponents below
-// -100 run the convert on the block times 2^64 with the scale times 2^64 (the
-// same codes; the scale argument stays a normal fp32), in place.
-__device__ __forceinline__ void scale_block(uint32_t (&w)[16], float f) {
+__device__ __forceinline__ void unpack_block(const uint32_t (&w)[16], Block32& b) {
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    const float a = bf16_bits_to_f32(w[i] & 0xffffu) * f;
-    const float b = bf16_bits_to_f32(w[i] >> 16) * f;
-    w[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    b.ev[i] = __uint_as_float(w[i] << 16);
+    b.od[i] = __uint_as_float(w[i] & 0xffff0000u);
   }
 }
 
-__device__ __forceinline__ void fp6_term(uint32_t (&w)[16], v6i& codes, uint32_t& byte) {
-  const uint32_t amax = max_abs_bf16(w);
+// the block's largest magnitude
+__device__ __forceinline__ float max_abs(const Block32& b) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) m = fmaxf(m, fmaxf(fabsf(b.ev[i]), fabsf(b.od[i])));
+  return m;
+}
+
+// One MX-FP6 term of block b: its codes and E8M0 byte (127 for a zero block),
+// and b replaced by the residual b - term (exact).  amax = max_abs(b), which
+// the caller has at hand.  The convert rounds x / 2^e to the nearest E2M3
+// value (ties to even).  Exponents below -100 run the convert on the block
+// times 2^64 with the scale times 2^64 (the same codes; the scale argument
+// stays a normal fp32), in place.
+__device__ __forceinline__ void scale_block(Block32& b, float f) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    b.ev[i] *= f;
+    b.od[i] *= f;
+  }
+}
+
+__device__ __forceinline__ void fp6_term(Block32& b, float amax, v6i& codes, uint32_t& byte) {
   codes = v6i{0, 0, 0, 0, 0, 0};
   byte = 127u;
-  if (amax == 0) return;
-  const int e = block_exponent(amax);
+  if (amax == 0.f) return;
+  const int e = block_exponent(__float_as_uint(amax) >> 16);
   byte = (uint32_t)(e + 127);
   // The block is multiplied by 1 or 2^64 per lane, under a branch taken by the
   // whole wave when any lane shifts (a per-lane select of the whole block
   // would double the registers it holds); none does for ordinary inputs.
   const bool shift = e < -100;
   const bool any_shift = wave_ballot(shift) != 0;
-  if (any_shift) scale_block(w, shift ? 0x1p64f : 1.0f);
+  if (any_shift) scale_block(b, shift ? 0x1p64f : 1.0f);
   const float scale = __uint_as_float((uint32_t)(e + (shift ? 64 : 0) + 127) << 23);
-  codes = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32_t, w), scale);
+  codes = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(b.ev, b.od, scale);
   const v32f dv = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes, scale);
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    const float a = bf16_bits_to_f32(w[i] & 0xffffu) - dv[2 * i];
-    const float b = bf16_bits_to_f32(w[i] >> 16) - dv[2 * i + 1];
-    w[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    b.ev[i] -= dv[2 * i];
+    b.od[i] -= dv[2 * i + 1];
   }
-  if (any_shift) scale_block(w, shift ? 0x1p-64f : 1.0f);
+  if (any_shift) scale_block(b, shift ? 0x1p-64f : 1.0f);
 }
 
 // Whether a block whose residual after the terms so far has bf16 bits
@@ -164,8 +178,8 @@ __device__ __forceinline__ void fp6_term(uint32_t (&w)[16], v6i& codes, uint32_t
 // a block with an outlier channel, or heavy tails, takes three or four, so
 // that its small elements keep their own precision.
 constexpr float kExtraTermRatio = 31.0f * 64.0f;
-__device__ __forceinline__ bool needs_term(uint32_t rmax, float sum_rest) {
-  return bf16_bits_to_f32(rmax) * kExtraTermRatio > sum_rest;
+__device__ __forceinline__ bool needs_term(float rmax, float sum_rest) {
+  return rmax * kExtraTermRatio > sum_rest;
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -245,10 +259,11 @@ __device__ __forceinline__ void put_term(uint8_t* rec, int lane, const v6i& c, i
 }
 
 // Workgroup blk = (row tile t, group of kQSteps k-steps): each wave locates
-// its rows once and walks the group's k-steps, the next block's load in
-// flight while the current one is split (loads are unconditional, from a
-// clamped address, and masked afterwards).
+// its rows once and walks the group's k-steps with the blocks of the next
+// kQAhead k-steps in flight while the current one is split (loads are
+// unconditional, from a clamped address, and masked afterwards).
 constexpr int kQSteps = 8;
+constexpr int kQAhead = 4;
 
 __device__ __forceinline__ void load_block(const uint4* p, uint32_t (&w)[16]) {
 #pragma unroll
@@ -281,24 +296,29 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
   const int KB = K >> 5;
   const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)(r < 0 ? 0 : (x_per_slot ? r : r / k)) * K);
   auto src = [&](int g) { return row + (size_t)min(2 * g + h, KB - 1) * 4; };  // 4 x 16 bytes per block
-  uint32_t wn[16];
-  load_block(src(g0), wn);
-  for (int g = g0; g < g1; g++) {
+  uint32_t ring[kQAhead][16];
+#pragma unroll
+  for (int d = 0; d < kQAhead; d++) load_block(src(min(g0 + d, g1 - 1)), ring[d]);
+#pragma unroll
+  for (int j = 0; j < kQSteps; j++) {
+    const int g = g0 + j;
+    if (g >= g1) break;
     uint32_t w[16];
     const bool real = r >= 0 && 2 * g + h < KB;
 #pragma unroll
-    for (int i = 0; i < 16; i++) w[i] = real ? wn[i] : 0u;
-    load_block(src(min(g + 1, g1 - 1)), wn);
+    for (int i = 0; i < 16; i++) w[i] = real ? ring[j % kQAhead][i] : 0u;
+    if (j + kQAhead < kQSteps) load_block(src(min(g + kQAhead, g1 - 1)), ring[j % kQAhead]);
+    Block32 blk;
+    unpack_block(w, blk);
     // the block's magnitude without its largest element, in element order
-    float sum = 0.f, mx = 0.f;
+    float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const float a = fabsf(bf16_bits_to_f32(w[i] & 0xffffu)), c = fabsf(bf16_bits_to_f32(w[i] >> 16));
-      sum += a;
-      sum += c;
-      mx = fmaxf(mx, fmaxf(a, c));
+      sum += fabsf(blk.ev[i]);
+      sum += fabsf(blk.od[i]);
     }
-    const float sum_rest = sum - mx;
+    float amax = max_abs(blk);
+    const float sum_rest = sum - amax;
     // Terms 0 and 1 always; terms 2 and 3 when the unit needs them (unit-wide
     // decisions by ballot: the extra MFMAs serve all 32 rows x 2 blocks).  Each
     // term is stored as soon as it exists; one loop body (not unrolled), so
@@ -310,10 +330,11 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
     int nterm = 0;
 #pragma unroll 1
     for (; nterm < 4; nterm++) {
-      if (nterm >= 2 && __ballot(needs_term(max_abs_bf16(w), sum_rest)) == 0) break;
+      if (nterm >= 2 && __ballot(needs_term(amax, sum_rest)) == 0) break;
       v6i c;
       uint32_t byte;
-      fp6_term(w, c, byte);
+      fp6_term(blk, amax, c, byte);
+      amax = max_abs(blk);  // the residual's, for the next term
       put_term(nterm < 2 ? rec : xrec, lane, c, nterm & 1);
       bytes = (bytes & ~(0xffu << (8 * nterm))) | (byte << (8 * nterm));
     }
@@ -406,10 +427,11 @@ __device__ __forceinline__ void init_arrivals(int blk, const int32_t* __restrict
 }
 
 // The passes before the GEMM in one launch (they are independent, so their
-// workgroups run side by side): workgroups [0, nrep) repack the weight scales
-// of one (expert, panel) each, the next nq quantize one (row tile, k-step
-// range) each, and any after those set the fused combine's arrival counters.
-// Dynamic LDS: a panel's scale rows.
+// workgroups run side by side): workgroups [0, nq) quantize one (row tile,
+// k-step range) each, the next nrep repack the weight scales of one (expert,
+// panel) each, and any after those set the fused combine's arrival counters.
+// The long quantization workgroups go first (dispatched first, they no longer
+// wait behind the repack).  Dynamic LDS: a panel's scale rows.
 __global__ __launch_bounds__(kQThreads) void prepare_kernel(const uint8_t* __restrict__ scales, int E, int N, int KB,
                                                             int NT, int NS, uint32_t* __restrict__ wsc, int nrep,
                                                             const uint16_t* __restrict__ x, int x_per_slot, int k,
@@ -421,12 +443,12 @@ __global__ __launch_bounds__(kQThreads) void prepare_kernel(const uint8_t* __res
                                                             const int32_t* __restrict__ ids, int32_t* __restrict__ cnt,
                                                             float* __restrict__ y) {
   extern __shared__ uint32_t panel[];  // (kBN * KB + 4) / 4 + 1 words
-  if ((int)blockIdx.x < nrep)
-    repack_panel(blockIdx.x, panel, scales, E, N, KB, NT, NS, wsc);
-  else if ((int)blockIdx.x < nrep + nq)
-    quantize_tile(blockIdx.x - nrep, x, x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, q, qx, qs, qf);
+  if ((int)blockIdx.x < nq)
+    quantize_tile(blockIdx.x, x, x_per_slot, k, R, E, K, NKP, offsets, sorted_rows, q, qx, qs, qf);
+  else if ((int)blockIdx.x < nq + nrep)
+    repack_panel(blockIdx.x - nq, panel, scales, E, N, KB, NT, NS, wsc);
   else
-    init_arrivals(blockIdx.x - nrep - nq, ids, R / k, k, E, NT, N, cnt, y);
+    init_arrivals(blockIdx.x - nq - nrep, ids, R / k, k, E, NT, N, cnt, y);
 }
 
 // ---------------------------------------------------------------------------
