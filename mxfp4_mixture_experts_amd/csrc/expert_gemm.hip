@@ -248,14 +248,14 @@ __device__ __forceinline__ bool locate_row_tile(const int32_t* offsets, int E, i
 // 24), one load per stage; and the unit's count of extra terms (0, 1 or 2) in
 // one byte.  The k-steps of a sub-tile are consecutive.  Rows past the
 // expert's last routed row, and blocks past K, are zero codes with scale 127.
-__device__ __forceinline__ void put_term(uint8_t* rec, int lane, const v6i& c, int second) {
-  if (!second) {
-    *reinterpret_cast<uint4*>(rec + lane * 16) = make_uint4(c[0], c[1], c[2], c[3]);
-    *reinterpret_cast<uint2*>(rec + 1024 + lane * 16) = make_uint2(c[4], c[5]);
-  } else {
-    *reinterpret_cast<uint2*>(rec + 1024 + lane * 16 + 8) = make_uint2(c[0], c[1]);
-    *reinterpret_cast<uint4*>(rec + 2048 + lane * 16) = make_uint4(c[2], c[3], c[4], c[5]);
-  }
+// A pair of terms (a: the first, b: the second) as the record's three chunks,
+// each store a whole 16 bytes per lane (1 KB per wave instruction); has_b =
+// false (a third term without a fourth): the first two chunks only, the
+// fourth term's half of the second zero (never read).
+__device__ __forceinline__ void put_terms(uint8_t* rec, int lane, const v6i& a, const v6i& b, bool has_b) {
+  *reinterpret_cast<uint4*>(rec + lane * 16) = make_uint4(a[0], a[1], a[2], a[3]);
+  *reinterpret_cast<uint4*>(rec + 1024 + lane * 16) = make_uint4(a[4], a[5], has_b ? b[0] : 0, has_b ? b[1] : 0);
+  if (has_b) *reinterpret_cast<uint4*>(rec + 2048 + lane * 16) = make_uint4(b[2], b[3], b[4], b[5]);
 }
 
 // Workgroup blk = (row tile t, group of kQSteps k-steps): each wave locates
@@ -299,6 +299,9 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
   uint32_t ring[kQAhead][16];
 #pragma unroll
   for (int d = 0; d < kQAhead; d++) load_block(src(min(g0 + d, g1 - 1)), ring[d]);
+  uint32_t sw4[4] = {0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+  uint64_t flags = 0;
+  static_assert(kQSteps % 4 == 0 && kQSteps <= 8, "whole stages of scale words; eight flag bytes");
 #pragma unroll
   for (int j = 0; j < kQSteps; j++) {
     const int g = g0 + j;
@@ -320,14 +323,15 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
     float amax = max_abs(blk);
     const float sum_rest = sum - amax;
     // Terms 0 and 1 always; terms 2 and 3 when the unit needs them (unit-wide
-    // decisions by ballot: the extra MFMAs serve all 32 rows x 2 blocks).  Each
-    // term is stored as soon as it exists; one loop body (not unrolled), so
-    // that few registers are live.
+    // decisions by ballot: the extra MFMAs serve all 32 rows x 2 blocks).  Terms
+    // are stored in pairs, whole chunks at a time; one loop body (not
+    // unrolled), so that few registers are live.
     const size_t unit = ((size_t)t * kWaves + sub) * NKP + g;
     uint8_t* rec = q + unit * kAUnit;
     uint8_t* xrec = qx + unit * kAUnit;
     uint32_t bytes = 0x7f7f7f7fu;
     int nterm = 0;
+    v6i first = v6i{0, 0, 0, 0, 0, 0};
 #pragma unroll 1
     for (; nterm < 4; nterm++) {
       if (nterm >= 2 && __ballot(needs_term(amax, sum_rest)) == 0) break;
@@ -335,11 +339,28 @@ __device__ __forceinline__ void quantize_tile(int blk, const uint16_t* __restric
       uint32_t byte;
       fp6_term(blk, amax, c, byte);
       amax = max_abs(blk);  // the residual's, for the next term
-      put_term(nterm < 2 ? rec : xrec, lane, c, nterm & 1);
+      if (nterm & 1)
+        put_terms(nterm < 2 ? rec : xrec, lane, first, c, true);
+      else
+        first = c;
       bytes = (bytes & ~(0xffu << (8 * nterm))) | (byte << (8 * nterm));
     }
-    s[(unit - g) * 64 + (g >> 2) * 256 + lane * 4 + (g & 3)] = bytes;
-    if (lane == 0) qf[unit] = (uint8_t)(nterm - 2);
+    if (nterm == 3) put_terms(xrec, lane, first, first, false);
+    // the scale words of a stage's four k-steps (g0 is a multiple of 4) as one
+    // 16-byte store per lane, the counts of extra terms of the group's k-steps
+    // as one store of lane 0
+    sw4[j & 3] = bytes;
+    if ((j & 3) == 3 || g + 1 == g1)
+      *reinterpret_cast<uint4*>(s + (unit - g) * 64 + (g >> 2) * 256 + lane * 4) =
+          make_uint4(sw4[0], sw4[1], sw4[2], sw4[3]);
+    flags |= (uint64_t)(nterm - 2) << (8 * j);
+  }
+  if (lane == 0) {
+    uint8_t* fl = qf + ((size_t)t * kWaves + sub) * NKP + g0;
+    if (g1 - g0 == kQSteps)
+      *reinterpret_cast<uint2*>(fl) = make_uint2((uint32_t)flags, (uint32_t)(flags >> 32));
+    else
+      for (int j = 0; j < g1 - g0; j++) fl[j] = (uint8_t)(flags >> (8 * j));
   }
 }
 
