@@ -292,12 +292,12 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(int32_t* __restric
           topk_ids[r] = e;
         }
       }
-      const uint64_t peers = peers_of(e);
-      if (e >= 0 && lanes_below(peers) == 0) {
-        const int n = __popcll(peers);
-        cnt_all[wave * E + e] += n;
-        if (t < (int)blockIdx.x * kGroupWaves) cnt_pre[wave * E + e] += n;
-        if (t == own_tile) cnt_own[wave * E + e] += n;
+      // counts only (their order is irrelevant): one LDS atomic per row into
+      // the wave's own counters; the scatter below finds each row's place
+      if (e >= 0) {
+        atomicAdd(&cnt_all[wave * E + e], 1);
+        if (t < (int)blockIdx.x * kGroupWaves) atomicAdd(&cnt_pre[wave * E + e], 1);
+        if (t == own_tile) atomicAdd(&cnt_own[wave * E + e], 1);
       }
     }
   }
