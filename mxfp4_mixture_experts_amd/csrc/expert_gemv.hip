@@ -511,11 +511,36 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
   int e, m0, m1;
   int fused_row = -1;
   if constexpr (FUSED) {
-    const float l = lane < E ? bf16_bits_to_f32(fr.logits[lane]) : -INFINITY;
+    float l = -INFINITY;
     int rank = 0;
-    for (int jj = 0; jj < E; jj++) {
-      const float lj = readlane_f(l, jj);
-      rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
+    if (E == 32) {
+      // gpt-oss-20b's 32 experts: the logits as 16 words through the scalar
+      // cache (one wave-uniform load; about 0.5 us sooner than a vector load
+      // of the same 64 bytes by every wave), each expert's logit then a
+      // uniform value.  Other counts take the vector load below (a second
+      // specialised path made the kernel larger and its start slower).
+      const __attribute__((address_space(4))) uint32_t* lw =
+          (const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(fr.logits);
+      uint32_t wv[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) wv[i] = lw[i];
+      auto logit = [&](int j) { return __uint_as_float((j & 1) ? (wv[j >> 1] & 0xffff0000u) : (wv[j >> 1] << 16)); };
+#pragma unroll
+      for (int jj = 0; jj < 32; jj++) {
+        const float lj = logit(jj);  // a select per lane, not a branch
+        if (lane == jj) l = lj;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 32; jj++) {
+        const float lj = logit(jj);
+        rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
+      }
+    } else {
+      l = lane < E ? bf16_bits_to_f32(fr.logits[lane]) : -INFINITY;
+      for (int jj = 0; jj < E; jj++) {
+        const float lj = readlane_f(l, jj);
+        rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
+      }
     }
     // Logits without NaN rank the lanes 0 .. E - 1, each rank once.  A NaN
     // compares false both ways and breaks that: then, as in the routing

@@ -304,6 +304,28 @@ def test_fused_decode(case):
             np.testing.assert_array_equal(g[key], g2[key], err_msg=key)
 
 
+@pytest.mark.parametrize("E,k", [(32, 4), (64, 8), (32, 32)])
+def test_fused_decode_tied_logits(E, k):
+    """Logits with many exact ties (rounded to a coarse grid): the one-launch
+    decode reads the 32 or 64 logits through scalar loads and ranks them by the
+    rank definition (ties to the lower index); its routing must equal the
+    oracle's and the routing launch's bit for bit."""
+    p = S.make_custom(E=E, N=40, K=64, T=1, k=k, route="logits", tag=700 + E + k)
+    vals = np.round(O.bf16_to_f64(p.logits) * 2.0) / 2.0          # multiples of 0.5: many ties
+    p.logits = S.f32_to_bf16_bits(vals.astype(np.float32))
+    _announce(f"decode with tied logits E={E} k={k}")
+    ref = O.run_problem(p)
+    dp = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp.run_decode()
+    g = dp.results()
+    check_routing(g, ref)
+    dp2 = DeviceProblem(p, path=B.MXFP4_PATH_GEMV)
+    dp2.run()
+    g2 = dp2.results()
+    for key in ("ids", "offsets", "sorted_rows", "gates", "out"):
+        np.testing.assert_array_equal(g[key], g2[key], err_msg=key)
+
+
 DECODE_SWIGLU_CASES = {
     "gate_up_like": dict(E=32, N=200, K=2880, T=1, k=4, route="logits"),
     "k3072": dict(E=16, N=100, K=3072, T=1, k=3, route="logits"),
