@@ -59,6 +59,17 @@ def test_graph_route_project_combine(path):
     _replay_matches(dp.run, [dp.topk_ids, dp.gates, dp.offsets, dp.sorted_rows, dp.out, dp.y])
 
 
+@pytest.mark.parametrize("path", [1, 2])
+def test_graph_fused_combine(path):
+    """route_group + the projection with the combine fused in: the arrival
+    counters are set by the grouped GEMM's own pre-pass each replay (no memset
+    node), so every replay sums each token once."""
+    p = S.make_custom(E=16, N=400, K=256, T=300, k=4, x_per_slot=True, route="zipf+logits", combine=True)
+    _announce(f"graph: route_group + expert_proj_combine_routed, path {path}")
+    dp = DeviceProblem(p, path=path)
+    _replay_matches(dp.run_fused, [dp.topk_ids, dp.gates, dp.offsets, dp.sorted_rows, dp.out, dp.y])
+
+
 def test_graph_swiglu_gemm():
     p = S.make_custom(E=8, N=512, K=320, T=300, k=4, route="logits")
     _announce("graph: route_group + expert_proj_swiglu (GEMM)")
