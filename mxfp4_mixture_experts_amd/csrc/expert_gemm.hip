@@ -480,22 +480,28 @@ struct TileCoord {
   int e, m_begin, m_count, nt, mtile;  // mtile: the row tile's number over all experts
 };
 
-// Tile t of the grouped problem: experts in order; within an expert the weight
-// panel (n-tile) varies slowest so that the row tiles sharing a panel are
-// consecutive.  Workgroup L takes tile (L % 8) * ceil(tiles / 8) + L / 8:
-// workgroups are dispatched round-robin over the 8 XCDs, so consecutive tiles
-// run on one XCD and share its L2.  Each wave decodes its tile itself (wave
-// scans over 64 experts at a time), so no barrier is needed.
+// Tile t of the grouped problem (TM routed rows x one weight panel): experts
+// in order; within an expert the weight panel (n-tile) varies slowest so that
+// the row tiles sharing a panel are consecutive.  Workgroup L takes tile
+// (L % 8) * ceil(tiles / 8) + L / 8: workgroups are dispatched round-robin
+// over the 8 XCDs, so consecutive tiles run on one XCD and share its L2.  Each
+// wave decodes its tile itself (wave scans over 64 experts at a time), so no
+// barrier is needed.  c.mtile numbers the tile's first 128-row tile (the
+// pre-pass's unit of activation records) over all experts.
+template <int TM>
 __device__ __forceinline__ bool locate_tile(const int32_t* offsets, int E, int R, int NT, int lane, TileCoord& c) {
+  static_assert(TM % kBM == 0, "whole 128-row tiles");
   if (E <= 64) {
     // one lane per expert: one read of the offsets and one scan give both the
     // tile count and this workgroup's tile
-    int b = 0, f = 0, cnt = 0;
+    int b = 0, f = 0, cnt = 0, c128 = 0;
     if (lane < E) {
       expert_rows(offsets, lane, R, b, f);
-      cnt = (f - b + kBM - 1) / kBM * NT;
+      cnt = (f - b + TM - 1) / TM * NT;
+      c128 = (f - b + kBM - 1) / kBM;
     }
     const int incl = wave_incl_scan(cnt, lane);
+    const int incl128 = wave_incl_scan(c128, lane);
     const int total = __shfl(incl, 63, 64);
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int j = blockIdx.x / kXcds;
@@ -506,15 +512,16 @@ __device__ __forceinline__ bool locate_tile(const int32_t* offsets, int E, int R
     const int src = __builtin_ctzll(hit);
     const int eb = __shfl(b, src, 64), ef = __shfl(f, src, 64);
     const int before = __shfl(incl, src, 64) - __shfl(cnt, src, 64);
+    const int before128 = __shfl(incl128, src, 64) - __shfl(c128, src, 64);
     const int local = t - before;
-    const int mt = (ef - eb + kBM - 1) / kBM;
+    const int mt = (ef - eb + TM - 1) / TM;
     const int nt = local / mt;
     const int mi = local - nt * mt;
     c.e = __builtin_amdgcn_readfirstlane(src);
-    c.m_begin = __builtin_amdgcn_readfirstlane(eb + mi * kBM);
-    c.m_count = __builtin_amdgcn_readfirstlane(min(kBM, ef - (eb + mi * kBM)));
+    c.m_begin = __builtin_amdgcn_readfirstlane(eb + mi * TM);
+    c.m_count = __builtin_amdgcn_readfirstlane(min(TM, ef - (eb + mi * TM)));
     c.nt = __builtin_amdgcn_readfirstlane(nt);
-    c.mtile = __builtin_amdgcn_readfirstlane(before / NT + mi);
+    c.mtile = __builtin_amdgcn_readfirstlane(before128 + mi * (TM / kBM));
     return true;
   }
   int total = 0;
@@ -524,7 +531,7 @@ __device__ __forceinline__ bool locate_tile(const int32_t* offsets, int E, int R
     if (e < E) {
       int b, f;
       expert_rows(offsets, e, R, b, f);
-      cnt = (f - b + kBM - 1) / kBM * NT;
+      cnt = (f - b + TM - 1) / TM * NT;
     }
     total += wave_sum_i(cnt);
   }
@@ -534,34 +541,37 @@ __device__ __forceinline__ bool locate_tile(const int32_t* offsets, int E, int R
   if (j >= per_xcd) return false;
   const int t = (L % kXcds) * per_xcd + j;
   if (t >= total) return false;
-  int before = 0;
+  int before = 0, before128 = 0;
   for (int base = 0; base < E; base += 64) {
     const int e = base + lane;
-    int cnt = 0, b = 0, f = 0;
+    int cnt = 0, c128 = 0, b = 0, f = 0;
     if (e < E) {
       expert_rows(offsets, e, R, b, f);
-      cnt = (f - b + kBM - 1) / kBM * NT;
+      cnt = (f - b + TM - 1) / TM * NT;
+      c128 = (f - b + kBM - 1) / kBM;
     }
     const int incl = wave_incl_scan(cnt, lane);
+    const int incl128 = wave_incl_scan(c128, lane);
     const int tl = t - before;
     const uint64_t hit = wave_ballot(cnt > 0 && incl - cnt <= tl && tl < incl);
     if (hit) {
       const int src = __builtin_ctzll(hit);
       const int eb = __shfl(b, src, 64), ef = __shfl(f, src, 64);
       const int local = tl - (__shfl(incl, src, 64) - __shfl(cnt, src, 64));
-      const int mt = (ef - eb + kBM - 1) / kBM;
+      const int mt = (ef - eb + TM - 1) / TM;
       const int nt = local / mt;
       const int mi = local - nt * mt;
       // wave-uniform by construction; say so, so that branches on them are scalar
       c.e = __builtin_amdgcn_readfirstlane(base + src);
-      c.m_begin = __builtin_amdgcn_readfirstlane(eb + mi * kBM);
-      c.m_count = __builtin_amdgcn_readfirstlane(min(kBM, ef - (eb + mi * kBM)));
+      c.m_begin = __builtin_amdgcn_readfirstlane(eb + mi * TM);
+      c.m_count = __builtin_amdgcn_readfirstlane(min(TM, ef - (eb + mi * TM)));
       c.nt = __builtin_amdgcn_readfirstlane(nt);
-      // the experts before e hold (tiles before e) / NT row tiles
-      c.mtile = __builtin_amdgcn_readfirstlane((__shfl(incl, src, 64) - __shfl(cnt, src, 64)) / NT + before / NT + mi);
+      c.mtile = __builtin_amdgcn_readfirstlane(before128 + __shfl(incl128, src, 64) - __shfl(c128, src, 64) +
+                                               mi * (TM / kBM));
       return true;
     }
     before += __shfl(incl, 63, 64);
+    before128 += __shfl(incl128, 63, 64);
   }
   return false;
 }
@@ -691,6 +701,7 @@ __device__ __forceinline__ void store_out_rows(const v16f (&acc)[kSubN], uint8_t
 // level all XCDs share) then do not weigh on the GEMM's register allocation.
 constexpr int kSumItems = 4;  // items per thread in flight
 constexpr int kSumSlots = 4;  // slot rows per item in flight
+template <int NTH>
 __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int ncol, int N, int E, int k,
                                         const int32_t* __restrict__ ids, const float* __restrict__ gates, bool vec,
                                         __amdgpu_buffer_rsrc_t orsrc, float* __restrict__ y) {
@@ -702,12 +713,12 @@ __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int n
     // item = (token, 4 columns)
     const int n4 = ncol >> 2;
     const int items = nl * n4;
-    for (int it0 = tid; it0 < items; it0 += kSumItems * kThreads) {
+    for (int it0 = tid; it0 < items; it0 += kSumItems * NTH) {
       int tt[kSumItems], cc[kSumItems];
       f32x4_t a[kSumItems];
 #pragma unroll
       for (int u = 0; u < kSumItems; u++) {
-        const int it = min(it0 + u * kThreads, items - 1);  // past the end: a repeat, not stored
+        const int it = min(it0 + u * NTH, items - 1);  // past the end: a repeat, not stored
         const int i = it / n4;
         tt[u] = last_t[i];
         cc[u] = n0 + 4 * (it - i * n4);
@@ -741,11 +752,11 @@ __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int n
       }
 #pragma unroll
       for (int u = 0; u < kSumItems; u++)
-        if (it0 + u * kThreads < items) *reinterpret_cast<f32x4_t*>(y + (size_t)tt[u] * N + cc[u]) = a[u];
+        if (it0 + u * NTH < items) *reinterpret_cast<f32x4_t*>(y + (size_t)tt[u] * N + cc[u]) = a[u];
     }
     return;
   }
-  for (int it = tid; it < nl * ncol; it += kThreads) {
+  for (int it = tid; it < nl * ncol; it += NTH) {
     const int i = it / ncol;
     const int col = n0 + (it - i * ncol);
     const int t = last_t[i];
@@ -760,17 +771,18 @@ __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int n
   }
 }
 
+template <int TM, int NTH>
 __device__ __forceinline__ void combine_arrived(const int* rows_lds, int nt, int NT, int n0, int N, int E, int k,
                                                 const int32_t* __restrict__ ids, const float* __restrict__ gates,
                                                 bool vec, __amdgpu_buffer_rsrc_t orsrc, int32_t* __restrict__ cnt,
                                                 float* __restrict__ y) {
   __shared__ int last_n;
-  __shared__ int last_t[kBM];
+  __shared__ int last_t[TM];
   const int tid = threadIdx.x;
   if (tid == 0) last_n = 0;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's row stores are complete
   __syncthreads();
-  if (tid < kBM) {
+  if (tid < TM) {
     const int r = rows_lds[tid];
     if (r >= 0) {
       const int t = r / k;
@@ -780,15 +792,18 @@ __device__ __forceinline__ void combine_arrived(const int* rows_lds, int nt, int
   __syncthreads();
   const int nl = last_n;
   if (nl == 0) return;
-  sum_tokens(last_t, nl, n0, min(kBN, N - n0), N, E, k, ids, gates, vec, orsrc, y);
+  sum_tokens<NTH>(last_t, nl, n0, min(kBN, N - n0), N, E, k, ids, gates, vec, orsrc, y);
 }
 
 // Epilogues: out (f32 rows), the gated activation (bf16 rows), or out followed
 // by the gate-weighted combine of every token whose last slot this tile holds.
 enum Epilogue { kEpiOut = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
 
-template <int NS_T, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void expert_gemm_kernel(
+// W waves: a tile of 32 W routed rows (W / 4 of the pre-pass's 128-row tiles)
+// x 192 weight rows; the weight stage is shared by all W waves, so eight waves
+// move half the weight bytes per MFMA that four do.
+template <int NS_T, int EPI, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void expert_gemm_kernel(
     const uint8_t* __restrict__ blocks, const uint32_t* __restrict__ wsc, const uint16_t* __restrict__ bias, int E,
     int N, int K, const uint8_t* __restrict__ aq, const uint8_t* __restrict__ aqx, const uint32_t* __restrict__ as,
     const uint8_t* __restrict__ aqf, int T, int k, const int32_t* __restrict__ offsets,
@@ -797,14 +812,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     float* __restrict__ y) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu;
   constexpr bool COMBINE = EPI == kEpiCombine;
-  // weight stages, double-buffered: codes [256 rows][8 swizzled blocks] and
-  // scale words [64 lanes][8 sub-tiles]
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBN * 128];
+  constexpr int TM = 32 * W;              // routed rows per tile
+  constexpr int kPieces = kBN / 8 / W;    // 1 KB weight pieces per wave and stage
+  static_assert(W % kWaves == 0 && kPieces * 8 * W == kBN, "whole 128-row tiles, whole pieces");
+  // weight stages, double-buffered: codes [192 rows][8 swizzled blocks] and
+  // scale words [64 lanes][8 sub-tiles]; each slot large enough that the
+  // epilogue's 8 KB per wave fits in the two
+  constexpr int kSlot = kBN * 128 > W * 4096 ? kBN * 128 : W * 4096;
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kSlot];
   __shared__ __attribute__((aligned(16))) uint32_t sS0[kSubW * 64];
   __shared__ __attribute__((aligned(16))) uint32_t sS1[kSubW * 64];
   uint8_t* const sB0 = sB[0];
   uint8_t* const sB1 = sB[1];
-  __shared__ __attribute__((aligned(16))) int rows_lds[kBM];  // routed row of each tile row, -1 if none
+  __shared__ __attribute__((aligned(16))) int rows_lds[TM];  // routed row of each tile row, -1 if none
   __shared__ __attribute__((aligned(16))) float bias_lds[kBN];  // bias of each tile column (0 without bias)
 
   const int tid = threadIdx.x;
@@ -816,14 +836,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int R = T * k;
   const int NT = (N + kBN - 1) / kBN;
   TileCoord tc;
-  if (!locate_tile(offsets, E, R, NT, lane, tc)) return;
+  if (!locate_tile<TM>(offsets, E, R, NT, lane, tc)) return;
   const int e = tc.e;
   const int KB = K >> 5;
   const int NS = NS_T > 0 ? NS_T : stage_count(K);
   const int NKP = NS * kStepsPerStage;
   const int nks = (KB + 1) >> 1;  // k-steps holding real blocks
 
-  if (tid < kBM) {
+  if (tid < TM) {
     int r = -1;
     if (tid < tc.m_count) {
       r = sorted_rows[tc.m_begin + tid];
@@ -836,25 +856,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     bias_lds[tid] = bias ? bf16_bits_to_f32(bias[(size_t)tc.e * N + min(tc.nt * kBN + tid, N - 1)]) : 0.f;
   const bool valid = wave * 32 < tc.m_count;
 
-  // activations: this wave's row sub-tile, k-steps consecutive.  Buffer
-  // loads: the wave's records as one resource (SGPRs), a 32-bit lane offset
-  // in a VGPR and the k-step in the scalar offset.
+  // activations: this wave's row sub-tile (sub-tile wave % 4 of 128-row tile
+  // mtile + wave / 4), k-steps consecutive.  Buffer loads: the wave's records
+  // as one resource (SGPRs), a 32-bit lane offset in a VGPR and the k-step in
+  // the scalar offset.
   const size_t unit0 = ((size_t)tc.mtile * kWaves + wave) * NKP;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(aq + unit0 * kAUnit), (short)0, NKP * kAUnit, kBufferFlags);
   const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(as + unit0 * 64), (short)0, NKP * 256, kBufferFlags);
 
-  // weight stage pieces: piece i = wave + 4q (q < kSubN) covers tile rows 8i ..
-  // 8i + 7 (1 KB); lane L takes row 8i + L / 8 and LDS slot L % 8, which holds
-  // block (L % 8) ^ swizzle(row) of the stage (rows past N re-read row N - 1,
-  // blocks past K re-read block K - 1)
+  // weight stage pieces: piece i = wave + W q (q < kPieces) covers tile rows
+  // 8i .. 8i + 7 (1 KB); lane L takes row 8i + L / 8 and LDS slot L % 8, which
+  // holds block (L % 8) ^ swizzle(row) of the stage (rows past N re-read row
+  // N - 1, blocks past K re-read block K - 1)
   const int n0 = tc.nt * kBN;
   // the expert's codes as one resource (at most 4 GiB, checked on the host)
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(blocks + (size_t)e * N * KB * 16), (short)0, N * KB * 16, kBufferFlags);
-  const int b_r0 = n0 + 8 * wave + (lane >> 3);  // row of piece q: b_r0 + 32 q
-  // swizzle(8 i + L / 8) = (L / 8) ^ (i & 1), and i = wave + 4 q has the parity of wave
+  const int b_r0 = n0 + 8 * wave + (lane >> 3);  // row of piece q: b_r0 + 8 W q
+  // swizzle(8 i + L / 8) = (L / 8) ^ (i & 1), and i = wave + W q has the parity of wave
   const int b_blk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
   // weight-scale words: the 2 KB of a stage as two 1 KB halves; waves of equal
   // parity move the same half (the same bytes to the same place)
@@ -863,25 +884,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       kBufferFlags);
   const int bs_off = (wave & 1) * 1024 + lane * 16;
 
-  // A stage's weights move global -> registers -> LDS, 6 pieces and the
+  // A stage's weights move global -> registers -> LDS, kPieces pieces and the
   // stage's scale words per wave.  Two register sets: set s % 2 is loaded with
   // stage s + 2 at the start of stage s (it held stage s, which is in LDS by
   // then) and written to LDS at the end of stage s + 1, so the loads have two
   // stages to arrive (HBM latency under load is about two k-steps' work).
-  u32x4_t rbs[2][kSubN + 1];
+  u32x4_t rbs[2][kPieces + 1];
   auto load_w = [&](int s, auto xc) {
     constexpr int X = decltype(xc)::value;
     const int blk = min(kStageBlocks * s + b_blk, KB - 1) * 16;
 #pragma unroll
-    for (int q = 0; q < kSubN; q++)
-      rbs[X][q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(b_r0 + 32 * q, N - 1) * (KB * 16) + blk, 0, 0);
-    rbs[X][kSubN] = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, bs_off, s * (kSubW * 64 * 4), 0);
+    for (int q = 0; q < kPieces; q++)
+      rbs[X][q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, min(b_r0 + 8 * W * q, N - 1) * (KB * 16) + blk, 0, 0);
+    rbs[X][kPieces] = __builtin_amdgcn_raw_buffer_load_b128(bs_rsrc, bs_off, s * (kSubW * 64 * 4), 0);
   };
   auto store_w = [&](uint8_t* sb, uint32_t* ss, auto xc) {
     constexpr int X = decltype(xc)::value;
 #pragma unroll
-    for (int q = 0; q < kSubN; q++) *reinterpret_cast<u32x4_t*>(sb + (wave + 4 * q) * 1024 + lane * 16) = rbs[X][q];
-    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(ss) + (wave & 1) * 1024 + lane * 16) = rbs[X][kSubN];
+    for (int q = 0; q < kPieces; q++) *reinterpret_cast<u32x4_t*>(sb + (wave + W * q) * 1024 + lane * 16) = rbs[X][q];
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(ss) + (wave & 1) * 1024 + lane * 16) = rbs[X][kPieces];
   };
 
   // this lane's offsets into a stage for the k-step j: row l32 of each 32-row
@@ -1132,16 +1153,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         __builtin_amdgcn_make_buffer_rsrc(out, (short)0, coh_off(T * k * N), kBufferFlags);
     const bool vec = (N & 3) == 0 && ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
     if (!valid) {
-      combine_arrived(rows_lds, tc.nt, NT, n0, N, E, k, ids, gates, vec, orsrc, cnt, y);
+      combine_arrived<TM, W * 64>(rows_lds, tc.nt, NT, n0, N, E, k, ids, gates, vec, orsrc, cnt, y);
       return;
     }
     store_out_rows(acc, sB[0] + wave * 8192, rows_lds + wave * 32, lane, n0, N, vec, orsrc);
-    combine_arrived(rows_lds, tc.nt, NT, n0, N, E, k, ids, gates, vec, orsrc, cnt, y);
+    combine_arrived<TM, W * 64>(rows_lds, tc.nt, NT, n0, N, E, k, ids, gates, vec, orsrc, cnt, y);
     return;
   }
   if (!valid) return;
   uint8_t* st = sB[0] + wave * 8192;  // [32 rows][16 pieces of 16 bytes], XOR-swizzled (slots 0 and 1)
-  static_assert(kWaves * 8192 <= 2 * kBN * 128, "the staging fits the weight slots");
+  static_assert(W * 8192 <= 2 * kSlot, "the staging fits the weight slots");
   auto st_at = [&](int row, int piece) { return st + row * 256 + ((piece ^ (row & 15)) << 4); };
   // the rows a lane stores: row 4 i + lane / 16 of the wave's 32, piece lane % 16
   auto out_rows = [&](int (&rr)[8]) {
@@ -1248,6 +1269,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (n0 + 32 * c + 8 * q + 4 * half + i < N) __builtin_nontemporal_store(acc[c][4 * q + i], orow + 32 * c + 8 * q + i);
 }
 
+// waves per GEMM workgroup: eight while the routed rows average at least 256
+// per expert, else four
+int gemm_waves(int E, int R) { return (long long)R >= 256LL * E ? 8 : 4; }
+
 struct GemmLayout {
   size_t codes, extra, scales, flags, wscales, counters, total;
 };
@@ -1352,13 +1377,21 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
                      as, aqf, (int)nq, ids, cnt, y);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long tiles_max = (long long)tiles * NT;
+  // Eight waves (256-row tiles) halve the weight bytes per MFMA where the
+  // experts hold enough rows to fill them; four where many experts hold fewer
+  // than 256 rows (an odd 128-row tile leaves half of an eight-wave tile idle).
+  const int W = gemm_waves(E, R);
+  const int TM = 32 * W;
+  const long long tiles_max = ((long long)(R + TM - 1) / TM + (R < E ? R : E)) * NT;
   const long long grid = (tiles_max + kXcds - 1) / kXcds * kXcds;
   // the gpt-oss-20b widths (K = 2880) have 12 stages
-  auto kern = act       ? (NS == 12 ? expert_gemm_kernel<12, kEpiSwiglu> : expert_gemm_kernel<0, kEpiSwiglu>)
-              : combine ? (NS == 12 ? expert_gemm_kernel<12, kEpiCombine> : expert_gemm_kernel<0, kEpiCombine>)
-                        : (NS == 12 ? expert_gemm_kernel<12, kEpiOut> : expert_gemm_kernel<0, kEpiOut>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, blocks, bsc, bias, E, N, K, aq, aqx, as,
+#define MXFP4_GEMM_KERN(WV)                                                                                        \
+  (act       ? (NS == 12 ? expert_gemm_kernel<12, kEpiSwiglu, WV> : expert_gemm_kernel<0, kEpiSwiglu, WV>)         \
+   : combine ? (NS == 12 ? expert_gemm_kernel<12, kEpiCombine, WV> : expert_gemm_kernel<0, kEpiCombine, WV>)       \
+             : (NS == 12 ? expert_gemm_kernel<12, kEpiOut, WV> : expert_gemm_kernel<0, kEpiOut, WV>))
+  auto kern = W == 8 ? MXFP4_GEMM_KERN(8) : MXFP4_GEMM_KERN(4);
+#undef MXFP4_GEMM_KERN
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), 0, stream, blocks, bsc, bias, E, N, K, aq, aqx, as,
                      aqf, T, k, offsets, sorted_rows, out, act, ids, gates, cnt, y);
   return hipGetLastError();
 }

@@ -81,6 +81,12 @@ SMALL_CASES = {
     "one_token_per_slot": dict(E=8, N=33, K=2880, T=1, k=4, x_per_slot=True, route="ids+logits"),
     "one_token_k32": dict(E=4, N=31, K=32, T=1, k=3, route="ids"),
     "one_token_all_experts": dict(E=8, N=64, K=544, T=1, k=8, route="logits"),
+    # at least 256 routed rows per expert on average: the grouped GEMM's
+    # eight-wave tiles (256 rows), with partial second tiles, experts of fewer
+    # than 128 rows (Zipf), and more than 64 experts
+    "eight_wave_tiles": dict(E=4, N=200, K=320, T=700, k=2, route="logits"),
+    "eight_wave_zipf": dict(E=8, N=192, K=128, T=1200, k=2, x_per_slot=True, route="zipf+logits"),
+    "eight_wave_many_experts": dict(E=70, N=72, K=64, T=4600, k=4, route="logits"),
 }
 
 
