@@ -351,7 +351,8 @@ int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, cons
  *           is routed when its id lies in [0, E); the grouping must hold
  *           exactly the routed slots (otherwise y is unspecified, though every
  *           access stays inside the arrays).
- *   out     [T, k, N] f32 out, as mxfp4_expert_proj writes it.
+ *   out     [T, k, N] f32 out, as mxfp4_expert_proj writes it; at most 4 GiB
+ *           (T * k * N * 4 bytes; larger returns MXFP4_ERR_INVALID_ARG).
  *   y       [T, N] f32 out: y[t, n] = sum over slots s, in slot order, of
  *           gates[t, s] * out[t, s, n], one fused multiply-add per slot; an
  *           unrouted slot or one with gate 0 adds a zero product.  A token with

@@ -262,6 +262,8 @@ def test_proj_combine_routed_rejects_bad_arguments():
     assert call(out=None) == 1
     assert call(y=None) == 1
     assert call(x=ctypes.c_void_p(8)) == 1
+    assert call(T=1 << 16, N=5760, k=4) == 1                  # out past 4 GiB
+    assert b"4 GiB" in lib.mxfp4_last_error()
     assert call(path=2) == 2                                  # the grouped GEMM needs its workspace
     assert b"workspace" in lib.mxfp4_last_error()
     assert call(T=0, ids=None, gates=None, out=None, y=None) == 0   # nothing to do
