@@ -1269,8 +1269,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (n0 + 32 * c + 8 * q + 4 * half + i < N) __builtin_nontemporal_store(acc[c][4 * q + i], orow + 32 * c + 8 * q + i);
 }
 
-// waves per GEMM workgroup: eight while the routed rows average at least 256
-// per expert, else four
+// waves per GEMM workgroup for the fp32 epilogue: eight while the routed rows
+// average at least 256 per expert, else four
 int gemm_waves(int E, int R) { return (long long)R >= 256LL * E ? 8 : 4; }
 
 struct GemmLayout {
@@ -1378,19 +1378,19 @@ hipError_t launch_expert_gemm(const uint8_t* blocks, const uint8_t* scales, cons
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   // Eight waves (256-row tiles) halve the weight bytes per MFMA where the
-  // experts hold enough rows to fill them; four where many experts hold fewer
-  // than 256 rows (an odd 128-row tile leaves half of an eight-wave tile idle).
-  const int W = gemm_waves(E, R);
+  // experts hold enough rows to fill them, for the fp32 epilogue; four where
+  // many experts hold fewer than 256 rows (an odd 128-row tile leaves half of
+  // an eight-wave tile idle), and for the gated-activation and combine
+  // epilogues, whose work the second workgroup on the CU overlaps.
+  const int W = (act || combine) ? 4 : gemm_waves(E, R);
   const int TM = 32 * W;
   const long long tiles_max = ((long long)(R + TM - 1) / TM + (R < E ? R : E)) * NT;
   const long long grid = (tiles_max + kXcds - 1) / kXcds * kXcds;
   // the gpt-oss-20b widths (K = 2880) have 12 stages
-#define MXFP4_GEMM_KERN(WV)                                                                                        \
-  (act       ? (NS == 12 ? expert_gemm_kernel<12, kEpiSwiglu, WV> : expert_gemm_kernel<0, kEpiSwiglu, WV>)         \
-   : combine ? (NS == 12 ? expert_gemm_kernel<12, kEpiCombine, WV> : expert_gemm_kernel<0, kEpiCombine, WV>)       \
-             : (NS == 12 ? expert_gemm_kernel<12, kEpiOut, WV> : expert_gemm_kernel<0, kEpiOut, WV>))
-  auto kern = W == 8 ? MXFP4_GEMM_KERN(8) : MXFP4_GEMM_KERN(4);
-#undef MXFP4_GEMM_KERN
+  auto kern = act       ? (NS == 12 ? expert_gemm_kernel<12, kEpiSwiglu, 4> : expert_gemm_kernel<0, kEpiSwiglu, 4>)
+              : combine ? (NS == 12 ? expert_gemm_kernel<12, kEpiCombine, 4> : expert_gemm_kernel<0, kEpiCombine, 4>)
+              : W == 8  ? (NS == 12 ? expert_gemm_kernel<12, kEpiOut, 8> : expert_gemm_kernel<0, kEpiOut, 8>)
+                        : (NS == 12 ? expert_gemm_kernel<12, kEpiOut, 4> : expert_gemm_kernel<0, kEpiOut, 4>);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), 0, stream, blocks, bsc, bias, E, N, K, aq, aqx, as,
                      aqf, T, k, offsets, sorted_rows, out, act, ids, gates, cnt, y);
   return hipGetLastError();
