@@ -923,10 +923,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   // ahead) until it is multiplied: three full-width loads of the unit's hi and
   // lo operands.  The scale words of a stage's four k-steps are one load,
   // made during the stage before.
-  v12i ra[kAhead];
+  constexpr int kA = W == 8 ? 4 : kAhead;  // activation k-steps in flight
+  v12i ra[kA];
   u32x4_t asw[2];
   auto load_a = [&](int g, auto jc) {
-    constexpr int J = decltype(jc)::value % kAhead;
+    constexpr int J = decltype(jc)::value % kA;
     const int so = g * kAUnit;
     const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16, so, 0);
     const u32x4_t c1 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, lane * 16 + 1024, so, 0);
@@ -955,7 +956,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   // they just freed, so the LDS latency hides under the remaining MFMAs.
   auto kstep = [&](const uint8_t* sb, const uint32_t (&bsc)[kSubN], uint32_t sw, auto jc, bool next) {
     constexpr int J = decltype(jc)::value;
-    constexpr int A = J % kAhead;
+    constexpr int A = J % kA;
     const v8i ahi = __builtin_shufflevector(ra[A], ra[A], 0, 1, 2, 3, 4, 5, -1, -1);
     const v8i alo = __builtin_shufflevector(ra[A], ra[A], 6, 7, 8, 9, 10, 11, -1, -1);
 #pragma unroll
@@ -1002,7 +1003,26 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int g = s * kStepsPerStage;
         pipeline_fence();  // the reads are issued before the first MFMA
         const u32x4_t sw = asw[X];
-        if (!last) {
+        if (kA == 4) {
+          // each k-step is followed by the activation loads of the k-step
+          // four later (the next stage's), into the ring slot it just freed
+          // (in the last stage, k-steps past the last real block are skipped)
+          kstep(sb, bsc, sw.x, J0{}, true);
+          if (!last) load_a(g + 4, J0{});
+          pipeline_fence();
+          if (!last || g + 1 < nks) kstep(sb, bsc, sw.y, J1{}, true);
+          if (!last) load_a(g + 5, J1{});
+          pipeline_fence();
+          if (!last || g + 2 < nks) kstep(sb, bsc, sw.z, J2{}, true);
+          if (!last) {
+            load_as(s + 1, std::integral_constant<int, 1 - X>{});
+            load_a(g + 6, J2{});
+          }
+          pipeline_fence();
+          if (!last || g + 3 < nks) kstep(sb, bsc, sw.w, J3{}, false);
+          if (!last) load_a(g + 7, J3{});
+          pipeline_fence();
+        } else if (!last) {
           // each k-step is followed by the activation loads of the k-step
           // two later, into the ring slot it just freed; the next stage's
           // scale words go with the first of its k-steps
@@ -1043,6 +1063,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
       load_as(0, J0{});
       load_a(0, J0{});
       load_a(1, J1{});
+      if (kA == 4) {
+        load_a(2, J2{});
+        load_a(3, J3{});
+      }
     }
     store_w(sB0, sS0, J0{});
     lds_barrier();
