@@ -430,7 +430,10 @@ def main():
     head = measure(args.config, args.steps, args.warmup, args.rotate_bytes, fused=True,
                    combine_fused=args.combine_fused)
     p, acc = head["p"], head["acc"]
-    kernel = "expert_gemv" if p.T * p.k <= 8 else "expert_gemm"
+    # the projection's automatic path: the GEMV while the routed rows average at
+    # most 16 per expert they touch, the grouped GEMM beyond
+    R = p.T * p.k
+    kernel = "expert_gemv" if R <= 16 * min(R, p.E) else "expert_gemm"
     gbs = acc["step"] / (head["ms_per_step"] * 1e-3) / 1e9
     # the fused launch moves the routing bytes too, the fused combine the combine's
     kernel_bytes = acc["proj"] + (acc["route"] if head["fused"] else 0) + (acc["combine"] if head["combine_fused"] else 0)

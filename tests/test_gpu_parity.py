@@ -144,8 +144,11 @@ def test_extreme_scale_bytes(lo, hi, shift, T, path):
 # ----------------------------------------------------------------- routing paths
 # one-wave grouping (T * k <= 64), else multi-workgroup routing then grouping
 # by one or more 1024-row chunks; 1, 2 and 8 lane chunks of experts
+# T * k <= 64: one wave groups; T <= 64 and T * k <= 1024: one workgroup routes
+# and groups; beyond: a routing launch and a grouping launch
 ROUTE_CASES = [(16, 4, 32), (13, 5, 32), (64, 1, 100), (65, 1, 100), (256, 4, 32), (257, 4, 32),
-               (40, 7, 300), (300, 3, 300), (1, 32, 512), (1024, 1, 8), (700, 3, 300), (2000, 4, 32)]
+               (40, 7, 300), (300, 3, 300), (1, 32, 512), (1024, 1, 8), (700, 3, 300), (2000, 4, 32),
+               (64, 4, 32), (64, 16, 512), (20, 32, 64), (17, 4, 8), (30, 8, 8), (65, 4, 32)]
 
 
 @pytest.mark.parametrize("route", ["logits", "ids+logits"])
@@ -208,15 +211,17 @@ def test_given_ids_errors_are_flagged():
     check_close(g["y"], y_ref, y_mag, "y over the valid slots")
 
 
-def test_given_ids_errors_flagged_multiworkgroup():
-    """The same with more than 64 rows and 2 chunks (the multi-workgroup grouping)."""
-    _announce("bad given ids, multi-workgroup grouping")
-    T, k, E = 600, 2, 8
+@pytest.mark.parametrize("T", [600, 60])
+def test_given_ids_errors_flagged_multiworkgroup(T):
+    """The same with more than 64 rows: 2 chunks (the multi-workgroup grouping)
+    at T = 600, one workgroup routing and grouping at T = 60."""
+    _announce(f"bad given ids, T={T}")
+    k, E = 2, 8
     p = S.make_custom(E=E, N=64, K=64, T=T, k=k, route="ids+logits")
     ids = np.stack([np.arange(T) % E, (np.arange(T) + 3) % E], axis=1).astype(np.int32)
-    ids[5] = [2, 2]        # repeat
-    ids[550] = [9, 1]      # out of range
-    ids[599] = [7, 7]      # repeat in the second chunk
+    ids[5] = [2, 2]            # repeat
+    ids[T - 50] = [9, 1]       # out of range
+    ids[T - 1] = [7, 7]        # repeat in the last rows
     p.ids_in = ids
     dp = DeviceProblem(p, path=1)
     dp.error_word.fill_(-1)
@@ -224,7 +229,7 @@ def test_given_ids_errors_flagged_multiworkgroup():
     g = dp.results()
     assert g["error_word"] == (B.MXFP4_ROUTE_ERR_ID_RANGE | B.MXFP4_ROUTE_ERR_ID_DUP)
     want = ids.copy()
-    want[550, 0] = -1
+    want[T - 50, 0] = -1
     np.testing.assert_array_equal(g["ids"], want)
     flat = want.reshape(-1)
     valid = np.nonzero(flat >= 0)[0]
