@@ -40,7 +40,8 @@ PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_gemm_gate_up_prefi
 # terms, so this is the grouped GEMM's ceiling in algorithmic flops
 TWO_TERM_CEILING_TFLOPS = 7700.0 / 2
 KERNEL_SOURCES = {
-    "expert_gemv": ["mxfp4_mixture_experts_amd/csrc/expert_gemv.hip", "mxfp4_mixture_experts_amd/csrc/common.h"],
+    "expert_gemv": ["mxfp4_mixture_experts_amd/csrc/expert_gemv.hip", "mxfp4_mixture_experts_amd/csrc/common.h",
+                    "mxfp4_mixture_experts_amd/csrc/route_common.h"],
     "expert_gemm": ["mxfp4_mixture_experts_amd/csrc/expert_gemm.hip", "mxfp4_mixture_experts_amd/csrc/common.h"],
 }
 
@@ -94,8 +95,11 @@ def algorithmic(p, used, swiglu=False):
 
 # ------------------------------------------------------------------ GPU measurement
 def fusable(p):
-    """One token routed from logits, within the single-launch decode's limits."""
-    return p.T == 1 and p.logits is not None and p.E <= 64 and p.K <= 3072
+    """A decode batch routed from logits within the single-launch decode's limits (up to 64
+    tokens and 64 experts, K <= 3072), on the projection's automatic path (the GEMV)."""
+    R = p.T * p.k
+    return (1 <= p.T <= 64 and p.logits is not None and p.ids_in is None and p.E <= 64 and p.K <= 3072
+            and R <= 16 * min(R, p.E))
 
 
 class Workload:
@@ -128,10 +132,10 @@ class Workload:
             self.dp.proj_combine_routed(stream, blocks=b, scales=s)
             return
         if self.fused and self.swiglu:
-            self.dp.decode_swiglu(stream, blocks=b, scales=s)
+            self.decode_swiglu(stream, blocks=b, scales=s)
             return
         if self.fused:
-            self.dp.decode(stream, blocks=b, scales=s)
+            self.decode(stream, blocks=b, scales=s)
         elif self.swiglu:
             self.dp.route_group(stream)
             self.dp.expert_proj_swiglu(stream, blocks=b, scales=s)
@@ -147,13 +151,26 @@ class Workload:
         if self.combine_fused:
             self.dp.proj_combine_routed(stream, blocks=b, scales=s)
         elif self.fused and self.swiglu:
-            self.dp.decode_swiglu(stream, blocks=b, scales=s)
+            self.decode_swiglu(stream, blocks=b, scales=s)
         elif self.fused:
-            self.dp.decode(stream, blocks=b, scales=s)
+            self.decode(stream, blocks=b, scales=s)
         elif self.swiglu:
             self.dp.expert_proj_swiglu(stream, blocks=b, scales=s)
         else:
             self.dp.expert_proj(stream, blocks=b, scales=s)
+
+    def decode(self, stream, blocks, scales):
+        """The single-launch decode: mxfp4_moe_decode for one token, mxfp4_moe_decode_batch beyond."""
+        if self.p.T == 1:
+            self.dp.decode(stream, blocks=blocks, scales=scales)
+        else:
+            self.dp.decode_batch(stream, blocks=blocks, scales=scales)
+
+    def decode_swiglu(self, stream, blocks, scales):
+        if self.p.T == 1:
+            self.dp.decode_swiglu(stream, blocks=blocks, scales=scales)
+        else:
+            self.dp.decode_batch_swiglu(stream, blocks=blocks, scales=scales)
 
     def capture(self, fn, n):
         torch = self.torch
@@ -454,7 +471,8 @@ def main():
         "config": {
             "workload": describe(p),
             "seed": 0,
-            "path": ("moe_decode (route + group + GEMV in one launch)" if head["fused"] else
+            "path": (("moe_decode" if p.T == 1 else "moe_decode_batch")
+                     + " (route + group + GEMV in one launch)" if head["fused"] else
                      "route_group + " + ("expert_proj_combine_routed" if head["combine_fused"] else "expert_proj")
                      + "(auto: " + ("GEMV" if kernel == "expert_gemv" else "GEMM") + ")")
                     + (" + combine" if p.combine and not head["combine_fused"] else ""),
@@ -489,9 +507,13 @@ def main():
         # the fused gated activation (bf16 [T, k, N / 2], the down projection's input)
         # (the one-token one as a single launch, mxfp4_moe_decode_swiglu)
         # (and the down prefill once more with the combine fused into the grouped GEMM)
-        for cfg, steps, swiglu, cf in ((2, 100, False, False), (3, 20, False, False), (4, 40, False, False),
-                                       (1, 200, True, False), (3, 20, True, False), (4, 40, False, True)):
-            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu, fused=swiglu,
+        # (the down decode of 64 tokens both as three calls and as one launch,
+        # mxfp4_moe_decode_batch, with the combine after it)
+        for cfg, steps, swiglu, cf, fz in ((2, 100, False, False, False), (2, 100, False, False, True),
+                                           (3, 20, False, False, False), (4, 40, False, False, False),
+                                           (1, 200, True, False, True), (3, 20, True, False, False),
+                                           (4, 40, False, True, False)):
+            r = measure(cfg, steps, 5, args.rotate_bytes, kernel_reps=steps, swiglu=swiglu, fused=fz,
                         combine_fused=cf)
             a = r["acc"]
             if cfg == 3 and not swiglu:
@@ -518,8 +540,10 @@ def main():
             # the single launch routes too; the fused combine reads and writes the combine's bytes
             a_proj = a["proj"] + (a["route"] if r["fused"] else 0) + (a["combine"] if cf else 0)
             sec.append({
-                "workload": describe(r["p"], swiglu) + (" (routing + projection + activation in one launch)"
-                                                        if r["fused"] else "")
+                "workload": describe(r["p"], swiglu)
+                            + ((" (routing + projection + activation in one launch)" if swiglu else
+                                " (routing, grouping and projection in one launch: mxfp4_moe_decode_batch; "
+                                "then the combine)") if r["fused"] else "")
                             + (" (the combine fused into the grouped GEMM: route_group + "
                                "mxfp4_expert_proj_combine_routed; proj_us covers both)" if cf else ""),
                 "ms_per_step": round(r["ms_per_step"], 4),

@@ -64,6 +64,7 @@ typedef enum {
 #define MXFP4_GEMM_MAX_K 8192        /* grouped-GEMM path: a weight panel's scale rows staged in LDS */
 #define MXFP4_DECODE_MAX_EXPERTS 64  /* mxfp4_moe_decode: experts routed in one wave */
 #define MXFP4_DECODE_MAX_K 3072      /* mxfp4_moe_decode: all of a row's loads in flight at once */
+#define MXFP4_DECODE_MAX_T 64        /* mxfp4_moe_decode_batch: tokens ranked one per lane */
 
 /* Projection paths for mxfp4_expert_proj. */
 #define MXFP4_PATH_AUTO 0  /* GEMV while T * k <= 16 * min(E, T * k), grouped GEMM otherwise */
@@ -302,6 +303,56 @@ int mxfp4_moe_decode_swiglu(const uint16_t* logits, int E, int k, const uint8_t*
                             const uint16_t* bias, int N, int K, const uint16_t* x, int32_t* topk_ids, float* gates,
                             int32_t* expert_offsets, int32_t* sorted_rows, int32_t* error_word, uint16_t* act,
                             void* stream);
+
+/*
+ * A decode batch of up to MXFP4_DECODE_MAX_T tokens: routing, grouping and the
+ * expert projection in a single launch -- mxfp4_moe_route_group (logits route)
+ * followed by mxfp4_expert_proj on the GEMV path, with the same results bit for
+ * bit.  The workgroups of each expert rank that expert among every token's
+ * logits themselves, so no launch waits on another's outputs; one more
+ * workgroup routes and groups the batch into the routing outputs with the code
+ * of the routing launch.  T = 1 runs mxfp4_moe_decode.
+ * (README "Dense routing" for the routing; README "Loading" and
+ * src/experts.linnet fn forward_topk for the decode product, which streams each
+ * chosen expert's four-bit bytes once for all of its tokens.)
+ *
+ *   logits  [T, E] bf16.  1 <= T <= MXFP4_DECODE_MAX_T,
+ *           1 <= E <= MXFP4_DECODE_MAX_EXPERTS, 1 <= k <= min(E, MXFP4_MAX_TOPK).
+ *   blocks, scales, bias, N: as for mxfp4_expert_proj;
+ *           32 <= K <= MXFP4_DECODE_MAX_K, K % 32 == 0.
+ *   x       x_per_slot == 0: [T, K] bf16; x_per_slot != 0: [T, k, K] bf16.
+ *           16-byte aligned.
+ *   topk_ids [T, k] i32, gates [T, k] f32 (or NULL), expert_offsets [E + 1]
+ *   i32, sorted_rows [T * k] i32, error_word [1] i32 (or NULL): out, exactly
+ *           as mxfp4_moe_route_group writes them.
+ *   out     [T, k, N] f32 out, as mxfp4_expert_proj writes it (GEMV path).
+ * One kernel launch, no workspace.  A token with a NaN logit: as
+ * mxfp4_moe_route_group (ids -1 and gates 0 in its slots, its rows left out of
+ * the grouping, error_word MXFP4_ROUTE_ERR_ID_RANGE), and its rows of out are
+ * not written.
+ */
+int mxfp4_moe_decode_batch(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks,
+                           const uint8_t* scales, const uint16_t* bias, int N, int K, const uint16_t* x,
+                           int x_per_slot, int32_t* topk_ids, float* gates, int32_t* expert_offsets,
+                           int32_t* sorted_rows, int32_t* error_word, float* out, void* stream);
+
+/*
+ * The same through the gate/up projection and the gated activation:
+ * mxfp4_moe_route_group (logits route) followed by mxfp4_expert_proj_swiglu on
+ * the GEMV path, with the same results bit for bit.  (src/experts.linnet fn
+ * activate: even rows the gate, odd rows the multiplier.)
+ *
+ *   logits, T, E, k, blocks, scales, bias, K, topk_ids, gates, expert_offsets,
+ *   sorted_rows, error_word: as for mxfp4_moe_decode_batch (x [T, K] bf16, one
+ *           row per token).  N even.
+ *   act     [T, k, N / 2] bf16 out, as mxfp4_expert_proj_swiglu writes it.
+ * One kernel launch, no workspace; the NaN-logit behaviour of
+ * mxfp4_moe_decode_batch.
+ */
+int mxfp4_moe_decode_batch_swiglu(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks,
+                                  const uint8_t* scales, const uint16_t* bias, int N, int K, const uint16_t* x,
+                                  int32_t* topk_ids, float* gates, int32_t* expert_offsets, int32_t* sorted_rows,
+                                  int32_t* error_word, uint16_t* act, void* stream);
 
 /*
  * One decode token's projection through all of its k experts and the

@@ -40,6 +40,8 @@ ENTRY_POINTS = (
     "mxfp4_expert_proj_combine",
     "mxfp4_expert_proj_noalloc",
     "mxfp4_expert_proj_combine_routed",
+    "mxfp4_moe_decode_batch",
+    "mxfp4_moe_decode_batch_swiglu",
 )
 
 _lib_handle = None
@@ -94,6 +96,12 @@ def load_library():
     lib.mxfp4_moe_router.restype = i32
     lib.mxfp4_moe_decode_swiglu.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mxfp4_moe_decode_swiglu.restype = i32
+    lib.mxfp4_moe_decode_batch.argtypes = [vp, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                           vp, vp]
+    lib.mxfp4_moe_decode_batch.restype = i32
+    lib.mxfp4_moe_decode_batch_swiglu.argtypes = [vp, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                                  vp, vp]
+    lib.mxfp4_moe_decode_batch_swiglu.restype = i32
     lib.mxfp4_expert_proj_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.mxfp4_expert_proj_combine.restype = i32
     lib.mxfp4_expert_proj_combine_routed.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp,
@@ -253,6 +261,39 @@ def mxfp4_moe_decode_swiglu(logits, E: int, k: int, blocks, scales, bias, N: int
     dev = act.device
     st = lib.mxfp4_moe_decode_swiglu(
         _ptr(logits, "logits", _BF16, dev), int(E), int(k), _ptr(blocks, "blocks", _U8, dev),
+        _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(N), int(K), _ptr(x, "x", _BF16, dev),
+        _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(error_word, "error_word", _I32, dev), _ptr(act, "act", _BF16, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_moe_decode_batch(logits, T: int, E: int, k: int, blocks, scales, bias, N: int, K: int, x,
+                           x_per_slot: bool, topk_ids, gates, expert_offsets, sorted_rows, out, error_word=None,
+                           stream=None):
+    """Up to 64 decode tokens in one launch (mxfp4_moe_decode_batch): routing and grouping from
+    logits [T,E] bf16 and the projection into out [T,k,N] f32, with the same outputs as
+    mxfp4_moe_route_group followed by mxfp4_expert_proj on the GEMV path."""
+    lib = load_library()
+    dev = out.device
+    st = lib.mxfp4_moe_decode_batch(
+        _ptr(logits, "logits", _BF16, dev), int(T), int(E), int(k), _ptr(blocks, "blocks", _U8, dev),
+        _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(N), int(K), _ptr(x, "x", _BF16, dev),
+        int(bool(x_per_slot)), _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
+        _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),
+        _ptr(error_word, "error_word", _I32, dev), _ptr(out, "out", _F32, dev), _stream(stream, dev))
+    _check(st)
+
+
+def mxfp4_moe_decode_batch_swiglu(logits, T: int, E: int, k: int, blocks, scales, bias, N: int, K: int, x,
+                                  topk_ids, gates, expert_offsets, sorted_rows, act, error_word=None, stream=None):
+    """Up to 64 decode tokens through the gate/up projection and the gated activation in one
+    launch (mxfp4_moe_decode_batch_swiglu): act [T,k,N/2] bf16, with the same outputs as
+    mxfp4_moe_route_group followed by mxfp4_expert_proj_swiglu on the GEMV path."""
+    lib = load_library()
+    dev = act.device
+    st = lib.mxfp4_moe_decode_batch_swiglu(
+        _ptr(logits, "logits", _BF16, dev), int(T), int(E), int(k), _ptr(blocks, "blocks", _U8, dev),
         _ptr(scales, "scales", _U8, dev), _ptr(bias, "bias", _BF16, dev), int(N), int(K), _ptr(x, "x", _BF16, dev),
         _ptr(topk_ids, "topk_ids", _I32, dev), _ptr(gates, "gates", _F32, dev),
         _ptr(expert_offsets, "expert_offsets", _I32, dev), _ptr(sorted_rows, "sorted_rows", _I32, dev),

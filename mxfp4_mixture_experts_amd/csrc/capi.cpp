@@ -275,6 +275,35 @@ int moe_decode_impl(const uint16_t* logits, int E, int k, const uint8_t* blocks,
   if (e != hipSuccess) return hip_fail(e, "moe_decode launch");
   return MXFP4_OK;
 }
+int moe_decode_batch_impl(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks, const uint8_t* scales,
+                          const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot, int32_t* topk_ids,
+                          float* gates, int32_t* expert_offsets, int32_t* sorted_rows, int32_t* error_word,
+                          float* out, uint16_t* act, void* stream) {
+  g_last_error[0] = '\0';
+  if (T < 1 || T > MXFP4_DECODE_MAX_T)
+    return fail(MXFP4_ERR_INVALID_ARG, "T = %d must be in [1, %d]", T, MXFP4_DECODE_MAX_T);
+  if (E < 1 || E > MXFP4_DECODE_MAX_EXPERTS)
+    return fail(MXFP4_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, MXFP4_DECODE_MAX_EXPERTS);
+  if (k < 1 || k > E || k > MXFP4_MAX_TOPK)
+    return fail(MXFP4_ERR_INVALID_ARG, "k = %d must be in [1, min(E = %d, %d)]", k, E, MXFP4_MAX_TOPK);
+  if (N < 1) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+  if (act && N % 2 != 0) return fail(MXFP4_ERR_INVALID_ARG, "N = %d must be even (gate/up row pairs)", N);
+  if (K < 32 || K % 32 != 0 || K > MXFP4_DECODE_MAX_K)
+    return fail(MXFP4_ERR_INVALID_ARG, "K = %d must be a positive multiple of 32 up to %d", K, MXFP4_DECODE_MAX_K);
+  if ((long long)E * N > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "E * N overflows int32");
+  if ((long long)T * k * N > 0x7fffffffLL) return fail(MXFP4_ERR_INVALID_ARG, "T * k * N overflows int32");
+  if (!logits || !blocks || !scales || !x || !topk_ids || !expert_offsets || !sorted_rows || (!out && !act))
+    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
+  if (!gemv_fits(T, K)) return fail(MXFP4_ERR_INVALID_ARG, "K = %d needs more LDS than a workgroup has", K);
+  int st = check_device();
+  if (st != MXFP4_OK) return st;
+  hipError_t e = mxfp4::launch_moe_decode_batch(logits, T, E, k, blocks, scales, bias, N, K, x, x_per_slot, topk_ids,
+                                                gates, expert_offsets, sorted_rows, error_word, out, act,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_decode_batch launch");
+  return MXFP4_OK;
+}
 }  // namespace
 
 int mxfp4_moe_decode(const uint16_t* logits, int E, int k, const uint8_t* blocks, const uint8_t* scales,
@@ -299,6 +328,30 @@ int mxfp4_moe_decode_swiglu(const uint16_t* logits, int E, int k, const uint8_t*
   }
   return moe_decode_impl(logits, E, k, blocks, scales, bias, N, K, x, 0, topk_ids, gates, expert_offsets,
                          sorted_rows, error_word, nullptr, act, stream);
+}
+
+int mxfp4_moe_decode_batch(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks,
+                           const uint8_t* scales, const uint16_t* bias, int N, int K, const uint16_t* x,
+                           int x_per_slot, int32_t* topk_ids, float* gates, int32_t* expert_offsets,
+                           int32_t* sorted_rows, int32_t* error_word, float* out, void* stream) {
+  if (!out) {
+    g_last_error[0] = '\0';
+    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  }
+  return moe_decode_batch_impl(logits, T, E, k, blocks, scales, bias, N, K, x, x_per_slot, topk_ids, gates,
+                               expert_offsets, sorted_rows, error_word, out, nullptr, stream);
+}
+
+int mxfp4_moe_decode_batch_swiglu(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks,
+                                  const uint8_t* scales, const uint16_t* bias, int N, int K, const uint16_t* x,
+                                  int32_t* topk_ids, float* gates, int32_t* expert_offsets, int32_t* sorted_rows,
+                                  int32_t* error_word, uint16_t* act, void* stream) {
+  if (!act) {
+    g_last_error[0] = '\0';
+    return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
+  }
+  return moe_decode_batch_impl(logits, T, E, k, blocks, scales, bias, N, K, x, 0, topk_ids, gates, expert_offsets,
+                               sorted_rows, error_word, nullptr, act, stream);
 }
 
 int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,

@@ -34,9 +34,14 @@
 #include "kernels.h"
 #include "common.h"
 #include "mxfp4_moe.h"
+#include "route_common.h"
 
 namespace mxfp4 {
 namespace {
+
+constexpr int kFusedMaxE = MXFP4_DECODE_MAX_EXPERTS;  // fused decode: experts ranked per lane
+constexpr int kFusedMaxT = MXFP4_DECODE_MAX_T;        // fused decode: tokens, one per lane
+static_assert(kFusedMaxE <= 64 && kFusedMaxT <= 64, "one wave");
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -108,18 +113,151 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU>
+// The routing a fused decode launch computes itself (the outputs of
+// mxfp4_moe_route_group for its logits).
+struct FusedRoute {
+  const uint16_t* logits;
+  int32_t* topk_ids;
+  float* gates;
+  int32_t* offsets;
+  int32_t* sorted_rows;
+  int32_t* error_word;
+};
+
+// The routing outputs of a fused decode launch that concern expert e, by the
+// expert's workgroup chosen for it, from the batch's logits staged in lg (T
+// rows of LP floats).  Wave w takes tokens w, w + WAVES, ..., one at a time,
+// lane j holding expert j's logit: the token's kept experts are found as
+// route_ranked keeps them (k rounds of the largest remaining logit, the lowest
+// lane first among equal ones), its gates as route_ranked computes them (the
+// exponentials relative to the largest logit over the same wave sum), so that
+// every output equals the routing launch's bit for bit.  Writes the id and gate
+// of every slot that holds e, offsets[e] (offsets[E] for the last expert), e's
+// segment of sorted_rows (rows, m of them), and for e = 0 the slots of the
+// tokens with a NaN logit and the error word.  cnt: WAVES x 64 ints; nan_seen:
+// zero on entry.  Every thread of the workgroup calls it.
+template <int WAVES>
+__device__ __forceinline__ void fused_write_routing(const FusedRoute fr, int T, int E, int k, int e, int lane,
+                                                    int wave, const float* lg, int LP, const int* rows, int m,
+                                                    int* cnt, int* nan_seen) {
+  int kept_count = 0;  // lane j: this wave's tokens that keep expert j
+  for (int t = wave; t < T; t += WAVES) {
+    const float l = lane < E ? lg[t * LP + lane] : -INFINITY;
+    if (__ballot(lane < E && l != l)) {
+      if (lane == 0) *nan_seen = 1;
+      if (e == 0 && lane < k) {
+        fr.topk_ids[(size_t)t * k + lane] = -1;
+        if (fr.gates) fr.gates[(size_t)t * k + lane] = 0.f;
+      }
+      continue;
+    }
+    bool taken = false;
+    int slot = 0;
+    float mx = 0.f;
+    for (int s = 0; s < k; s++) {
+      const float top = wave_max(taken || lane >= E ? -INFINITY : l);
+      const uint64_t cand = __ballot(!taken && lane < E && l == top);
+      if (lane == __ffsll((long long)cand) - 1) {
+        taken = true;
+        slot = s;
+      }
+      if (s == 0) mx = top;
+    }
+    const float num = taken ? expf(l - mx) : 0.f;
+    const float sum = wave_sum(num);
+    if (lane == e && taken) {
+      fr.topk_ids[(size_t)t * k + slot] = e;
+      if (fr.gates) fr.gates[(size_t)t * k + slot] = num / sum;
+    }
+    kept_count += taken ? 1 : 0;
+  }
+  cnt[wave * 64 + lane] = kept_count;
+  __syncthreads();
+  if (wave == 0) {
+    int tot = 0;
+    for (int w = 0; w < WAVES; w++) tot += cnt[w * 64 + lane];
+    int inc = tot;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += o;
+    }
+    const int off = __builtin_amdgcn_readlane(inc - tot, e);
+    const int total = __builtin_amdgcn_readlane(inc, 63);
+    if (lane < m) fr.sorted_rows[off + lane] = rows[lane];
+    if (lane == 0) {
+      fr.offsets[e] = off;
+      if (e == E - 1) fr.offsets[E] = total;
+      if (e == 0 && fr.error_word) *fr.error_word = *nan_seen ? MXFP4_ROUTE_ERR_ID_RANGE : 0;
+    }
+  }
+}
+
+// A fused decode launch of T <= 64 tokens (E <= 64): the workgroup of expert e
+// finds its routed rows itself.  The batch's logits are staged in LDS (lg,
+// T x (E + 1) floats: rows padded so that one lane per token reads without
+// bank conflicts) with coalesced loads, all in flight at once; then lane t of
+// wave 0 ranks expert e among token t's logits (the rank definition of
+// route_ranked, evaluated for one expert).  The rows t * k + rank of the
+// tokens that keep e, in ascending t, are the rows mxfp4_moe_route_group
+// groups under e, in its order; a token with a NaN logit keeps no expert.
+// Wave 0 writes them to rows_out; the workgroup chosen to (route) then writes
+// the routing outputs for e, with WAVES x 64 + 1 ints of LDS after lg.
+// Returns the row count (every wave).
+template <int WAVES>
+__device__ __forceinline__ int fused_expert_rows(const FusedRoute fr, int T, int E, int k, int e, int lane, int wave,
+                                                 bool route, float* lg, int* rows_out, int* count) {
+  const int LP = E + 1;
+  int* scratch = reinterpret_cast<int*>(lg + T * LP);
+  constexpr int kPer = (kFusedMaxT + WAVES - 1) / WAVES;  // token rows per wave
+  uint32_t v[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; q++) {
+    const int t = wave + q * WAVES;
+    v[q] = fr.logits[(size_t)min(t, T - 1) * E + min(lane, E - 1)];  // unconditional loads
+  }
+#pragma unroll
+  for (int q = 0; q < kPer; q++) {
+    const int t = wave + q * WAVES;
+    if (t < T && lane < E) lg[t * LP + lane] = bf16_bits_to_f32(v[q]);
+  }
+  if (threadIdx.x == 0) scratch[WAVES * 64] = 0;
+  __syncthreads();
+  if (wave == 0) {
+    const float* row = lg + min(lane, T - 1) * LP;
+    const float le = row[e];
+    int rank = 0;
+    bool nan = false;
+    for (int j = 0; j < E; j++) {
+      const float lj = row[j];
+      rank += (lj > le || (lj == le && j < e)) ? 1 : 0;
+      nan |= lj != lj;
+    }
+    const bool keep = lane < T && !nan && rank < k;
+    const uint64_t mask = __ballot(keep);
+    if (keep) rows_out[lanes_below(mask)] = lane * k + rank;
+    if (lane == 0) *count = __popcll(mask);
+  }
+  __syncthreads();
+  const int m = *count;
+  if (route) fused_write_routing<WAVES>(fr, T, E, k, e, lane, wave, lg, LP, rows_out, m, scratch, scratch + WAVES * 64);
+  __syncthreads();
+  return m;
+}
+
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR = false>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void expert_gemv_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int T, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
-    uint16_t* __restrict__ act, int sc_blk) {
+    uint16_t* __restrict__ act, int sc_blk, FusedRoute fr) {
   // [MT][XS] bf16 token rows, 16 bytes per entry (16 per K group), staged by
   // LDS DMA; entries past K and rows past the pass's count are zeroed in
   // registers when read.  Then, per row block of the workgroup, sc_blk
   // entries of weight scales.
   extern __shared__ uint4 xs[];
   __shared__ int rows_lds[MT];
+  __shared__ int fused_rows[FR ? kFusedMaxT : 1];  // FR: the expert's routed rows and their count
+  __shared__ int fused_count;
   // KS > 1: the KS waves of a row group split K and add their partial sums here
   constexpr int RW = WAVES / KS;  // row groups (16 weight rows each) per workgroup
   static_assert(WAVES % KS == 0, "whole row groups");
@@ -138,10 +276,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   const int wave = threadIdx.x >> 6;
 
   int e, m0, m1;
-  if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
-  e = __builtin_amdgcn_readfirstlane(e);
-  m0 = __builtin_amdgcn_readfirstlane(m0);
-  m1 = __builtin_amdgcn_readfirstlane(m1);
+  if constexpr (FR) {
+    // one row of workgroups per expert by index; the last workgroup of each
+    // (one with the fewest weight-row blocks, done early) writes the expert's
+    // routing outputs
+    e = blockIdx.y;
+    m0 = 0;
+    m1 = __builtin_amdgcn_readfirstlane(fused_expert_rows<WAVES>(fr, T, E, k, e, lane, wave,
+                                                                 blockIdx.x == gridDim.x - 1,
+                                                                 reinterpret_cast<float*>(xs), fused_rows,
+                                                                 &fused_count));
+    if (m1 == 0) return;
+  } else {
+    if (!find_group(offsets, E, R, blockIdx.y, lane, e, m0, m1)) return;
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    m1 = __builtin_amdgcn_readfirstlane(m1);
+  }
 
   // Row blocks of RW * 16 weight rows: this workgroup takes blocks
   // blockIdx.x + j * gridDim.x, j < nb, and streams them back to back (the
@@ -214,7 +365,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     // scalar loads behind branches would each wait for the one before)
     int src[MT];
     {
-      int r = sorted_rows[mb + min(lane, mc - 1)];
+      int r = FR ? fused_rows[mb + min(lane, mc - 1)] : sorted_rows[mb + min(lane, mc - 1)];
       if (lane >= mc || r < 0 || r >= R) r = -1;
       const int s = r < 0 ? 0 : (x_per_slot ? r : r / k);  // row 0 stands in: masked when read
 #pragma unroll
@@ -452,15 +603,6 @@ struct T1Shape {
 
 // Routing parameters of the fused single-token decode: the token's router
 // logits in, the routing outputs (written by workgroup (0, 0)) out.
-struct FusedRoute {
-  const uint16_t* logits;
-  int32_t* topk_ids;
-  float* gates;
-  int32_t* offsets;
-  int32_t* sorted_rows;
-  int32_t* error_word;
-};
-
 // One MXFP4 block's 32 products with 32 staged bf16 inputs, added to a: the
 // block's four code words w (8 codes each) become exact bf16 weights through
 // v_cvt_scalef32_pk_bf16_fp4 with the E8M0 factor sf, and v_dot2_f32_bf16
@@ -482,10 +624,6 @@ __device__ __forceinline__ float block_dot(const uint4 w, uint32_t keep, float s
                                         __builtin_bit_cast(bf16x2_t, xv[d].w), a, false);
   }
   return a;
-}
-
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 // FUSED: the workgroup routes the token itself (E <= 64) instead of reading
@@ -865,10 +1003,11 @@ size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K, int nbpw
   return (gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * 64 + (size_t)nbpw * gemv_sc_entries(WAVES, KS, K)) * 16;
 }
 
-template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU>
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR = false>
 hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                              const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
-                             const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream) {
+                             const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream,
+                             const FusedRoute& fr = FusedRoute{}) {
   // Row blocks per workgroup: enough workgroups for one wave of them over the
   // 256 CUs (as many per CU as the waves allow), each streaming its share of
   // an expert's row blocks with the token rows staged once, within the LDS.
@@ -883,17 +1022,22 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
   G = G < (nblk + nbpw_max - 1) / nbpw_max ? (nblk + nbpw_max - 1) / nbpw_max : G;
   G = G > nblk ? nblk : G;
   const int nbpw = (nblk + G - 1) / G;
-  const size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K, nbpw);
+  size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K, nbpw);
+  // fused routing: the staged logits, T x (E + 1) floats, and the routing
+  // writer's WAVES x 64 + 1 counters
+  if (FR && lds < ((size_t)T * (E + 1) + WAVES * 64 + 1) * 4) lds = ((size_t)T * (E + 1) + WAVES * 64 + 1) * 4;
   // above 64 KB the dynamic LDS limit is raised (to what any K may need)
   static DynLdsLimit gemv_lds(
-      reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>), kGemvMaxDynLds);
+      reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR>), kGemvMaxDynLds);
   if (lds > 65536) {
     const hipError_t err = gemv_lds.ensure();
     if (err != hipSuccess) return err;
   }
-  const dim3 grid(G, groups);
-  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU>), grid, dim3(WAVES * 64), lds, stream, blocks,
-                     scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act, (int)sc);
+  // fused routing: one row of workgroups per expert by index (those of
+  // unused experts write its offset and exit)
+  const dim3 grid(G, FR ? E : groups);
+  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR>), grid, dim3(WAVES * 64), lds, stream,
+                     blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act, (int)sc, fr);
   return hipGetLastError();
 }
 
@@ -950,6 +1094,23 @@ hipError_t launch_gemv_any(const uint8_t* blocks, const uint8_t* scales, const u
 #undef MXFP4_GEMV_LAUNCH
 }
 
+// T = 2 .. 64 tokens routed by the projection launch itself (FusedRoute): the
+// shapes of launch_gemv_any.
+template <bool SWIGLU>
+hipError_t launch_gemv_fused(const FusedRoute& fr, const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias,
+                             int E, int N, int K, const uint16_t* x, int x_per_slot, int T, int k, float* out,
+                             uint16_t* act, hipStream_t stream) {
+#define MXFP4_GEMV_FUSED(MT, W, NCH, NST, KS, OCC)                                                                  \
+  return launch_gemv_shape<MT, W, NCH, NST, KS, OCC, SWIGLU, true>(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, \
+                                                                   nullptr, nullptr, out, act, stream, fr)
+  const GemvShape g = gemv_shape(T, K);
+  if (g.mt == 4) MXFP4_GEMV_FUSED(4, 4, 4, 3, 1, 2);
+  if (g.nch == 4) MXFP4_GEMV_FUSED(16, 8, 4, 2, 1, 2);
+  if (g.nch == 6) MXFP4_GEMV_FUSED(16, 8, 6, 2, 1, 2);
+  MXFP4_GEMV_FUSED(16, 8, 8, 2, 1, 2);
+#undef MXFP4_GEMV_FUSED
+}
+
 }  // namespace
 
 size_t gemv_lds_bytes(int T, int K) {
@@ -996,6 +1157,25 @@ hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint
                        blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr);
   }
   return hipGetLastError();
+}
+
+}  // namespace mxfp4
+
+namespace mxfp4 {
+
+// T <= 64 decode tokens: routing, grouping and the projection in one launch
+// (act != NULL: through the gated activation instead of out).
+hipError_t launch_moe_decode_batch(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks,
+                                   const uint8_t* scales, const uint16_t* bias, int N, int K, const uint16_t* x,
+                                   int x_per_slot, int32_t* topk_ids, float* gates, int32_t* offsets,
+                                   int32_t* sorted_rows, int32_t* error_word, float* out, uint16_t* act,
+                                   hipStream_t stream) {
+  if (T == 1)
+    return launch_moe_decode_t1(logits, E, k, blocks, scales, bias, N, K, x, x_per_slot, topk_ids, gates, offsets,
+                                sorted_rows, error_word, out, act, stream);
+  const FusedRoute fr{logits, topk_ids, gates, offsets, sorted_rows, error_word};
+  if (act) return launch_gemv_fused<true>(fr, blocks, scales, bias, E, N, K, x, x_per_slot, T, k, nullptr, act, stream);
+  return launch_gemv_fused<false>(fr, blocks, scales, bias, E, N, K, x, x_per_slot, T, k, out, nullptr, stream);
 }
 
 }  // namespace mxfp4

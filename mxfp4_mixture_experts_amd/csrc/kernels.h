@@ -29,6 +29,12 @@ hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint
                                 const uint16_t* bias, int N, int K, const uint16_t* x, int x_per_slot,
                                 int32_t* topk_ids, float* gates, int32_t* offsets, int32_t* sorted_rows,
                                 int32_t* error_word, float* out, uint16_t* act, hipStream_t stream);
+// T <= 64 tokens (E <= 64): routing, grouping and the projection in one launch
+hipError_t launch_moe_decode_batch(const uint16_t* logits, int T, int E, int k, const uint8_t* blocks,
+                                   const uint8_t* scales, const uint16_t* bias, int N, int K, const uint16_t* x,
+                                   int x_per_slot, int32_t* topk_ids, float* gates, int32_t* offsets,
+                                   int32_t* sorted_rows, int32_t* error_word, float* out, uint16_t* act,
+                                   hipStream_t stream);
 
 // one token, k slots (topk_ids [k], gates [k]): out [k, N] (or NULL) and the
 // gate-weighted combine y [N] in one launch

@@ -89,6 +89,23 @@ class DeviceProblem:
                                   self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.act,
                                   self.error_word, stream)
 
+    def decode_batch(self, stream=None, blocks=None, scales=None):
+        """Up to 64 tokens from logits: routing, grouping and the projection (GEMV
+        path) in one launch."""
+        p = self.p
+        B.mxfp4_moe_decode_batch(self.logits, p.T, p.E, p.k, self.blocks if blocks is None else blocks,
+                                 self.scales if scales is None else scales, self.bias, p.N, p.K, self.x,
+                                 p.x_per_slot, self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.out,
+                                 self.error_word, stream)
+
+    def decode_batch_swiglu(self, stream=None, blocks=None, scales=None):
+        """Up to 64 tokens from logits through the gated activation in one launch."""
+        p = self.p
+        B.mxfp4_moe_decode_batch_swiglu(self.logits, p.T, p.E, p.k, self.blocks if blocks is None else blocks,
+                                        self.scales if scales is None else scales, self.bias, p.N, p.K, self.x,
+                                        self.topk_ids, self.gates, self.offsets, self.sorted_rows, self.act,
+                                        self.error_word, stream)
+
     def proj_combine(self, stream=None, blocks=None, scales=None, with_out=True):
         """One token (T = 1): every slot's projection and the combine in one launch,
         from the routing already in topk_ids and gates."""

@@ -140,6 +140,32 @@ def test_moe_decode_swiglu_rejects_bad_arguments(kw):
     assert lib.mxfp4_last_error() != b""
 
 
+def _decode_batch(lib, T=64, E=32, k=4, N=64, K=2880, ptr=16, logits=16, out=16, swiglu=False):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    lg = ctypes.c_void_p(logits) if logits else None
+    o = ctypes.c_void_p(out) if out else None
+    if swiglu:
+        return lib.mxfp4_moe_decode_batch_swiglu(lg, T, E, k, p, p, None, N, K, p, p, None, p, p, None, o, None)
+    return lib.mxfp4_moe_decode_batch(lg, T, E, k, p, p, None, N, K, p, 0, p, None, p, p, None, o, None)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("kw", [
+    dict(T=0), dict(T=65), dict(E=0), dict(E=65), dict(k=0), dict(k=5, E=4), dict(k=33, E=64), dict(N=0),
+    dict(K=0), dict(K=100), dict(K=3104), dict(ptr=0), dict(ptr=8), dict(logits=0), dict(out=0),
+])
+def test_moe_decode_batch_rejects_bad_arguments(kw, swiglu):
+    lib = B.load_library()
+    assert _decode_batch(lib, swiglu=swiglu, **kw) == 1, kw
+    assert lib.mxfp4_last_error() != b""
+
+
+def test_moe_decode_batch_swiglu_needs_even_n():
+    lib = B.load_library()
+    assert _decode_batch(lib, N=63, swiglu=True) == 1
+    assert b"even" in lib.mxfp4_last_error()
+
+
 def test_expert_proj_t0_is_a_noop():
     lib = B.load_library()
     assert _proj(lib, T=0, ptr=0) == 0
