@@ -632,23 +632,88 @@ __device__ __forceinline__ float block_dot(const uint4 w, uint32_t keep, float s
 // are chosen, and workgroup row blockIdx.y takes the blockIdx.y-th chosen
 // expert in index order; its slot is its count, its routed row the slot.
 // The same arithmetic as the routing kernel, so the outputs are identical.
-template <int QUADS, int WAVES, bool FUSED, bool SWIGLU>
+// The routing outputs of a fused one-row-per-workgroup decode of T tokens
+// (T * k <= E <= 64), by the first workgroup: the tokens' logits staged in LDS
+// by all its waves, then wave 0 routes them one at a time with the routing
+// launch's arithmetic (lane e: expert e's rank; the gates over the same wave
+// sum), writes ids and gates, counts the rows per expert, and places each row
+// after the rows of its expert with a lower token (the grouping's order).
+template <int WAVES>
+__device__ __forceinline__ void multi_route_outputs(const FusedRoute& fr, int T, int E, int k, int lane, int wave) {
+  __shared__ uint16_t lg[kFusedMaxT * kFusedMaxE];  // T rows of E logits (T * k <= E)
+  __shared__ int8_t slot[kFusedMaxT * 64];        // token t, expert e: its slot, or -1
+  for (int i = threadIdx.x; i < T * E; i += WAVES * 64) lg[i] = fr.logits[i];
+  __syncthreads();
+  if (wave != 0) return;
+  int cnt = 0;  // lane e: rows of expert e
+  bool nan_seen = false;
+  for (int t = 0; t < T; t++) {
+    const float l = lane < E ? bf16_bits_to_f32(lg[t * E + lane]) : -INFINITY;
+    int rank = 0;
+    for (int j = 0; j < E; j++) {
+      const float lj = readlane_f(l, j);
+      rank += (lj > l || (lj == l && j < lane)) ? 1 : 0;
+    }
+    const bool ok = __ballot(lane < E && l != l) == 0;
+    const bool chosen = ok && lane < E && rank < k;
+    if (ok) {
+      const float mx = readlane_f(l, __ffsll((long long)__ballot(chosen && rank == 0)) - 1);
+      const float num = chosen ? expf(l - mx) : 0.f;
+      const float sum = wave_sum(num);
+      if (chosen) {
+        fr.topk_ids[(size_t)t * k + rank] = lane;
+        if (fr.gates) fr.gates[(size_t)t * k + rank] = num / sum;
+      }
+    } else {
+      nan_seen = true;
+      if (lane < k) {
+        fr.topk_ids[(size_t)t * k + lane] = -1;
+        if (fr.gates) fr.gates[(size_t)t * k + lane] = 0.f;
+      }
+    }
+    slot[t * 64 + lane] = (int8_t)(chosen ? rank : -1);
+    cnt += chosen ? 1 : 0;
+  }
+  int inc = cnt;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  const int total = __shfl(inc, 63, 64);
+  if (lane < E) fr.offsets[lane] = inc - cnt;
+  if (lane == 0) {
+    fr.offsets[E] = total;
+    if (fr.error_word) *fr.error_word = nan_seen ? MXFP4_ROUTE_ERR_ID_RANGE : 0;
+  }
+  int run = inc - cnt;
+  for (int t = 0; t < T; t++) {
+    const int s = slot[t * 64 + lane];
+    if (s >= 0) fr.sorted_rows[run++] = t * k + s;
+  }
+}
+
+template <int QUADS, int WAVES, bool FUSED, bool SWIGLU, bool MULTI = false>
 __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, float* __restrict__ out,
-    uint16_t* __restrict__ act, FusedRoute fr) {
+    uint16_t* __restrict__ act, FusedRoute fr, int T) {
   using Sh = T1Shape<QUADS, WAVES>;
   __shared__ uint4 xs1[kT1MaxKB * 4];        // the token row: 4 entries of 8 bf16 per block
   __shared__ uint4 sc1[Sh::kScBlocks];       // the workgroup's scale rows, from their aligned blocks
   const int KB = K >> 5;
   const int K8 = K >> 3;
-  const int R = k;  // one token
+  const int R = T * k;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int e, m0, m1;
   int fused_row = -1;
   if constexpr (FUSED) {
+    // MULTI: workgroup row blockIdx.y serves token blockIdx.y / k and the
+    // (blockIdx.y % k)-th of its experts in index order; else one token
+    const int tok = MULTI ? (int)blockIdx.y / k : 0;
+    const int jsel = (int)blockIdx.y - tok * k;
+    const uint16_t* lrow = fr.logits + (size_t)tok * E;
     float l = -INFINITY;
     int rank = 0;
     if (E == 32) {
@@ -658,7 +723,7 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
       // uniform value.  Other counts take the vector load below (a second
       // specialised path made the kernel larger and its start slower).
       const __attribute__((address_space(4))) uint32_t* lw =
-          (const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(fr.logits);
+          (const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(lrow);
       uint32_t wv[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) wv[i] = lw[i];
@@ -674,7 +739,7 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
         rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
       }
     } else {
-      l = lane < E ? bf16_bits_to_f32(fr.logits[lane]) : -INFINITY;
+      l = lane < E ? bf16_bits_to_f32(lrow[lane]) : -INFINITY;
       for (int jj = 0; jj < E; jj++) {
         const float lj = readlane_f(l, jj);
         rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
@@ -687,7 +752,9 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     const bool ok = __ballot(lane < E && l != l) == 0;
     const bool chosen = ok && lane < E && rank < k;
     const uint64_t mask = __ballot(chosen);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
+    if (MULTI && blockIdx.x == 0 && blockIdx.y == 0) {
+      multi_route_outputs<WAVES>(fr, T, E, k, lane, (int)(threadIdx.x >> 6));
+    } else if (!MULTI && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
       // the routing outputs: ids and gates by slot, offsets, grouped rows
       if (ok) {
         const float mx = readlane_f(l, __ffsll((long long)__ballot(chosen && rank == 0)) - 1);
@@ -708,10 +775,10 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
         if (fr.error_word) *fr.error_word = ok ? 0 : MXFP4_ROUTE_ERR_ID_RANGE;
       }
     }
-    const uint64_t mine = __ballot(chosen && lanes_below(mask) == (int)blockIdx.y);
+    const uint64_t mine = __ballot(chosen && lanes_below(mask) == jsel);
     if (mine == 0) return;
     e = __builtin_amdgcn_readfirstlane(__ffsll((long long)mine) - 1);
-    fused_row = __builtin_amdgcn_readlane(rank, e);
+    fused_row = tok * k + __builtin_amdgcn_readlane(rank, e);
     m0 = 0;
     m1 = 1;
   } else {
@@ -765,10 +832,10 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     // its load then waits behind the weight loads instead of in front of them.
     int src = 0;
     if (FUSED) {
-      src = x_per_slot ? fused_row : 0;
-    } else if (x_per_slot) {
+      src = x_per_slot ? fused_row : fused_row / k;
+    } else if (x_per_slot || T > 1) {
       const int r_raw = sorted_rows[mb];
-      src = (r_raw < 0 || r_raw >= R) ? 0 : r_raw;
+      src = (r_raw < 0 || r_raw >= R) ? 0 : (x_per_slot ? r_raw : r_raw / k);
     }
     if (mb > m0) bare_barrier<63>();  // the previous row is done with the staged token row
     // ---- LDS DMAs (scale blocks, then the token row), spread over the waves;
@@ -981,6 +1048,13 @@ constexpr int kT1Quads = MXFP4_T1_QUADS;
 constexpr int kT1Waves = MXFP4_T1_WAVES;
 constexpr int kT1Rows = T1Shape<kT1Quads, kT1Waves>::kRows;
 
+// The one-token kernel's streaming (a workgroup row per expert, or per routed
+// row when it routes) while the routed rows number no more than the experts:
+// few experts then hold two rows, and the multi-token kernel's 16-row MFMA
+// tiles would run mostly empty (at the gpt-oss decode shapes, 2 to 4 tokens:
+// 21-33 against 30-42 us).  K <= 3072: all of a row's loads in flight at once.
+inline bool gemv_one_row(int T, int k, int E, int K) { return (long long)T * k <= E && K / 32 <= kT1MaxKB; }
+
 // largest dynamic LDS a launch may use (the rest of the 160 KB holds rows_lds)
 constexpr int kGemvMaxDynLds = 160 * 1024 - 1024;
 
@@ -1075,11 +1149,11 @@ template <bool SWIGLU>
 hipError_t launch_gemv_any(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                            const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
                            const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream) {
-  if (T == 1 && K / 32 <= kT1MaxKB) {
-    const dim3 grid((N + kT1Rows - 1) / kT1Rows, k < E ? k : E);
+  if (gemv_one_row(T, k, E, K)) {
+    const dim3 grid((N + kT1Rows - 1) / kT1Rows, T * k < E ? T * k : E);
     hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, false, SWIGLU>), grid, dim3(kT1Waves * 64), 0,
                        stream, blocks, scales, bias, E, N, K, x, x_per_slot, k, offsets, sorted_rows, out, act,
-                       FusedRoute{});
+                       FusedRoute{}, T);
     return hipGetLastError();
   }
 #define MXFP4_GEMV_LAUNCH(MT, W, NCH, NST, KS, OCC)                                                               \
@@ -1114,7 +1188,7 @@ hipError_t launch_gemv_fused(const FusedRoute& fr, const uint8_t* blocks, const 
 }  // namespace
 
 size_t gemv_lds_bytes(int T, int K) {
-  if (T == 1 && K / 32 <= kT1MaxKB) return 0;  // static LDS only
+  if (T == 1 && K / 32 <= kT1MaxKB) return 0;  // static LDS only (more tokens: the larger of the two shapes)
   const GemvShape g = gemv_shape(T, K);
   return gemv_lds_for(g.mt, g.waves, g.nch, g.nst, g.ks, K, 1);
 }
@@ -1151,10 +1225,10 @@ hipError_t launch_moe_decode_t1(const uint16_t* logits, int E, int k, const uint
   const FusedRoute fr{logits, topk_ids, gates, offsets, sorted_rows, error_word};
   if (act) {
     hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, true>), grid, dim3(kT1Waves * 64), 0, stream,
-                       blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, nullptr, act, fr);
+                       blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, nullptr, act, fr, 1);
   } else {
     hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, false>), grid, dim3(kT1Waves * 64), 0, stream,
-                       blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr);
+                       blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr, 1);
   }
   return hipGetLastError();
 }
@@ -1174,6 +1248,17 @@ hipError_t launch_moe_decode_batch(const uint16_t* logits, int T, int E, int k, 
     return launch_moe_decode_t1(logits, E, k, blocks, scales, bias, N, K, x, x_per_slot, topk_ids, gates, offsets,
                                 sorted_rows, error_word, out, act, stream);
   const FusedRoute fr{logits, topk_ids, gates, offsets, sorted_rows, error_word};
+  if (gemv_one_row(T, k, E, K)) {
+    // as expert_proj's GEMV for so few rows: one routed row per workgroup row
+    const dim3 grid((N + kT1Rows - 1) / kT1Rows, T * k);
+    if (act)
+      hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, true, true>), grid, dim3(kT1Waves * 64), 0,
+                         stream, blocks, scales, bias, E, N, K, x, 0, k, nullptr, nullptr, nullptr, act, fr, T);
+    else
+      hipLaunchKernelGGL((expert_gemv_t1_kernel<kT1Quads, kT1Waves, true, false, true>), grid, dim3(kT1Waves * 64), 0,
+                         stream, blocks, scales, bias, E, N, K, x, x_per_slot, k, nullptr, nullptr, out, nullptr, fr, T);
+    return hipGetLastError();
+  }
   if (act) return launch_gemv_fused<true>(fr, blocks, scales, bias, E, N, K, x, x_per_slot, T, k, nullptr, act, stream);
   return launch_gemv_fused<false>(fr, blocks, scales, bias, E, N, K, x, x_per_slot, T, k, out, nullptr, stream);
 }

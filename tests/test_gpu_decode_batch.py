@@ -8,7 +8,8 @@ for bit, outputs within the projection's bound).  The shapes take both kernel
 shapes of the multi-token GEMV (up to 4 tokens, and more), experts with more
 rows than one pass holds, k = 1, k = E, up to 64 experts and tokens, partial
 weight-row blocks, shared and per-slot inputs, T = 1 (the one-token decode),
-tokens with a NaN logit, and the model-size down decode of 64 tokens.
+batches with no more routed rows than experts (a workgroup row per routed
+row), tokens with a NaN logit, and the model-size down decode of 64 tokens.
 """
 import numpy as np
 import pytest
@@ -104,17 +105,18 @@ def test_decode_batch_swiglu_cases(case):
     np.testing.assert_array_equal(g["act"], g2["act"])
 
 
-def test_decode_batch_nan_tokens():
+@pytest.mark.parametrize("T,E,k", [(40, 16, 4), (6, 32, 4), (3, 8, 2)])
+def test_decode_batch_nan_tokens(T, E, k):
     """Tokens with a NaN logit keep no expert: ids -1, gates 0, their rows left
     out of the grouping and of out, the range error; the other tokens as the
-    separate calls."""
-    T, E, k, N = 40, 16, 4, 96
-    _announce("decode batch with NaN logits")
-    p = S.make_custom(E=E, N=N, K=256, T=T, k=k, route="logits", tag=810)
+    separate calls.  (T * k <= E: the one-row-per-workgroup kernel.)"""
+    N = 96
+    _announce(f"decode batch with NaN logits T={T} E={E} k={k}")
+    p = S.make_custom(E=E, N=N, K=256, T=T, k=k, route="logits", tag=810 + T)
     p.logits = p.logits.copy()
-    bad = [0, 17, T - 1]
+    bad = sorted({0, T // 2, T - 1})
     p.logits[0, 3] = NAN_BF16
-    p.logits[17, :] = NAN_BF16
+    p.logits[T // 2, :] = NAN_BF16
     p.logits[T - 1, E - 1] = NAN_BF16
     g = _batch(p)
     assert g["error_word"] == B.MXFP4_ROUTE_ERR_ID_RANGE
