@@ -109,7 +109,8 @@ class Workload:
         from mxfp4_mixture_experts_amd import synthetic as S
         from mxfp4_mixture_experts_amd.runner import DeviceProblem
         self.torch = torch
-        self.p = S.make_config(cfg_index)
+        # a workload index, or a problem built by the caller
+        self.p = S.make_config(cfg_index) if isinstance(cfg_index, int) else cfg_index
         self.fused = fused and fusable(self.p)
         self.swiglu = swiglu
         # many tokens: the projection with the combine fused in (mxfp4_expert_proj_combine_routed)
@@ -235,6 +236,7 @@ def describe(p, swiglu=False):
         "down_decode_t64": "gpt-oss-20b down decode",
         "gate_up_prefill_t4096": "gpt-oss-20b gate_up prefill",
         "down_prefill_zipf_t2048": "gpt-oss-20b down prefill, Zipf(1.2) routing",
+        "gate_up_decode_t4": "gpt-oss-20b gate_up decode of a 4-token batch",
     }[p.name]
     if swiglu:
         return (f"{name} + gated activation: E={p.E} N={p.N} K={p.K} T={p.T} top-{p.k}, MXFP4 blocks "
@@ -509,7 +511,12 @@ def main():
         # (and the down prefill once more with the combine fused into the grouped GEMM)
         # (the down decode of 64 tokens both as three calls and as one launch,
         # mxfp4_moe_decode_batch, with the combine after it)
+        # (and a decode batch of 4 tokens at gate_up, both ways: the one-row-per-workgroup GEMV)
+        from mxfp4_mixture_experts_amd import synthetic as S
+        p4 = S.make_custom(E=32, N=5760, K=2880, T=4, k=4, route="logits", tag=1204)
+        p4.name = "gate_up_decode_t4"
         for cfg, steps, swiglu, cf, fz in ((2, 100, False, False, False), (2, 100, False, False, True),
+                                           (p4, 200, False, False, False), (p4, 200, False, False, True),
                                            (3, 20, False, False, False), (4, 40, False, False, False),
                                            (1, 200, True, False, True), (3, 20, True, False, False),
                                            (4, 40, False, True, False)):
@@ -542,8 +549,8 @@ def main():
             sec.append({
                 "workload": describe(r["p"], swiglu)
                             + ((" (routing + projection + activation in one launch)" if swiglu else
-                                " (routing, grouping and projection in one launch: mxfp4_moe_decode_batch; "
-                                "then the combine)") if r["fused"] else "")
+                                " (routing, grouping and projection in one launch: mxfp4_moe_decode_batch"
+                                + ("; then the combine)" if r["p"].combine else ")")) if r["fused"] else "")
                             + (" (the combine fused into the grouped GEMM: route_group + "
                                "mxfp4_expert_proj_combine_routed; proj_us covers both)" if cf else ""),
                 "ms_per_step": round(r["ms_per_step"], 4),
