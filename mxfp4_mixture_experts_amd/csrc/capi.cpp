@@ -81,7 +81,8 @@ static_assert(mxfp4::kGemmStaticScratchBytes == MXFP4_NOALLOC_SCRATCH_BYTES, "on
 // noalloc: the grouped GEMM's scratch is the library's static device array
 // (workspace and workspace_bytes are ignored).  y != NULL: out, then y [T, N]
 // = the gate-weighted combine of each token's routed slots (ids, gates [T, k]),
-// fused into the grouped GEMM, after the projection on the GEMV path.
+// fused into the grouped GEMM; on the GEMV path in the same launch while T * k
+// <= E, else after the projection.
 int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
                      const uint16_t* x, int x_per_slot, int T, int k, const int32_t* expert_offsets,
                      const int32_t* sorted_rows, float* out, uint16_t* act, int path, void* workspace,
@@ -132,11 +133,12 @@ int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_
     if (se != hipSuccess) return hip_fail(se, "static scratch address");
   }
   hipError_t e;
-  if (p == MXFP4_PATH_GEMV) {
+  if (p == MXFP4_PATH_GEMV && y) {
+    e = mxfp4::launch_expert_gemv_combine(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets,
+                                          sorted_rows, ids, gates, out, y, static_cast<hipStream_t>(stream));
+  } else if (p == MXFP4_PATH_GEMV) {
     e = mxfp4::launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
                                   out, act, static_cast<hipStream_t>(stream));
-    if (e == hipSuccess && y)
-      e = mxfp4::launch_combine(out, gates, T, k, N, y, static_cast<hipStream_t>(stream), ids, E);
   } else {
     e = mxfp4::launch_expert_gemm(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, expert_offsets, sorted_rows,
                                   out, act, workspace, static_cast<hipStream_t>(stream), ids, gates, y);

@@ -40,7 +40,13 @@ hipError_t launch_moe_decode_batch(const uint16_t* logits, int T, int E, int k, 
 // gate-weighted combine y [N] in one launch
 hipError_t launch_proj_combine_t1(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
                                   int K, const uint16_t* x, int x_per_slot, int k, const int32_t* topk_ids,
-                                  const float* gates, float* out, float* y, hipStream_t stream);
+                                  const float* gates, float* out, float* y, hipStream_t stream, int T = 1);
+// the routed projection (GEMV path) and the gate-weighted combine: one launch
+// while T * k <= E (and K <= 3072), else the projection and the combine
+hipError_t launch_expert_gemv_combine(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E,
+                                      int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
+                                      const int32_t* offsets, const int32_t* sorted_rows, const int32_t* topk_ids,
+                                      const float* gates, float* out, float* y, hipStream_t stream);
 
 // expert_gemm.hip
 size_t gemm_workspace_bytes(int E, int N, int T, int k, int K, int x_per_slot);

@@ -8,7 +8,8 @@ paths.  On the grouped-GEMM path the combine runs inside the GEMM, summed by
 whichever tile brings a token's last routed row; the shapes below give tokens
 whose slots land in different row tiles and weight panels, partial panels,
 widths with N % 4 != 0 (the scalar store and sum), k = 1, k = E and more than
-64 experts.  The model-size down prefill is checked bit for bit against the
+64 experts.  On the GEMV path, batches of up to 4 tokens with T * k <= E run
+the projection and the sums in one launch (a workgroup per token and row block).  The model-size down prefill is checked bit for bit against the
 separate calls and for determinism over repeated runs (the tiles' finishing
 order varies from run to run; y must not).
 """
@@ -41,6 +42,10 @@ FUSED_CASES = {
     "one_token": dict(E=8, N=96, K=64, T=1, k=2, route="logits"),
     "all_experts_k8": dict(E=8, N=192, K=128, T=64, k=8, x_per_slot=True, route="logits"),
     "given_ids": dict(E=12, N=392, K=2880, T=70, k=4, x_per_slot=True, route="ids+logits"),
+    # T * k <= E: on the GEMV path a workgroup sums one token's slots (one launch)
+    "small_batch_down": dict(E=32, N=2880, K=2880, T=4, k=4, x_per_slot=True, route="logits"),
+    "small_batch_shared": dict(E=16, N=200, K=320, T=3, k=4, route="logits"),
+    "small_given_ids": dict(E=12, N=96, K=256, T=3, k=4, x_per_slot=True, route="ids+logits"),
 }
 
 
@@ -97,21 +102,23 @@ def test_fused_combine_unrouted_tokens():
         np.testing.assert_array_equal(g["y"], g2["y"])
         np.testing.assert_array_equal(g["out"][good], g2["out"][good])
 
-    q = S.make_custom(E=E, N=200, K=128, T=50, k=k, x_per_slot=True, route="ids+logits", combine=True, tag=641)
-    q.ids_in = np.array(q.ids_in, dtype=np.int32, copy=True)
-    q.ids_in[3, 1] = -1
-    q.ids_in[7, 0] = E + 5
-    q.ids_in[20, :] = -2            # a token with no valid id at all
-    for path in (B.MXFP4_PATH_GEMV, B.MXFP4_PATH_GEMM):
-        dp = DeviceProblem(q, path=path)
-        dp.route_group()
-        dp.y.fill_(float("nan"))
-        dp.proj_combine_routed()
-        g = dp.results()
-        assert g["error_word"] & B.MXFP4_ROUTE_ERR_ID_RANGE
-        assert np.all(g["y"][20] == 0.0)
-        g2 = _separate(q, path)
-        np.testing.assert_array_equal(g["y"], g2["y"])
+    for T2, bad2 in ((50, [3, 7, 20]), (4, [0, 1, 3])):  # T2 * k <= E: the one-launch GEMV combine
+        q = S.make_custom(E=E, N=200, K=128, T=T2, k=k, x_per_slot=True, route="ids+logits", combine=True,
+                          tag=641 + T2)
+        q.ids_in = np.array(q.ids_in, dtype=np.int32, copy=True)
+        q.ids_in[bad2[0], 1] = -1
+        q.ids_in[bad2[1], 0] = E + 5
+        q.ids_in[bad2[2], :] = -2       # a token with no valid id at all
+        for path in (B.MXFP4_PATH_GEMV, B.MXFP4_PATH_GEMM):
+            dp = DeviceProblem(q, path=path)
+            dp.route_group()
+            dp.y.fill_(float("nan"))
+            dp.proj_combine_routed()
+            g = dp.results()
+            assert g["error_word"] & B.MXFP4_ROUTE_ERR_ID_RANGE
+            assert np.all(g["y"][bad2[2]] == 0.0)
+            g2 = _separate(q, path)
+            np.testing.assert_array_equal(g["y"], g2["y"])
 
 
 def test_fused_combine_model_size_deterministic():
