@@ -108,9 +108,14 @@ __device__ __forceinline__ void lds_barrier() {
 // the bias of a projection without one
 __device__ const uint16_t kZeroBf16 = 0;
 
+// word 3 of a raw buffer resource (stride 0, byte offsets, 32-bit data format)
+constexpr int kWBufferFlags = 0x00020000;
+// cache policy of a buffer load: non-temporal (streamed data read once)
+constexpr int kNtPolicy = 2;
+
 __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   // 2^(s - 127) as an fp32 bit pattern; s = 0 is the subnormal 2^-127
-  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+  return __uint_as_float(max(s << 23, 0x00400000u));  // s >= 1: at least 2^-126 = 0x00800000
 }
 
 // The routing a fused decode launch computes itself (the outputs of
@@ -244,7 +249,7 @@ __device__ __forceinline__ int fused_expert_rows(const FusedRoute fr, int T, int
   return m;
 }
 
-template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR = false>
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR = false, bool TR2 = false>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void expert_gemv_kernel(
     const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     int E, int N, int K, const uint16_t* __restrict__ x, int x_per_slot, int T, int k,
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   // re-read the row's last block and meet zero activations)
   const int NITC = (NIT + KS * NST * NCH - 1) / (KS * NST * NCH) * (KS * NST * NCH);
   const int XS = (NITC * 16 + 63) / 64 * 64 + 1;  // whole 64-entry DMAs, +1 spreads rows over banks
-  static_assert(NST == 2 || NST == 3, "two or three chunks in flight");
+  static_assert(NST >= 2 && NST <= 4, "two to four chunks in flight");
   static_assert(NCH % 2 == 0, "whole squares of 16 rows x 8 blocks");
   const int R = T * k;
   const int lane = threadIdx.x & 63;
@@ -314,22 +319,37 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   // step 1: the chunk's groups; step 0: the first square again (a placeholder
   // request, almost free).  Rows past N re-read row N - 1 and blocks past K
   // the row's last block; they meet zero activations.
-  const uint4* wbase = reinterpret_cast<const uint4*>(blocks) + (size_t)e * N * KB;
+  // The expert's codes as one buffer resource (at most 4 GiB, checked on the
+  // host): a 32-bit lane offset per row half and the K position in the scalar
+  // offset.  A lane's blocks past K fall in the next row, or past the expert's
+  // last byte, where the resource returns zeros: finite codes that meet zero
+  // activations.
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(blocks + (size_t)e * N * KB * 16), (short)0, (int)((uint32_t)N * (uint32_t)(KB * 16)),
+      kWBufferFlags);
   auto load_chunk = [&](int wr, int c0, uint4 (&w)[NCH], int step = 1) {
+    const uint32_t voff[2] = {(uint32_t)min(wr + (lane >> 3), N - 1) * (uint32_t)(KB * 16) + (lane & 7) * 16,
+                              (uint32_t)min(wr + 8 + (lane >> 3), N - 1) * (uint32_t)(KB * 16) + (lane & 7) * 16};
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int r = min(wr + 8 * (i & 1) + (lane >> 3), N - 1);
-      const int b = min((c0 + (i & ~1) * step) * 4 + (lane & 7), KB - 1);
-      w[i] = load_nt(wbase + (size_t)r * KB + b);
+      const u32x4_t v =
+          __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)voff[i & 1], (c0 + (i & ~1) * step) * 64, kNtPolicy);
+      w[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
-  // The MFMA wants lane l on row l % 16 and block 4 g + l / 16 of K group g:
-  // each K group of a square passes through the wave's own 1 KB of LDS, [16
-  // rows][4 pieces of 16 bytes] with piece b of row r at b ^ (r / 4 % 4), so
-  // that the writes (2 rows per 16 lanes) and the reads (16 rows, one piece)
+  // The MFMA wants lane l on row l % 16 and block 4 g + l / 16 of K group g.
+  // TR2: each square passes through the wave's own 2 KB of LDS, [16 rows][8
+  // pieces of 16 bytes] with piece b of row r at b ^ (r / 2 % 8), written by
+  // every lane before the square's first group.  Otherwise (less LDS, for the
+  // widest K) each K group passes through 1 KB, [16 rows][4 pieces] with piece
+  // b of row r at b ^ (r / 4 % 4), written by the lanes that hold it.  Either
+  // way the writes (2 rows per 16 lanes) and the reads (16 rows, one piece)
   // hit distinct banks.  A wave's LDS accesses complete in order.
-  uint8_t* trw = reinterpret_cast<uint8_t*>(xs + MT * XS) + wave * 1024;
-  auto tr_at = [&](int r, int b) { return trw + r * 64 + ((b ^ ((r >> 2) & 3)) << 4); };
+  constexpr int kTrBytes = TR2 ? 2048 : 1024;
+  uint8_t* trw = reinterpret_cast<uint8_t*>(xs + MT * XS) + wave * kTrBytes;
+  auto tr_at = [&](int r, int b) {
+    return TR2 ? trw + r * 128 + ((b ^ ((r >> 1) & 7)) << 4) : trw + r * 64 + ((b ^ ((r >> 2) & 3)) << 4);
+  };
 
   // ---- weight scales of block j: rows row0 .. row0 + RW * 16 - 1 (clamped to
   // N - 1), contiguous in memory: the aligned 16-byte blocks from the one
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     // the same blocks through the (global) scales pointer, so loads stay global
     s_blocks = reinterpret_cast<const uint4*>(scales - (sbase - s_blk0));
   };
-  uint4* sc_lds = xs + MT * XS + WAVES * 64;
+  uint4* sc_lds = xs + MT * XS + WAVES * (kTrBytes / 16);
 
   for (int mb = m0; mb < m1; mb += MT) {
     const int mc = min(MT, m1 - mb);
@@ -360,12 +380,32 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     // repeats one: the same bytes to the same place).  Lanes past the data
     // read a clamped source into padding that is never read.
     bare_barrier<63>();  // the previous pass is done with the staged rows (its reads have returned)
-    // the pass's routed rows: one vector load (lane m, an unconditional read
-    // of a clamped index), then token row m's source as a uniform value (MT
-    // scalar loads behind branches would each wait for the one before)
+    uint4 wq[NST][NCH];  // the ring of chunks in flight
+    const int g_first = kpart * (NITC / KS);  // this wave's first K group
+    // Without fused routing the first weight chunks go out first: their
+    // addresses need only the expert, and the routed rows below are read with
+    // scalar loads, whose counter is not behind them.
+    if constexpr (!FR) {
+      const int wr0 = wrow_of(0);
+#pragma unroll
+      for (int st = 0; st < NST; st++) load_chunk(wr0, g_first + st * NCH, wq[st]);
+    }
+    // the pass's routed rows (lane m: row m, clamped indices read
+    // unconditionally), then token row m's source as a uniform value
     int src[MT];
     {
-      int r = FR ? fused_rows[mb + min(lane, mc - 1)] : sorted_rows[mb + min(lane, mc - 1)];
+      int r;
+      if constexpr (FR) {
+        r = fused_rows[mb + min(lane, mc - 1)];
+      } else {
+        const int32_t* srp = sorted_rows + mb;
+        r = -1;
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+          const int rm = srp[min(m, mc - 1)];
+          r = lane == m ? rm : r;
+        }
+      }
       if (lane >= mc || r < 0 || r >= R) r = -1;
       const int s = r < 0 ? 0 : (x_per_slot ? r : r / k);  // row 0 stands in: masked when read
 #pragma unroll
@@ -386,37 +426,39 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           dma16(s_blocks + b, reinterpret_cast<uint8_t*>(sc_lds + j * sc_blk + ins * 64));
         }
       }
-      // token rows: 64 entries per DMA
+      // token rows: 64 entries per DMA, the lanes below K only
       const int x_per_row = (NITC * 16 + 63) >> 6;
       const int n_xi = mc * x_per_row;
       const int xper_wave = (n_xi + WAVES - 1) / WAVES;
       for (int q = 0; q < xper_wave; q++) {
         const int ins = (q * WAVES + wave) % n_xi;
         const int m = ins / x_per_row, jx = ins - m * x_per_row;
-        const int c = min(jx * 64 + lane, K8 - 1);
-        dma16(reinterpret_cast<const uint4*>(x + (size_t)src[m] * K) + c,
-              reinterpret_cast<uint8_t*>(xs + m * XS + jx * 64));
+        const int c = jx * 64 + lane;
+        if (c < K8)
+          dma16(reinterpret_cast<const uint4*>(x + (size_t)src[m] * K) + c,
+                reinterpret_cast<uint8_t*>(xs + m * XS + jx * 64));
+      }
+      // the entries past K that the padded K groups read are zeros (they meet
+      // the finite codes past each row's end); rows past the pass's count are
+      // not written: they feed only output rows that are never stored
+      const int npad = NITC * 16 - K8;
+      for (int i = threadIdx.x; i < MT * npad; i += WAVES * 64) {
+        const int m = i / npad;
+        xs[m * XS + K8 + (i - m * npad)] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
     asm volatile("" ::: "memory");  // the weight loads stay behind the DMAs
-    uint4 wa[NCH], wb[NCH], wc[NCH];
-    const int g_first = kpart * (NITC / KS);  // this wave's first K group
-    {
+    if constexpr (FR) {
       const int wr0 = wrow_of(0);
-      load_chunk(wr0, g_first, wa);
-      load_chunk(wr0, g_first + NCH, wb);
-      if (NST == 3) load_chunk(wr0, g_first + 2 * NCH, wc);
+#pragma unroll
+      for (int st = 0; st < NST; st++) load_chunk(wr0, g_first + st * NCH, wq[st]);
+      bare_barrier<NST * NCH>();  // every wave's DMAs have landed
+    } else {
+      bare_barrier<0>();  // every wave's DMAs (and the older first chunks) have landed
     }
-    bare_barrier<NST * NCH>();  // every wave's DMAs have landed
 
-    const bool xrow_ok = (lane & 15) < mc;
     const uint4* xrow = xs + min(lane & 15, mc - 1) * XS + kq * 4;
-    // rows past the pass's count and entries past K (LDS padding) read as zero
-    auto xread = [&](int idx) {
-      const uint4 v = xrow[idx];
-      const uint32_t keep = (xrow_ok && idx + kq * 4 < K8) ? 0xffffffffu : 0u;
-      return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-    };
+    auto xread = [&](int idx) { return xrow[idx]; };
 
     for (int j = 0; j < nb; j++) {
       const int row0 = block_row0(j);
@@ -474,14 +516,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 #pragma unroll
             for (int d = 0; d < 4; d++) xv[d] = xread((c0 + i) * 16 + d);
           }
-          // group i is blocks 4 (i % 2) .. 4 (i % 2) + 3 of square i / 2: the
-          // lanes that loaded them write them, then every lane reads its own
-          if (((lane >> 2) & 1) == (i & 1)) {
+          // group i is blocks 4 (i % 2) .. 4 (i % 2) + 3 of square i / 2
+          if constexpr (TR2) {
+            if ((i & 1) == 0) {  // the whole square, before its first group
+              *reinterpret_cast<uint4*>(tr_at(lane >> 3, lane & 7)) = wl[i];
+              *reinterpret_cast<uint4*>(tr_at(8 + (lane >> 3), lane & 7)) = wl[i + 1];
+            }
+          } else if (((lane >> 2) & 1) == (i & 1)) {  // the lanes that loaded the group
             *reinterpret_cast<uint4*>(tr_at(lane >> 3, lane & 3)) = wl[i & ~1];
             *reinterpret_cast<uint4*>(tr_at(8 + (lane >> 3), lane & 3)) = wl[i | 1];
           }
           asm volatile("" ::: "memory");
-          const uint4 w = *reinterpret_cast<const uint4*>(tr_at(lane & 15, kq));
+          const uint4 w = *reinterpret_cast<const uint4*>(tr_at(lane & 15, TR2 ? 4 * (i & 1) + kq : kq));
           const float sf = e8m0_to_float(sv[i]);
           const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -507,24 +553,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       const int rounds = NITC / (KS * NST * NCH);
       for (int rd = 0; rd + 1 < rounds; rd++) {
         const int c0 = g_first + rd * NST * NCH;
-        compute_chunk(c0, wa);
-        load_chunk(wrow, c0 + NST * NCH, wa);
-        compute_chunk(c0 + NCH, wb);
-        load_chunk(wrow, c0 + (NST + 1) * NCH, wb);
-        if (NST == 3) {
-          compute_chunk(c0 + 2 * NCH, wc);
-          load_chunk(wrow, c0 + 5 * NCH, wc);
+#pragma unroll
+        for (int st = 0; st < NST; st++) {
+          compute_chunk(c0 + st * NCH, wq[st]);
+          load_chunk(wrow, c0 + (NST + st) * NCH, wq[st]);
         }
       }
       {
         const int c0 = g_first + (rounds - 1) * NST * NCH;
-        compute_chunk(c0, wa);
-        load_chunk(wnext, nfirst, wa, nstep);
-        compute_chunk(c0 + NCH, wb);
-        load_chunk(wnext, nfirst + NCH * nstep, wb, nstep);
-        if (NST == 3) {
-          compute_chunk(c0 + 2 * NCH, wc);
-          load_chunk(wnext, nfirst + 2 * NCH * nstep, wc, nstep);
+#pragma unroll
+        for (int st = 0; st < NST; st++) {
+          compute_chunk(c0 + st * NCH, wq[st]);
+          load_chunk(wnext, nfirst + st * NCH * nstep, wq[st], nstep);
         }
       }
       asm volatile("" : "+v"(bias_bits));
@@ -1079,17 +1119,18 @@ size_t gemv_sc_entries(int WAVES, int KS, int K) {
   return (blocks + 63) / 64 * 64;
 }
 // LDS of one workgroup, in 16-byte entries: the staged token rows, each
-// wave's 1 KB transpose region, then the weight-scale rows of each of its
-// nbpw row blocks.
-size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K, int nbpw) {
-  return (gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * 64 + (size_t)nbpw * gemv_sc_entries(WAVES, KS, K)) * 16;
+// wave's transpose region (2 KB with tr2, else 1 KB), then the weight-scale
+// rows of each of its nbpw row blocks.
+size_t gemv_lds_for(int MT, int WAVES, int NCH, int NST, int KS, int K, int nbpw, bool tr2 = false) {
+  return (gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * (tr2 ? 128 : 64) +
+          (size_t)nbpw * gemv_sc_entries(WAVES, KS, K)) * 16;
 }
 
-template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR = false>
-hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
-                             const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
-                             const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream,
-                             const FusedRoute& fr = FusedRoute{}) {
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR, bool TR2>
+hipError_t launch_gemv_tr(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
+                          const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
+                          const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream,
+                          const FusedRoute& fr) {
   // Row blocks per workgroup: enough workgroups for one wave of them over the
   // 256 CUs (as many per CU as the waves allow), each streaming its share of
   // an expert's row blocks with the token rows staged once, within the LDS.
@@ -1097,20 +1138,22 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
   const int groups = R < E ? R : E;
   constexpr int RW = WAVES / KS;
   const int nblk = (N + RW * 16 - 1) / (RW * 16);
-  const size_t xs = gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * 64, sc = gemv_sc_entries(WAVES, KS, K);
+  const size_t xs = gemv_xs_entries(MT, NCH, NST, KS, K) + (size_t)WAVES * (TR2 ? 128 : 64),
+               sc = gemv_sc_entries(WAVES, KS, K);
   const int nbpw_max = (int)((kGemvMaxDynLds / 16 - xs) / sc);  // >= 1: checked by the caller
   constexpr int kPerCu = (OCC * 4) / WAVES > 0 ? (OCC * 4) / WAVES : 1;
   int G = (256 * kPerCu + groups - 1) / groups;
   G = G < (nblk + nbpw_max - 1) / nbpw_max ? (nblk + nbpw_max - 1) / nbpw_max : G;
   G = G > nblk ? nblk : G;
   const int nbpw = (nblk + G - 1) / G;
-  size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K, nbpw);
+  size_t lds = gemv_lds_for(MT, WAVES, NCH, NST, KS, K, nbpw, TR2);
   // fused routing: the staged logits, T x (E + 1) floats, and the routing
   // writer's WAVES x 64 + 1 counters
   if (FR && lds < ((size_t)T * (E + 1) + WAVES * 64 + 1) * 4) lds = ((size_t)T * (E + 1) + WAVES * 64 + 1) * 4;
   // above 64 KB the dynamic LDS limit is raised (to what any K may need)
   static DynLdsLimit gemv_lds(
-      reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR>), kGemvMaxDynLds);
+      reinterpret_cast<const void*>(&expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR, TR2>),
+      kGemvMaxDynLds);
   if (lds > 65536) {
     const hipError_t err = gemv_lds.ensure();
     if (err != hipSuccess) return err;
@@ -1118,9 +1161,25 @@ hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const
   // fused routing: one row of workgroups per expert by index (those of
   // unused experts write its offset and exit)
   const dim3 grid(G, FR ? E : groups);
-  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR>), grid, dim3(WAVES * 64), lds, stream,
-                     blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act, (int)sc, fr);
+  hipLaunchKernelGGL((expert_gemv_kernel<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR, TR2>), grid, dim3(WAVES * 64), lds,
+                     stream, blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out, act, (int)sc,
+                     fr);
   return hipGetLastError();
+}
+
+// The 2 KB transpose regions where one row block's LDS fits with them (every
+// K the gpt-oss widths use), else the 1 KB ones.
+template <int MT, int WAVES, int NCH, int NST, int KS, int OCC, bool SWIGLU, bool FR = false>
+hipError_t launch_gemv_shape(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N, int K,
+                             const uint16_t* x, int x_per_slot, int T, int k, const int32_t* offsets,
+                             const int32_t* sorted_rows, float* out, uint16_t* act, hipStream_t stream,
+                             const FusedRoute& fr = FusedRoute{}) {
+  if (gemv_lds_for(MT, WAVES, NCH, NST, KS, K, 1, true) <= kGemvMaxDynLds)
+    return launch_gemv_tr<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR, true>(blocks, scales, bias, E, N, K, x, x_per_slot,
+                                                                         T, k, offsets, sorted_rows, out, act, stream,
+                                                                         fr);
+  return launch_gemv_tr<MT, WAVES, NCH, NST, KS, OCC, SWIGLU, FR, false>(blocks, scales, bias, E, N, K, x, x_per_slot, T,
+                                                                        k, offsets, sorted_rows, out, act, stream, fr);
 }
 
 // Chunk length NCH (K groups of 128 elements) for a ring of NST chunks per K
