@@ -170,7 +170,8 @@ size_t mxfp4_expert_proj_workspace_size(int E, int N, int T, int k, int K, int x
  * and forward_routed for the products; fn activate / down_bias_of for the
  * per-expert bias rows.)
  *
- *   blocks  [E, N, K/32, 16] u8   MXFP4 codes, low nibble = even element.
+ *   blocks  [E, N, K/32, 16] u8   MXFP4 codes, low nibble = even element;
+ *           one expert's N * K / 2 bytes at most 4 GiB.
  *   scales  [E, N, K/32]     u8   E8M0 exponents (bias 127); bytes 0..254.
  *   bias    [E, N] bf16, or NULL (no bias).
  *   E, N, K: 1 <= E <= MXFP4_MAX_EXPERTS, N >= 1, K >= 32 and K % 32 == 0.

@@ -111,7 +111,7 @@ int expert_proj_impl(const uint8_t* blocks, const uint8_t* scales, const uint16_
     return fail(MXFP4_ERR_INVALID_ARG, "K = %d too large for the GEMV path's LDS staging", K);
   if (p == MXFP4_PATH_GEMM && K > MXFP4_GEMM_MAX_K)
     return fail(MXFP4_ERR_INVALID_ARG, "K = %d above the grouped GEMM's limit %d", K, MXFP4_GEMM_MAX_K);
-  if (p == MXFP4_PATH_GEMM && (size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull)
+  if ((size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull)  // one buffer resource per expert, either path
     return fail(MXFP4_ERR_INVALID_ARG, "N * K / 2 = %zu bytes per expert exceeds 4 GiB", (size_t)N * (K / 32) * 16);
   if (p == MXFP4_PATH_GEMM) {
     const size_t need = mxfp4::gemm_workspace_bytes(E, N, T, k, K, x_per_slot);
@@ -298,6 +298,8 @@ int moe_decode_batch_impl(const uint16_t* logits, int T, int E, int k, const uin
     return fail(MXFP4_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(blocks) || !aligned16(x)) return fail(MXFP4_ERR_INVALID_ARG, "blocks and x must be 16-byte aligned");
   if (!gemv_fits(T, K)) return fail(MXFP4_ERR_INVALID_ARG, "K = %d needs more LDS than a workgroup has", K);
+  if ((size_t)N * (size_t)(K / 32) * 16 > 0xFFFFFFFFull)
+    return fail(MXFP4_ERR_INVALID_ARG, "N * K / 2 = %zu bytes per expert exceeds 4 GiB", (size_t)N * (K / 32) * 16);
   int st = check_device();
   if (st != MXFP4_OK) return st;
   hipError_t e = mxfp4::launch_moe_decode_batch(logits, T, E, k, blocks, scales, bias, N, K, x, x_per_slot, topk_ids,

@@ -81,6 +81,7 @@ def _proj(lib, E=32, N=64, K=128, T=4, k=4, path=0, ws=None, ws_bytes=0, ptr=16,
     (dict(path=1, K=8192, T=64, k=4), 1),
     (dict(path=1, K=4128, T=64, k=4), 1),      # GEMV LDS staging: K <= 4096 when T > 4
     (dict(path=2, K=8224, ws=ctypes.c_void_p(16), ws_bytes=1 << 40), 1),  # GEMM: K <= 8192
+    (dict(path=1, E=1, N=3_000_000, K=3072, T=64, k=1), 1),  # one expert's codes above 4 GiB (GEMV)
 ])
 def test_expert_proj_rejects_bad_arguments(kw, status):
     lib = B.load_library()
@@ -158,6 +159,12 @@ def test_moe_decode_batch_rejects_bad_arguments(kw, swiglu):
     lib = B.load_library()
     assert _decode_batch(lib, swiglu=swiglu, **kw) == 1, kw
     assert lib.mxfp4_last_error() != b""
+
+
+def test_moe_decode_batch_rejects_experts_above_4gib():
+    lib = B.load_library()
+    assert _decode_batch(lib, T=2, E=1, k=1, N=3_000_000, K=3072) == 1
+    assert b"4 GiB" in lib.mxfp4_last_error()
 
 
 def test_moe_decode_batch_swiglu_needs_even_n():
