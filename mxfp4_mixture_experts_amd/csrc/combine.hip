@@ -30,24 +30,39 @@ __device__ __forceinline__ float slot_gate(const float* __restrict__ gates, cons
   return (ids && (unsigned)ids[r] >= (unsigned)E) ? 0.f : g;
 }
 
+// I: the index type, 32-bit whenever every float4 index of proj fits (no
+// 64-bit divisions then)
+template <typename I>
 __global__ __launch_bounds__(kCombineThreads) void combine_vec4_kernel(
     const float* __restrict__ proj, const float* __restrict__ gates, int T, int k, int N4,
     float* __restrict__ y, const int32_t* __restrict__ ids, int E) {
-  const size_t total = (size_t)T * N4;
-  const size_t stride = (size_t)gridDim.x * kCombineThreads;
-  for (size_t i = (size_t)blockIdx.x * kCombineThreads + threadIdx.x; i < total; i += stride) {
-    const size_t t = i / N4;
-    const size_t c = i - t * N4;
+  const I total = (I)T * (I)N4;
+  const I stride = (I)gridDim.x * kCombineThreads;
+  for (I i = (I)blockIdx.x * kCombineThreads + threadIdx.x; i < total; i += stride) {
+    const I t = i / (I)N4;
+    const I c = i - t * (I)N4;
     const float4* p = reinterpret_cast<const float4*>(proj) + (t * k) * N4 + c;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < k; s++) {
-      const float g = gates[t * k + s];
-      float4 v = load_nt(p + (size_t)s * N4);  // unconditional: no branch per load
-      if (slot_gate(gates, ids, E, t * k + s) == 0.f) v = make_float4(0.f, 0.f, 0.f, 0.f);
-      acc.x = fmaf(g, v.x, acc.x);
-      acc.y = fmaf(g, v.y, acc.y);
-      acc.z = fmaf(g, v.z, acc.z);
-      acc.w = fmaf(g, v.w, acc.w);
+    // four slots' loads in flight at a time (unconditional, from a clamped
+    // slot), then their sums in slot order
+    for (int s0 = 0; s0 < k; s0 += 4) {
+      float4 v[4];
+      float g[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int s = min(s0 + u, k - 1);
+        v[u] = load_nt(p + (size_t)s * N4);
+        g[u] = slot_gate(gates, ids, E, t * k + s);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        if (s0 + u >= k) break;
+        if (g[u] == 0.f) v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        acc.x = fmaf(g[u], v[u].x, acc.x);
+        acc.y = fmaf(g[u], v[u].y, acc.y);
+        acc.z = fmaf(g[u], v[u].z, acc.z);
+        acc.w = fmaf(g[u], v[u].w, acc.w);
+      }
     }
     reinterpret_cast<float4*>(y)[i] = acc;
   }
@@ -79,8 +94,11 @@ hipError_t launch_combine(const float* proj, const float* gates, int T, int k, i
   const size_t items = (size_t)T * (vec ? N / 4 : N);
   size_t blocks = (items + kCombineThreads - 1) / kCombineThreads;
   if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
-  if (vec)
-    hipLaunchKernelGGL(combine_vec4_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
+  if (vec && (size_t)T * k * (N / 4) + (size_t)blocks * kCombineThreads < 0xFFFFFFFFull)
+    hipLaunchKernelGGL(combine_vec4_kernel<uint32_t>, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
+                       gates, T, k, N / 4, y, ids, E);
+  else if (vec)
+    hipLaunchKernelGGL(combine_vec4_kernel<size_t>, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
                        gates, T, k, N / 4, y, ids, E);
   else
     hipLaunchKernelGGL(combine_scalar_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, proj,
