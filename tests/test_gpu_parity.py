@@ -73,6 +73,10 @@ SMALL_CASES = {
     "one_expert": dict(E=1, N=1, K=32, T=5, k=1, route="logits"),
     "one_token_top1": dict(E=16, N=70, K=64, T=1, k=1, route="logits"),
     "wide_k": dict(E=6, N=64, K=4096, T=9, k=2, x_per_slot=True, route="ids"),
+    # multi-token GEMV with most of the padded K groups past K (zeroed LDS
+    # entries meet the codes past each row's end): 16- and 4-token tiles
+    "k32_batch": dict(E=8, N=100, K=32, T=40, k=2, route="logits"),
+    "four_token_k160": dict(E=8, N=90, K=160, T=3, k=4, x_per_slot=True, route="logits"),
     # more than 64 experts: the multi-chunk expert scans
     "many_experts": dict(E=100, N=70, K=96, T=60, k=3, route="logits"),
     # one token: the row-streaming kernel up to K = 3072, the MFMA kernel past it
