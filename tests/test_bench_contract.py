@@ -31,3 +31,13 @@ def test_headline_algorithmic_bytes():
     assert acc["proj"] == weights + 2880 * 2 + 4 * 5760 * 4 + 33 * 4 + 4 * 4
     assert acc["flops"] == 2.0 * 4 * 5760 * 2880
 
+
+
+def test_published_context_is_quoted_not_compared():
+    """The pages' only measured numbers (whole-model decode on an H100) ride
+    along in the line as context; no ratio is formed with them."""
+    pc = bench.PUBLISHED_CONTEXT
+    assert pc["gpt2_124m_decode_tok_s"]["transformers_eager"] == 175.29
+    assert pc["gpt2_124m_decode_tok_s"]["transformers_torch_compile"] == 419.13
+    assert pc["gpt2_124m_decode_tok_s"]["vllm"] == 696.25
+    assert "H100" in pc["note"]
