@@ -17,11 +17,11 @@
 // of the wave covers 8 rows x 128 contiguous bytes (whole lines), and the
 // square then passes through the wave's LDS so that lane l holds row l % 16,
 // block 4 g + l / 16 of K group g, as the MFMA wants it.  The loads run a
-// pipeline of two or three chunks of NCH 128-element K groups (the next
-// chunks are in flight while the current one is multiplied), and the first
-// chunks are issued before the expert's token rows (up to MT per pass) are
-// staged in LDS as bf16; the four MFMAs of a group accumulate into four
-// independent accumulators.
+// ring of two to four chunks of NCH 128-element K groups (the next chunks are
+// in flight while the current one is multiplied), and the first chunks are
+// issued before the expert's token rows (up to MT per pass) are staged in LDS
+// as bf16, with zeros past K so that the padded K groups need no mask; the
+// four MFMAs of a group accumulate into four independent accumulators.
 //
 // Arithmetic.  Each 32-bit word of a block (8 codes) becomes 8 bf16 weights
 // through the gfx950 convert v_cvt_scalef32_pk_bf16_fp4 with the block's E8M0
