@@ -389,8 +389,8 @@ int mxfp4_expert_proj_combine(const uint8_t* blocks, const uint8_t* scales, cons
  * per (token, 192-column weight panel) an arrival counter in the workspace,
  * set by the GEMM's pre-pass, counts the token's routed rows as their tiles
  * finish, and the tile that brings the last of them sums the token's k rows
- * over its panel in slot order.  On the GEMV path, for T <= 4 with T * k <= E
- * and K <= MXFP4_DECODE_MAX_K, one launch: a workgroup runs all k slots of one token
+ * over its panel in slot order.  On the GEMV path, while T * k <= E and K <=
+ * MXFP4_DECODE_MAX_K, one launch: a workgroup runs all k slots of one token
  * over its weight rows and sums them (as mxfp4_expert_proj_combine does for
  * one token); otherwise the combine is a second launch.
  * (src/experts.linnet fn forward_routed: the routed rows' down products

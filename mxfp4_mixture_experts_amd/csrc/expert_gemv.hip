@@ -958,8 +958,9 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
 // router).  A workgroup owns 4 * WPS weight rows of token blockIdx.y and runs
 // kT1Group slots of the token over them at a time, WPS waves per slot, so the
 // combine needs no other workgroup's results (an expert two tokens chose is
-// streamed once per token: for batches with no more routed rows than experts).  Each slot's value is the row-streaming kernel's (the
-// same lane split, products, fixed lane sum and bias added last); the values
+// streamed once per token: for batches with no more routed rows than
+// experts).  Each slot's value is the row-streaming kernel's (the same lane
+// split, products, fixed lane sum and bias added last); the values
 // meet in LDS and the first slot's waves sum them in slot order with one fused
 // multiply-add each, as moe_combine does: y equals mxfp4_expert_proj followed
 // by moe_combine bit for bit.
@@ -1274,7 +1275,11 @@ hipError_t launch_expert_gemv(const uint8_t* blocks, const uint8_t* scales, cons
 hipError_t launch_proj_combine_t1(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E, int N,
                                   int K, const uint16_t* x, int x_per_slot, int k, const int32_t* topk_ids,
                                   const float* gates, float* out, float* y, hipStream_t stream, int T) {
-  constexpr int kWps = 2;  // 8 rows per workgroup, 8 waves: 360 workgroups per token at N = 2880
+  // 4 rows per workgroup, one wave per slot: 720 workgroups per token at N =
+  // 2880 (at the gpt-oss down decode of one token 7.1 us, against 7.8 us with
+  // two waves per slot and 9.0 us with four; the token rows are staged more
+  // often, but more, smaller workgroups start sooner)
+  constexpr int kWps = 1;
   constexpr int kRows = T1Shape<1, kWps>::kRows;
   hipLaunchKernelGGL(expert_gemv_combine_t1_kernel<kWps>, dim3((N + kRows - 1) / kRows, T),
                      dim3(kWps * kT1Group * 64), 0, stream, blocks, scales, bias, E, N, K, x, x_per_slot, k, topk_ids,
@@ -1283,18 +1288,16 @@ hipError_t launch_proj_combine_t1(const uint8_t* blocks, const uint8_t* scales, 
 }
 
 // The projection of the routed rows and the gate-weighted combine on the GEMV
-// path: one launch for up to kCombineOneLaunchT tokens whose routed rows
-// number no more than the experts, else the projection and then the combine.
-// (The one-launch form re-reads each token's input rows per 8-row workgroup;
-// measured at the gpt-oss-20b down decode, 2 tokens 12.0 against 12.6 us and 4
-// tokens 18.9 against 20.1 us; larger batches keep the two launches.)
-constexpr int kCombineOneLaunchT = 4;
-
+// path: one launch while the routed rows number no more than the experts (a
+// workgroup per token and 4 weight rows; measured at the gpt-oss down decode
+// against the projection and then the combine: 1 token 7.1 against 9.3 us, 2
+// tokens 11.0 against 12.6, 4 tokens 17.6 against 20.5, 6 tokens 24.7 against
+// 26.3, 8 tokens 31.3 against 31.2), else the projection and then the combine.
 hipError_t launch_expert_gemv_combine(const uint8_t* blocks, const uint8_t* scales, const uint16_t* bias, int E,
                                       int N, int K, const uint16_t* x, int x_per_slot, int T, int k,
                                       const int32_t* offsets, const int32_t* sorted_rows, const int32_t* topk_ids,
                                       const float* gates, float* out, float* y, hipStream_t stream) {
-  if (T <= kCombineOneLaunchT && gemv_one_row(T, k, E, K))
+  if (gemv_one_row(T, k, E, K))
     return launch_proj_combine_t1(blocks, scales, bias, E, N, K, x, x_per_slot, k, topk_ids, gates, out, y, stream, T);
   hipError_t e = launch_expert_gemv(blocks, scales, bias, E, N, K, x, x_per_slot, T, k, offsets, sorted_rows, out,
                                     nullptr, stream);

@@ -8,8 +8,8 @@ paths.  On the grouped-GEMM path the combine runs inside the GEMM, summed by
 whichever tile brings a token's last routed row; the shapes below give tokens
 whose slots land in different row tiles and weight panels, partial panels,
 widths with N % 4 != 0 (the scalar store and sum), k = 1, k = E and more than
-64 experts.  On the GEMV path, batches of up to 4 tokens with T * k <= E run
-the projection and the sums in one launch (a workgroup per token and row block).  The model-size down prefill is checked bit for bit against the
+64 experts.  On the GEMV path, batches with T * k <= E run the projection and
+the sums in one launch (a workgroup per token and row block).  The model-size down prefill is checked bit for bit against the
 separate calls and for determinism over repeated runs (the tiles' finishing
 order varies from run to run; y must not).
 """
