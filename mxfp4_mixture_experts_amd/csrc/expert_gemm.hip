@@ -707,7 +707,8 @@ __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int n
                                         __amdgpu_buffer_rsrc_t orsrc, float* __restrict__ y) {
   const int tid = threadIdx.x;
   // a slot's row counts when the slot is routed and its gate is not 0;
-  // otherwise it adds a zero product, whatever the row holds
+  // otherwise it adds a zero product (a zero weight times a zero), whatever
+  // the row or the gate holds
   auto counts = [&](int id, float g) { return (unsigned)id < (unsigned)E && g != 0.f; };
   if (vec) {
     // item = (token, 4 columns)
@@ -743,10 +744,11 @@ __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int n
 #pragma unroll
           for (int j = 0; j < kSumSlots; j++) {
             if (s0 + j < k) {
-              const f32x4_t x = counts(id[u][j], g[u][j]) ? __builtin_bit_cast(f32x4_t, v[u][j])
-                                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
-              a[u] = f32x4_t{fmaf(g[u][j], x[0], a[u][0]), fmaf(g[u][j], x[1], a[u][1]),
-                             fmaf(g[u][j], x[2], a[u][2]), fmaf(g[u][j], x[3], a[u][3])};
+              const bool c = counts(id[u][j], g[u][j]);
+              const f32x4_t x = c ? __builtin_bit_cast(f32x4_t, v[u][j]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+              const float gw = c ? g[u][j] : 0.f;
+              a[u] = f32x4_t{fmaf(gw, x[0], a[u][0]), fmaf(gw, x[1], a[u][1]), fmaf(gw, x[2], a[u][2]),
+                             fmaf(gw, x[3], a[u][3])};
             }
           }
       }
@@ -765,7 +767,8 @@ __device__ __noinline__ void sum_tokens(const int* last_t, int nl, int n0, int n
       const int r = t * k + s;
       const float g = gates[r];
       const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, coh_off(r * N + col), 0, kCohPolicy));
-      a = fmaf(g, counts(ids[r], g) ? v : 0.f, a);
+      const bool c = counts(ids[r], g);
+      a = fmaf(c ? g : 0.f, c ? v : 0.f, a);
     }
     y[(size_t)t * N + col] = a;
   }

@@ -143,3 +143,29 @@ def test_fused_combine_model_size_deterministic():
     dp.y.fill_(float("nan"))
     dp.proj_combine_routed()
     np.testing.assert_array_equal(dp.results()["y"], g2["y"])
+
+
+@pytest.mark.parametrize("T", [4, 50])
+def test_fused_combine_ignores_the_gates_of_unrouted_slots(T):
+    """A slot whose id lies outside [0, E) adds a zero product whatever its gate
+    holds: with NaN written into those gates after the routing, y is bit-equal to
+    the same call with the routing's own gates (0 there), on both paths (T = 4:
+    the one-launch GEMV combine; T = 50: the GEMV projection then the combine,
+    and the sums inside the grouped GEMM)."""
+    E, k = 16, 4
+    _announce(f"fused combine, NaN gates on unrouted slots, T={T}")
+    q = S.make_custom(E=E, N=200, K=128, T=T, k=k, x_per_slot=True, route="ids+logits", combine=True, tag=660 + T)
+    q.ids_in = np.array(q.ids_in, dtype=np.int32, copy=True)
+    q.ids_in[0, 1] = -1
+    q.ids_in[T - 1, 2] = E + 3
+    for path in (B.MXFP4_PATH_GEMV, B.MXFP4_PATH_GEMM):
+        dp = DeviceProblem(q, path=path)
+        dp.route_group()
+        dp.proj_combine_routed()
+        ref = dp.results()["y"].copy()
+        assert np.all(np.isfinite(ref))
+        bad = (dp.topk_ids < 0) | (dp.topk_ids >= E)
+        dp.gates[bad] = float("nan")
+        dp.y.fill_(float("nan"))
+        dp.proj_combine_routed()
+        np.testing.assert_array_equal(dp.results()["y"], ref)
