@@ -248,6 +248,7 @@ def describe(p, swiglu=False):
         "gate_up_prefill_t4096": "gpt-oss-20b gate_up prefill",
         "down_prefill_zipf_t2048": "gpt-oss-20b down prefill, Zipf(1.2) routing",
         "gate_up_decode_t4": "gpt-oss-20b gate_up decode of a 4-token batch",
+        "down_decode_t4": "gpt-oss-20b down decode of a 4-token batch",
     }[p.name]
     if swiglu:
         return (f"{name} + gated activation: E={p.E} N={p.N} K={p.K} T={p.T} top-{p.k}, MXFP4 blocks "
@@ -524,11 +525,16 @@ def main():
         # (the down decode of 64 tokens both as three calls and as one launch,
         # mxfp4_moe_decode_batch, with the combine after it)
         # (and a decode batch of 4 tokens at gate_up, both ways: the one-row-per-workgroup GEMV)
+        # (and one at down with the combine, as three calls and with the projection
+        # and the combine in one launch, mxfp4_expert_proj_combine_routed on the GEMV path)
         from mxfp4_mixture_experts_amd import synthetic as S
         p4 = S.make_custom(E=32, N=5760, K=2880, T=4, k=4, route="logits", tag=1204)
         p4.name = "gate_up_decode_t4"
+        p4d = S.make_custom(E=32, N=2880, K=2880, T=4, k=4, x_per_slot=True, route="logits", combine=True, tag=1205)
+        p4d.name = "down_decode_t4"
         for cfg, steps, swiglu, cf, fz in ((2, 100, False, False, False), (2, 100, False, False, True),
                                            (p4, 200, False, False, False), (p4, 200, False, False, True),
+                                           (p4d, 200, False, False, False), (p4d, 200, False, True, False),
                                            (3, 20, False, False, False), (4, 40, False, False, False),
                                            (1, 200, True, False, True), (3, 20, True, False, False),
                                            (4, 40, False, True, False)):
@@ -563,8 +569,11 @@ def main():
                             + ((" (routing + projection + activation in one launch)" if swiglu else
                                 " (routing, grouping and projection in one launch: mxfp4_moe_decode_batch"
                                 + ("; then the combine)" if r["p"].combine else ")")) if r["fused"] else "")
-                            + (" (the combine fused into the grouped GEMM: route_group + "
-                               "mxfp4_expert_proj_combine_routed; proj_us covers both)" if cf else ""),
+                            + ((" (route_group + mxfp4_expert_proj_combine_routed: the projection and the "
+                                "combine in one launch on the GEMV path; proj_us covers both)"
+                                if r["p"].T * r["p"].k <= r["p"].E else
+                                " (the combine fused into the grouped GEMM: route_group + "
+                                "mxfp4_expert_proj_combine_routed; proj_us covers both)") if cf else ""),
                 "ms_per_step": round(r["ms_per_step"], 4),
                 "step_GBps": round(a["step"] / t_step / 1e9, 1),
                 "step_TFLOPs": round(a["flops"] / t_step / 1e12, 2),
