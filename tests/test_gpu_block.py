@@ -59,6 +59,13 @@ ROUTER_CASES = {
     "narrow_h": (300, 32, 7),          # one K step: 15 of the 16 waves contribute nothing
     "long_h": (20, 8192, 32),          # several chunks per wave
     "one_expert": (5, 96, 1),
+    # up to 16 tokens: one workgroup per expert row
+    "rows_t3": (3, 2880, 32),
+    "rows_t8": (8, 2880, 32),
+    "rows_t16": (16, 2880, 32),
+    "rows_t7_ragged": (7, 160, 13),
+    "rows_t2_narrow": (2, 96, 7),
+    "rows_t4_long_h": (4, 8192, 100),
 }
 
 
