@@ -52,7 +52,8 @@ def check_logits(bits, r: S.RouterProblem, with_bias=True):
 
 
 ROUTER_CASES = {
-    "decode_t1": (1, 2880, 32),        # gpt-oss-20b decode: 16-expert tiles, one token tile
+    "decode_t1": (1, 2880, 32),        # gpt-oss-20b decode: one workgroup per expert row
+    "t17_first_tiles": (17, 2880, 32), # the smallest batch on 16-expert tiles: a ragged token tile
     "small_t64": (64, 2880, 32),       # the largest batch on 16-expert tiles
     "t65_wide_tiles": (65, 2880, 32),  # 32-expert tiles, a ragged token tile
     "ragged_experts": (37, 256, 100),  # E not a multiple of the tile
