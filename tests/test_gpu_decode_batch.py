@@ -35,6 +35,10 @@ BATCH_CASES = {
     "e64_t64": dict(E=64, N=130, K=3072, T=64, k=4, route="logits"),
     "e5_odd": dict(E=5, N=77, K=96, T=33, k=3, x_per_slot=True, route="logits"),
     "one_token": dict(E=32, N=200, K=2880, T=1, k=4, route="logits"),
+    # T * k = E: the largest batch with one routed row per workgroup row
+    "eight_tokens_rows_eq_experts": dict(E=32, N=192, K=2880, T=8, k=4, route="logits"),
+    # T * k = E + 4: the smallest gpt-oss batch on the multi-token kernel
+    "nine_tokens_rows_over_experts": dict(E=32, N=192, K=2880, T=9, k=4, x_per_slot=True, route="logits"),
 }
 
 
