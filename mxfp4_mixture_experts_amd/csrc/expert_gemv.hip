@@ -759,24 +759,45 @@ __global__ __launch_bounds__(WAVES * 64) void expert_gemv_t1_kernel(
     if (E == 32) {
       // gpt-oss-20b's 32 experts: the logits as 16 words through the scalar
       // cache (one wave-uniform load; about 0.5 us sooner than a vector load
-      // of the same 64 bytes by every wave), each expert's logit then a
-      // uniform value.  Other counts take the vector load below (a second
-      // specialised path made the kernel larger and its start slower).
+      // of the same 64 bytes by every wave); lane i < 16 takes word i and
+      // each lane its expert's word from lane e / 2.  Every wave
+      // of the launch (about 22 per CU) ranks the token at the same moment,
+      // so the ranking is held to a few instructions: lane e's logit becomes
+      // a unique integer key (the bf16 bits in an order-preserving form, -0
+      // as +0, above 255 - e, so equal logits favour the lower index: the
+      // order of the rank below), and k rounds of a wave maximum over the
+      // keys (DPP within rows of 16, then the 4 row maxima) each take the
+      // next expert.  The comparisons of 32 uniform logits with each lane's
+      // took about 220 vector and 300 scalar instructions per wave.  Other
+      // counts take the vector load below (a second specialised path made
+      // the kernel larger and its start slower).
       const __attribute__((address_space(4))) uint32_t* lw =
           (const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(lrow);
       uint32_t wv[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) wv[i] = lw[i];
-      auto logit = [&](int j) { return __uint_as_float((j & 1) ? (wv[j >> 1] & 0xffff0000u) : (wv[j >> 1] << 16)); };
+      int words = 0;
 #pragma unroll
-      for (int jj = 0; jj < 32; jj++) {
-        const float lj = logit(jj);  // a select per lane, not a branch
-        if (lane == jj) l = lj;
-      }
-#pragma unroll
-      for (int jj = 0; jj < 32; jj++) {
-        const float lj = logit(jj);
-        rank += (lj > l || (lj == l && jj < lane)) ? 1 : 0;
+      for (int i = 0; i < 16; i++) words = lane == i ? (int)wv[i] : words;
+      const uint32_t wsel = (uint32_t)__builtin_amdgcn_ds_bpermute((lane >> 1) << 2, words);
+      const uint32_t b = (lane & 1) ? (wsel >> 16) : (wsel & 0xffffu);
+      l = lane < 32 ? __uint_as_float(b << 16) : -INFINITY;
+      const uint32_t bz = b == 0x8000u ? 0u : b;
+      const uint32_t ord = (bz & 0x8000u) ? (~bz & 0xffffu) : (bz | 0x8000u);
+      uint32_t key = lane < 32 ? (ord << 8) | (uint32_t)(255 - lane) : 0u;
+      rank = 64;  // not chosen
+      for (int r = 0; r < k; r++) {
+        uint32_t v = key;
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+        const uint32_t m = max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+                               max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+        if (lane == 255 - (int)(m & 0xffu)) {
+          rank = r;
+          key = 0u;
+        }
       }
     } else {
       l = lane < E ? bf16_bits_to_f32(lrow[lane]) : -INFINITY;
